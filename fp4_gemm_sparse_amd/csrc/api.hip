@@ -1,0 +1,201 @@
+// api.hip -- the C ABI of libsplice.so (declared in include/splice.h):
+// host-side argument checks, then launches on the caller's stream.
+#include "../../include/splice.h"
+#include "kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+using namespace splice;
+
+namespace {
+
+constexpr int64_t MAX_K = 65536;
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t hs(splice_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? SPLICE_OK : SPLICE_ERR_HIP; }
+
+// shape rules shared by every entry point
+inline int check_k(int64_t K, int32_t k)
+{
+    if (K < 0 || K % 16 != 0 || k < 0 || k > K) return SPLICE_ERR_INVALID_ARG;
+    if (K > MAX_K) return SPLICE_ERR_UNSUPPORTED;
+    return SPLICE_OK;
+}
+
+int check_gemm(const GemmArgs &a, int path)
+{
+    if (a.M < 0 || a.N < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(a.K, a.k);
+    if (rc) return rc;
+    if (path != SPLICE_PATH_AUTO && path != SPLICE_PATH_DECODE && path != SPLICE_PATH_PREFILL)
+        return SPLICE_ERR_INVALID_ARG;
+    if (path == SPLICE_PATH_DECODE && a.M > SPLICE_DECODE_MAX_M) return SPLICE_ERR_INVALID_ARG;
+    if (a.M == 0 || a.N == 0) return SPLICE_OK;
+    if (a.ldy < a.N) return SPLICE_ERR_INVALID_ARG;
+    if (a.K % 128 != 0) return SPLICE_ERR_UNSUPPORTED;
+    if (!a.Y || !a.alpha_x || !a.alpha_w) return SPLICE_ERR_INVALID_ARG;
+    if (a.K > 0 && (!a.Xq || !a.Xs || !a.Wq || !a.Ws)) return SPLICE_ERR_INVALID_ARG;
+    if (a.k > 0 && (!a.X_S || !a.W_S)) return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(a.Xq, 16) || !aligned(a.Wq, 16) || !aligned(a.Xs, 8) || !aligned(a.Ws, 8) ||
+        !aligned(a.Y, 4))
+        return SPLICE_ERR_INVALID_ARG;
+    const uintptr_t side_al = (a.k % 8 == 0) ? 16 : 2;
+    if (a.k > 0 && (!aligned(a.X_S, side_al) || !aligned(a.W_S, side_al))) return SPLICE_ERR_INVALID_ARG;
+    return SPLICE_OK;
+}
+
+inline Path choose_path(int64_t M, int path)
+{
+    if (path == SPLICE_PATH_DECODE) return Path::Decode;
+    if (path == SPLICE_PATH_PREFILL) return Path::Prefill;
+    return M <= SPLICE_DECODE_MAX_M ? Path::Decode : Path::Prefill;
+}
+
+int run_gemm(const GemmArgs &a, void *ws, size_t ws_bytes, int path, hipStream_t s)
+{
+    int rc = check_gemm(a, path);
+    if (rc) return rc;
+    if (a.M == 0 || a.N == 0) return SPLICE_OK;
+    const Path p = choose_path(a.M, path);
+    const size_t need = gemm_ws_bytes(p, a.M, a.N, a.K);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16))) return SPLICE_ERR_WORKSPACE;
+    return hip_status(launch_gemm(p, a, ws, ws_bytes, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *splice_status_string(int status)
+{
+    switch (status) {
+    case SPLICE_OK: return "ok";
+    case SPLICE_ERR_INVALID_ARG: return "invalid argument";
+    case SPLICE_ERR_UNSUPPORTED: return "unsupported shape";
+    case SPLICE_ERR_WORKSPACE: return "workspace too small";
+    case SPLICE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t splice_select_workspace_size(int64_t) { return 0; }
+
+int splice_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int32_t k,
+                           int64_t *count, double *mean, double *m2, float *absmax, int32_t *idx,
+                           float *alpha_x, void *ws, size_t ws_bytes, splice_stream_t stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    if (T < 0 || !count || *count < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(K, k);
+    if (rc) return rc;
+    if (K == 0) {
+        *count += T;
+        return SPLICE_OK;
+    }
+    if (!mean || !m2 || !absmax || (k > 0 && !idx) || (T > 0 && !X)) return SPLICE_ERR_INVALID_ARG;
+    if (T > 0 && ldx < K) return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(X, 2) || !aligned(mean, 8) || !aligned(m2, 8) || !aligned(absmax, 4) ||
+        !aligned(idx, 4) || !aligned(alpha_x, 4))
+        return SPLICE_ERR_INVALID_ARG;
+    hipError_t e = launch_stats(X, T, K, ldx, *count, mean, m2, absmax, hs(stream));
+    if (e != hipSuccess) return SPLICE_ERR_HIP;
+    e = launch_select(m2, absmax, K, k, idx, alpha_x, hs(stream));
+    if (e != hipSuccess) return SPLICE_ERR_HIP;
+    *count += T;
+    return SPLICE_OK;
+}
+
+size_t splice_alpha_workspace_size(void) { return alpha_ws_bytes(); }
+
+int splice_compute_alpha(const uint16_t *A, int64_t R, int64_t K, int64_t lda, const int32_t *idx,
+                         int32_t k, float *alpha, void *ws, size_t ws_bytes,
+                         splice_stream_t stream)
+{
+    if (R < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(K, k);
+    if (rc) return rc;
+    if (!alpha || !aligned(alpha, 4)) return SPLICE_ERR_INVALID_ARG;
+    if (R > 0 && K > 0) {
+        if (!A || lda < K || (k > 0 && !idx)) return SPLICE_ERR_INVALID_ARG;
+        if (!aligned(A, 16) || lda % 8 != 0) return SPLICE_ERR_UNSUPPORTED;
+    }
+    if (!ws || ws_bytes < alpha_ws_bytes() || !aligned(ws, 4)) return SPLICE_ERR_WORKSPACE;
+    return hip_status(launch_alpha(A, R, K, lda, idx, k, alpha, ws, hs(stream)));
+}
+
+int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda, const int32_t *idx,
+                          int32_t k, const float *alpha, uint8_t *codes, uint8_t *scales,
+                          uint16_t *side, splice_stream_t stream)
+{
+    if (R < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(K, k);
+    if (rc) return rc;
+    if (R == 0 || K == 0) return SPLICE_OK;
+    if (!A || !alpha || !codes || !scales || lda < K || (k > 0 && (!idx || !side)))
+        return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || lda % 8 != 0) return SPLICE_ERR_UNSUPPORTED;
+    if (!aligned(codes, 8) || !aligned(alpha, 4) || (k > 0 && !aligned(side, 2)))
+        return SPLICE_ERR_INVALID_ARG;
+    return hip_status(launch_quantize(A, R, K, lda, idx, k, alpha, codes, scales, side, hs(stream)));
+}
+
+size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t)
+{
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return gemm_ws_bytes(M <= SPLICE_DECODE_MAX_M ? Path::Decode : Path::Prefill, M, N, K);
+}
+
+int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
+                const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
+                int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy, void *ws,
+                size_t ws_bytes, int path, splice_stream_t stream)
+{
+    GemmArgs a{Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy};
+    return run_gemm(a, ws, ws_bytes, path, hs(stream));
+}
+
+int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint8_t *Wq,
+               const uint8_t *Ws, const float *alpha_w, int64_t M, int64_t N, int64_t K, float *Y,
+               int64_t ldy, void *ws, size_t ws_bytes, int path, splice_stream_t stream)
+{
+    GemmArgs a{Xq, Xs, alpha_x, nullptr, Wq, Ws, alpha_w, nullptr, M, N, K, 0, Y, ldy};
+    return run_gemm(a, ws, ws_bytes, path, hs(stream));
+}
+
+size_t splice_grouped_workspace_size(const splice_group *groups, int32_t G, int64_t N, int64_t K,
+                                     int32_t)
+{
+    size_t need = 0;
+    if (!groups || G <= 0 || N <= 0 || K <= 0) return 0;
+    for (int32_t i = 0; i < G; i++) {
+        const int64_t M = groups[i].M;
+        if (M <= 0) continue;
+        const size_t b = gemm_ws_bytes(M <= SPLICE_DECODE_MAX_M ? Path::Decode : Path::Prefill, M, N, K);
+        need = b > need ? b : need;
+    }
+    return need;
+}
+
+int splice_gemm_grouped(const splice_group *groups, int32_t G, int64_t N, int64_t K, int32_t k,
+                        void *ws, size_t ws_bytes, splice_stream_t stream)
+{
+    if (G < 0 || (G > 0 && !groups)) return SPLICE_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < G; i++) {
+        const splice_group &g = groups[i];
+        GemmArgs a{g.Xq, g.Xs, g.alpha_x, g.X_S, g.Wq, g.Ws, g.alpha_w, g.W_S, g.M, N, K, k, g.Y, N};
+        int rc = check_gemm(a, SPLICE_PATH_AUTO);
+        if (rc) return rc;
+    }
+    if (splice_grouped_workspace_size(groups, G, N, K, k) > ws_bytes) return SPLICE_ERR_WORKSPACE;
+    for (int32_t i = 0; i < G; i++) {
+        const splice_group &g = groups[i];
+        GemmArgs a{g.Xq, g.Xs, g.alpha_x, g.X_S, g.Wq, g.Ws, g.alpha_w, g.W_S, g.M, N, K, k, g.Y, N};
+        int rc = run_gemm(a, ws, ws_bytes, SPLICE_PATH_AUTO, hs(stream));
+        if (rc) return rc;
+    }
+    return SPLICE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// common.hpp -- device-side building blocks shared by the SpliceGEMM kernels
+// (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splice {
+
+typedef _Float16 f16;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr int WAVE = 64;
+constexpr int NVFP4_BLOCK = 16;
+
+// ---------------------------------------------------------------------------
+// Exact NVFP4 -> FP16 decode.
+//
+// An E2M1 value (at most 2 significant bits) times an E4M3 block scale (4
+// significant bits, 2^-9 .. 448) has at most 6 significant bits and lies in
+// [2^-10, 2688]: it is exactly representable as an FP16 normal number.  The
+// gfx950 FP4 conversion applies only the exponent of its scale operand, so the
+// codes are converted with scale 1.0 and the E4M3 scale is applied with a
+// packed FP16 multiply, which is exact because the product is representable.
+// ---------------------------------------------------------------------------
+
+// (s, s) as FP16 from one E4M3FN byte.
+__device__ __forceinline__ f16x2 e4m3_pair(unsigned byte)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte * 0x0101u, 1.0f, false);
+}
+
+// 8 FP4 codes (one dword, code 0 in bits 3:0) times scale pair -> 8 FP16 values
+// in channel order, as one MFMA operand.
+__device__ __forceinline__ f16x8 decode8(unsigned codes, f16x2 sc)
+{
+    f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sc;
+    f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sc;
+    f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sc;
+    f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sc;
+    return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// v_mfma_f32_16x16x32_{f16,bf16}: lane l holds row (l%16) of A and column
+// (l%16) of B at reduction indices 8*(l/16) .. +8; the 16x16 result in lane l
+// is rows 4*(l/16) .. +4 of column l%16.
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 bf16 values (16 bytes) of a side buffer row, zero past `valid` elements.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p, int valid, bool aligned16)
+{
+    if (valid >= 8 && aligned16) {
+        u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+        return __builtin_bit_cast(bf16x8, v);
+    }
+    uint16_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) t[i] = (i < valid) ? p[i] : (uint16_t)0;
+    u32x4 v;
+    v.x = t[0] | ((unsigned)t[1] << 16);
+    v.y = t[2] | ((unsigned)t[3] << 16);
+    v.z = t[4] | ((unsigned)t[5] << 16);
+    v.w = t[6] | ((unsigned)t[7] << 16);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+}  // namespace splice

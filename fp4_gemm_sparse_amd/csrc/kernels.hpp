@@ -1,0 +1,42 @@
+// kernels.hpp -- internal launchers behind the C ABI (not exported).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace splice {
+
+// channel statistics + top-k (+ frozen activation scale)
+hipError_t launch_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int64_t count_prev,
+                        double *mean, double *m2, float *absmax, hipStream_t s);
+hipError_t launch_select(const double *m2, const float *absmax, int64_t K, int32_t k,
+                         int32_t *idx, float *alpha_x, hipStream_t s);
+
+// masked amax -> alpha
+size_t alpha_ws_bytes();
+hipError_t launch_alpha(const uint16_t *A, int64_t R, int64_t K, int64_t lda, const int32_t *idx,
+                        int32_t k, float *alpha, void *ws, hipStream_t s);
+
+// mask + NVFP4 quantize + side gather
+hipError_t launch_quantize(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
+                           const int32_t *idx, int32_t k, const float *alpha, uint8_t *codes,
+                           uint8_t *scales, uint16_t *side, hipStream_t s);
+
+// GEMMs
+struct GemmArgs {
+    const uint8_t *Xq, *Xs;
+    const float *alpha_x;
+    const uint16_t *X_S;
+    const uint8_t *Wq, *Ws;
+    const float *alpha_w;
+    const uint16_t *W_S;
+    int64_t M, N, K;
+    int32_t k;
+    float *Y;
+    int64_t ldy;
+};
+enum class Path { Decode, Prefill };
+size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace splice

@@ -1,0 +1,231 @@
+"""Thin Python binding of libsplice.so (C ABI in include/splice.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library; torch provides device memory and the current HIP
+stream.  The library must have been built (python -m fp4_gemm_sparse_amd.build);
+loading fails loudly otherwise -- there is no fallback.
+
+bf16 tensors may be torch.bfloat16 or 16-bit integer tensors holding bf16 bit
+patterns; codes and scales are torch.uint8; idx is torch.int32; tensor scales
+(alpha) are float32 device tensors of one element.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsplice.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "splice.h")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+DECODE_MAX_M = 64
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class SpliceError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({lib().splice_status_string(status).decode()})")
+
+
+class _Group(ctypes.Structure):
+    _fields_ = [("Xq", _vp), ("Xs", _vp), ("alpha_x", _vp), ("X_S", _vp), ("Wq", _vp), ("Ws", _vp),
+                ("alpha_w", _vp), ("W_S", _vp), ("M", _i64), ("Y", _vp)]
+
+
+_SIGS = {
+    "splice_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "splice_select_channels": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, ctypes.POINTER(_i64),
+                                              _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "splice_select_workspace_size": (_sz, [_i64]),
+    "splice_compute_alpha": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "splice_alpha_workspace_size": (_sz, []),
+    "splice_quantize_nvfp4": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp,
+                                             _vp]),
+    "splice_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
+                                   _vp, _i64, _vp, _sz, ctypes.c_int, _vp]),
+    "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
+                                  _sz, ctypes.c_int, _vp]),
+    "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "splice_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32, _vp, _sz,
+                                           _vp]),
+    "splice_grouped_workspace_size": (_sz, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32]),
+}
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fp4_gemm_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/splice.h declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _p(t):
+    if t is None:
+        return None
+    return _vp(t.data_ptr())
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != OK:
+        raise SpliceError(fn, rc)
+
+
+def _bf16(t):
+    assert t.dtype in (torch.bfloat16, torch.int16, torch.uint16), t.dtype
+    assert t.is_cuda
+    return t
+
+
+def _idx(idx, device):
+    if idx is None:
+        return torch.zeros(0, dtype=torch.int32, device=device)
+    assert idx.dtype == torch.int32 and idx.is_cuda
+    return idx
+
+
+# ------------------------------------------------------------------ entry points
+@dataclass
+class ChannelStats:
+    """Running per-channel moments kept on the device."""
+    count: int
+    mean: torch.Tensor     # float64 [K]
+    m2: torch.Tensor       # float64 [K]
+    absmax: torch.Tensor   # float32 [K]
+
+    @staticmethod
+    def empty(K, device="cuda"):
+        return ChannelStats(0, torch.zeros(K, dtype=torch.float64, device=device),
+                            torch.zeros(K, dtype=torch.float64, device=device),
+                            torch.zeros(K, dtype=torch.float32, device=device))
+
+
+def select_channels(X, k, stats: ChannelStats | None = None, ldx=None, T=None):
+    """Fold the rows of X (bf16 [T, K]) into `stats` and select the top-k
+    channels.  Returns (idx int32 [k] ascending, alpha_x float32 [1], stats)."""
+    X = _bf16(X)
+    K = X.shape[-1]
+    if ldx is None:
+        ldx = X.stride(0) if X.dim() == 2 else K
+    if T is None:
+        T = X.shape[0]
+    if stats is None:
+        stats = ChannelStats.empty(K, X.device)
+    idx = torch.empty(k, dtype=torch.int32, device=X.device)
+    alpha = torch.empty(1, dtype=torch.float32, device=X.device)
+    cnt = _i64(stats.count)
+    _check("splice_select_channels",
+           lib().splice_select_channels(_p(X), T, K, ldx, k, ctypes.byref(cnt), _p(stats.mean),
+                                        _p(stats.m2), _p(stats.absmax), _p(idx), _p(alpha), None, 0,
+                                        _stream()))
+    stats.count = cnt.value
+    return idx, alpha, stats
+
+
+def compute_alpha(A, idx=None, out=None):
+    A = _bf16(A)
+    R, K = A.shape
+    idx = _idx(idx, A.device)
+    alpha = out if out is not None else torch.empty(1, dtype=torch.float32, device=A.device)
+    ws = torch.empty(lib().splice_alpha_workspace_size(), dtype=torch.uint8, device=A.device)
+    _check("splice_compute_alpha",
+           lib().splice_compute_alpha(_p(A), R, K, A.stride(0), _p(idx), idx.numel(), _p(alpha),
+                                      _p(ws), ws.numel(), _stream()))
+    return alpha
+
+
+def quantize_nvfp4(A, idx, alpha, out=None):
+    """Returns (codes uint8 [R, K/2], scales uint8 [R, K/16], side bf16-bits [R, k])."""
+    A = _bf16(A)
+    R, K = A.shape
+    idx = _idx(idx, A.device)
+    k = idx.numel()
+    if out is None:
+        codes = torch.empty(R, K // 2, dtype=torch.uint8, device=A.device)
+        scales = torch.empty(R, K // 16, dtype=torch.uint8, device=A.device)
+        side = torch.empty(R, k, dtype=torch.int16, device=A.device)
+    else:
+        codes, scales, side = out
+    _check("splice_quantize_nvfp4",
+           lib().splice_quantize_nvfp4(_p(A), R, K, A.stride(0), _p(idx), k, _p(alpha), _p(codes),
+                                       _p(scales), _p(side) if k else None, _stream()))
+    return codes, scales, side
+
+
+def workspace_size(M, N, K, k=0):
+    return lib().splice_workspace_size(M, N, K, k)
+
+
+def splice_gemm(Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, path=PATH_AUTO, out=None, ws=None):
+    M, K = Xq.shape[0], Xq.shape[1] * 2
+    N = Wq.shape[0]
+    k = 0 if X_S is None else X_S.shape[1]
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    need = workspace_size(M, N, K, k) if path != PATH_PREFILL else 0
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+    _check("splice_gemm",
+           lib().splice_gemm(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, _p(Wq), _p(Ws),
+                             _p(alpha_w), _p(W_S) if k else None, M, N, K, k, _p(Y), Y.stride(0),
+                             _p(ws), 0 if ws is None else ws.numel(), path, _stream()))
+    return Y
+
+
+def nvfp4_gemm(Xq, Xs, alpha_x, Wq, Ws, alpha_w, path=PATH_AUTO, out=None, ws=None):
+    M, K = Xq.shape[0], Xq.shape[1] * 2
+    N = Wq.shape[0]
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    need = workspace_size(M, N, K, 0) if path != PATH_PREFILL else 0
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+    _check("nvfp4_gemm",
+           lib().nvfp4_gemm(_p(Xq), _p(Xs), _p(alpha_x), _p(Wq), _p(Ws), _p(alpha_w), M, N, K, _p(Y),
+                            Y.stride(0), _p(ws), 0 if ws is None else ws.numel(), path, _stream()))
+    return Y
+
+
+def splice_gemm_grouped(groups, N, K, k, ws=None):
+    """groups: list of dicts with keys Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, Y (device
+    tensors; Y fp32 [M, N]).  Each group's M is Xq.shape[0]."""
+    arr = (_Group * len(groups))()
+    for i, g in enumerate(groups):
+        arr[i] = _Group(_p(g["Xq"]), _p(g["Xs"]), _p(g["alpha_x"]), _p(g["X_S"]) if k else None,
+                        _p(g["Wq"]), _p(g["Ws"]), _p(g["alpha_w"]), _p(g["W_S"]) if k else None,
+                        g["Xq"].shape[0], _p(g["Y"]))
+    need = lib().splice_grouped_workspace_size(arr, len(groups), N, K, k)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _check("splice_gemm_grouped",
+           lib().splice_gemm_grouped(arr, len(groups), N, K, k, _p(ws), 0 if ws is None else ws.numel(),
+                                     _stream()))

@@ -1,0 +1,185 @@
+/*
+ * splice.h -- C ABI of libsplice.so, SpliceGEMM on AMD Instinct MI355X (gfx950).
+ *
+ * SpliceGEMM is the W4A4 NVFP4 linear layer of the FourSight paper
+ * (arXiv 2611.04887v1, Sec. 4.2 and 5.1): the K input channels are split into
+ * a small protected set S, kept in BF16, and its complement, quantized to NVFP4
+ * after the protected coordinates are set to zero (App. 9.3.1):
+ *
+ *     Y = alpha_X * alpha_W * deq(Xq) deq(Wq)^T  +  X_S W_S^T        (fp32)
+ *
+ * Number formats (NVFP4, Sec. 2.1):
+ *   codes   uint8 [R, K/2]   E2M1 nibbles, channel 2i in the low nibble of
+ *                            byte i; nibble = sign<<3 | magnitude code, the
+ *                            magnitude codes 0..7 standing for 0, 0.5, 1, 1.5,
+ *                            2, 3, 4, 6
+ *   scales  uint8 [R, K/16]  one OCP E4M3FN byte per 16-channel block
+ *                            (non-negative, finite), row-major
+ *   alpha   float            FP32 tensor scale (a decode scale: value =
+ *                            alpha * e2m1 * e4m3), passed as a DEVICE pointer
+ *   side    bf16  [R, k]     the protected columns A[:, idx[i]], bit for bit
+ *   bf16 tensors are passed as uint16_t bit patterns.
+ *
+ * Quantization rule (App. 9.3.1 Eq. 9 with encode gain 1/alpha; round-to-
+ * nearest-even decisions taken on exact real quotients):
+ *   a_b = max |x_j| over the block, protected lanes counted as +0
+ *   s_b = E4M3FN(a_b / (6 alpha)), ties to even, saturating at 448
+ *   code = nearest E2M1 magnitude to |x| / (s_b alpha), ties to the even code,
+ *          saturating at 6; 0 when s_b = 0; protected lanes give nibble 0
+ *   alpha (splice_compute_alpha, splice_select_channels) = fp32(amax / 2688)
+ *          over the unprotected entries, 1 when that maximum is 0
+ *
+ * General rules for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller unless marked HOST.  The
+ *     library allocates and frees nothing; scratch comes in through `ws`.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is asynchronous.
+ *     Argument errors are detected on the host and returned synchronously
+ *     before anything is enqueued; a launch failure returns SPLICE_ERR_HIP.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Shapes: K % 16 == 0 (NVFP4 block), 0 <= k <= K, K <= 65536,
+ *     M, N, R, T >= 0 (zero sizes are no-ops).  idx holds k strictly
+ *     ascending channel indices in [0, K) (a DEVICE array; its order is the
+ *     caller's contract and is not checked).
+ *   - Row strides (lda, ldx, ldy) are in elements and must be >= the row
+ *     length.  Buffers must be 16-byte aligned.
+ *   - Functions are stateless and thread-safe; calls that share output or
+ *     workspace buffers must be ordered by the caller.
+ *   - Results do not depend on the path taken or the launch configuration
+ *     except for fp32 rounding order in the GEMM accumulators.
+ */
+#ifndef SPLICE_H
+#define SPLICE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *splice_stream_t;   /* == hipStream_t */
+
+typedef enum {
+    SPLICE_OK = 0,
+    SPLICE_ERR_INVALID_ARG = -1,   /* bad pointer, size, stride or alignment */
+    SPLICE_ERR_UNSUPPORTED = -2,   /* valid but outside what the kernels handle */
+    SPLICE_ERR_WORKSPACE = -3,     /* ws too small (see the *_workspace_size calls) */
+    SPLICE_ERR_HIP = -4            /* the HIP runtime reported an error */
+} splice_status;
+
+enum { SPLICE_PATH_AUTO = 0, SPLICE_PATH_DECODE = 1, SPLICE_PATH_PREFILL = 2 };
+
+/* Largest M the automatic dispatch sends to the decode (weight-streaming)
+ * path.  The paper switches at 32 tokens (Sec. 5.1); this build uses 64. */
+#define SPLICE_DECODE_MAX_M 64
+
+/* Human-readable name of a status code (static string). */
+const char *splice_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * Channel statistics and top-k selection (Sec. 4.2 variance-based selection;
+ * Sec. 5.2 running channel moments from token rows).
+ *
+ * Folds the T rows of X (bf16 [T, K], row stride ldx -- a stride that is a
+ * multiple of K subsamples rows) into running per-channel moments, then
+ * selects the k channels with the largest M2 (equivalently the largest
+ * variance: every channel has the same count), ties to the lower index,
+ * written to idx[0..k) in ascending order.
+ *   count   HOST in/out: rows already folded into mean/m2/absmax; 0 means the
+ *           running buffers are ignored and overwritten.  Updated to count+T.
+ *   mean, m2  double [K] in/out (sum of squared deviations)
+ *   absmax  float [K] in/out
+ *   idx     int32 [k] out
+ *   alpha_x float [1] out (may be NULL): the frozen activation scale
+ *           fp32(max over unprotected channels of absmax / 2688), 1 if 0.
+ * Arithmetic: Welford inside 64-row tiles, tiles folded left to right with the
+ * pairwise update of Chan, Golub & LeVeque, then merge(running, batch); every
+ * step in fp64 with one IEEE rounding per operation, so the result is
+ * bit-identical to a sequential evaluation in that order.
+ * ws: splice_select_workspace_size(K) bytes. */
+int splice_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int32_t k,
+                           int64_t *count, double *mean, double *m2, float *absmax,
+                           int32_t *idx, float *alpha_x,
+                           void *ws, size_t ws_bytes, splice_stream_t stream);
+size_t splice_select_workspace_size(int64_t K);
+
+/* ---------------------------------------------------------------------------
+ * alpha = fp32(max |A| over the unprotected columns / 2688), 1 if that is 0
+ * (Sec. 2.1 FP32 tensor scale; App. 9.3.1 Eq. 9).  A: bf16 [R, K], stride
+ * lda.  alpha: float [1] out.  ws: splice_alpha_workspace_size() bytes. */
+int splice_compute_alpha(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
+                         const int32_t *idx, int32_t k, float *alpha,
+                         void *ws, size_t ws_bytes, splice_stream_t stream);
+size_t splice_alpha_workspace_size(void);
+
+/* ---------------------------------------------------------------------------
+ * Mask, quantize and gather (Sec. 5.1 data preparation; weight pre-split):
+ * one pass over A (bf16 [R, K], stride lda) writes the NVFP4 codes and block
+ * scales of the masked residual and the protected columns.
+ *   alpha  float [1] in (DEVICE), > 0 and finite
+ *   codes  uint8 [R, K/2] out;  scales uint8 [R, K/16] out
+ *   side   bf16 [R, k] out (may be NULL when k == 0) */
+int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
+                          const int32_t *idx, int32_t k, const float *alpha,
+                          uint8_t *codes, uint8_t *scales, uint16_t *side,
+                          splice_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * SpliceGEMM (Sec. 4.2 Eq. 5; Sec. 5.1 dual-path execution):
+ *   Y[m, n] = alpha_x*alpha_w * sum_j deq(Xq)[m, j] deq(Wq)[n, j]
+ *             + sum_i X_S[m, i] W_S[n, i]
+ * Xq/Xs: [M, K/2] / [M, K/16];  Wq/Ws: [N, K/2] / [N, K/16];
+ * X_S: bf16 [M, k], W_S: bf16 [N, k] (unscaled, bit copies of the protected
+ * columns); Y: fp32 [M, N] out with row stride ldy.
+ * The NVFP4 products are decoded exactly to BF16 and multiplied on the BF16
+ * matrix cores with fp32 accumulation; the accumulator is scaled by
+ * alpha_x*alpha_w before the BF16 side product is added into it.
+ * path: SPLICE_PATH_AUTO (decode path when M <= SPLICE_DECODE_MAX_M),
+ *       SPLICE_PATH_DECODE (requires M <= SPLICE_DECODE_MAX_M) or
+ *       SPLICE_PATH_PREFILL.
+ * ws: splice_workspace_size(M, N, K, k) bytes (0 is allowed when that is 0). */
+int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
+                const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
+                int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy,
+                void *ws, size_t ws_bytes, int path, splice_stream_t stream);
+
+/* Plain NVFP4 GEMM without compensation, the overhead baseline (the paper's
+ * uncompensated FP4, Sec. 6.3): splice_gemm with k = 0. */
+int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x,
+               const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w,
+               int64_t M, int64_t N, int64_t K, float *Y, int64_t ldy,
+               void *ws, size_t ws_bytes, int path, splice_stream_t stream);
+
+/* Workspace bytes splice_gemm / nvfp4_gemm need for this shape (k is
+ * ignored by the current kernels but part of the contract). */
+size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
+
+/* ---------------------------------------------------------------------------
+ * Grouped SpliceGEMM: G independent problems sharing N, K and k (experts of
+ * an MoE layer, each with its own S, alphas and token count M; the paper's
+ * Nemotron3 Up/Down projections, Sec. 6.3).  groups is a HOST array; each
+ * entry's pointers are device pointers laid out as for splice_gemm, with
+ * ldy = N.  Groups with M == 0 are skipped.  Each group takes the path the
+ * automatic dispatch would give it.
+ * ws: splice_grouped_workspace_size(groups, G, N, K, k) bytes. */
+typedef struct {
+    const uint8_t *Xq, *Xs;
+    const float *alpha_x;
+    const uint16_t *X_S;
+    const uint8_t *Wq, *Ws;
+    const float *alpha_w;
+    const uint16_t *W_S;
+    int64_t M;
+    float *Y;
+} splice_group;
+
+int splice_gemm_grouped(const splice_group *groups, int32_t G, int64_t N, int64_t K, int32_t k,
+                        void *ws, size_t ws_bytes, splice_stream_t stream);
+size_t splice_grouped_workspace_size(const splice_group *groups, int32_t G, int64_t N,
+                                     int64_t K, int32_t k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLICE_H */

@@ -1,0 +1,128 @@
+"""C ABI of libsplice.so on the CPU: the library loads, exports every function
+include/splice.h declares, and rejects bad arguments on the host before it
+touches a GPU (no compute call is made here)."""
+import ctypes
+
+import pytest
+
+from fp4_gemm_sparse_amd import splice
+
+FAKE = 0x100000          # a 16-byte aligned non-null address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    return splice.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = splice.header_functions()
+    assert {"splice_select_channels", "splice_quantize_nvfp4", "splice_gemm", "nvfp4_gemm",
+            "splice_compute_alpha", "splice_gemm_grouped", "splice_workspace_size"} <= set(names)
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.splice_status_string(code), bytes)
+
+
+def gemm(L, M=64, N=64, K=256, k=8, path=0, ws=None, wsb=0, **over):
+    args = dict(Xq=FAKE, Xs=FAKE, ax=FAKE, XS=FAKE, Wq=FAKE, Ws=FAKE, aw=FAKE, WS=FAKE, Y=FAKE,
+                ldy=N)
+    args.update(over)
+    return L.splice_gemm(args["Xq"], args["Xs"], args["ax"], args["XS"], args["Wq"], args["Ws"],
+                         args["aw"], args["WS"], M, N, K, k, args["Y"], args["ldy"], ws, wsb, path,
+                         None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=100), splice.ERR_INVALID_ARG),            # K % 16
+    (dict(K=256, k=257), splice.ERR_INVALID_ARG),     # k > K
+    (dict(k=-1), splice.ERR_INVALID_ARG),
+    (dict(M=-1), splice.ERR_INVALID_ARG),
+    (dict(K=144), splice.ERR_UNSUPPORTED),            # GEMM kernels need K % 128
+    (dict(K=131072), splice.ERR_UNSUPPORTED),         # beyond the largest K
+    (dict(path=7), splice.ERR_INVALID_ARG),
+    (dict(M=65, path=splice.PATH_DECODE), splice.ERR_INVALID_ARG),
+    (dict(Y=None), splice.ERR_INVALID_ARG),
+    (dict(ax=None), splice.ERR_INVALID_ARG),
+    (dict(Xq=None), splice.ERR_INVALID_ARG),
+    (dict(XS=None), splice.ERR_INVALID_ARG),
+    (dict(Xq=FAKE + 4), splice.ERR_INVALID_ARG),      # misaligned codes
+    (dict(ldy=10), splice.ERR_INVALID_ARG),
+    (dict(M=0), splice.OK),                           # no-op
+    (dict(N=0), splice.OK),
+])
+def test_gemm_argument_errors(L, kw, code):
+    assert gemm(L, **kw) == code
+
+
+def test_gemm_workspace_error(L):
+    # M=1 with a long K splits K across workgroups and needs a workspace
+    need = L.splice_workspace_size(1, 1024, 4096, 64)
+    assert need > 0
+    assert gemm(L, M=1, N=1024, K=4096, k=64) == splice.ERR_WORKSPACE
+    assert gemm(L, M=1, N=1024, K=4096, k=64, ws=FAKE, wsb=need - 1) == splice.ERR_WORKSPACE
+    assert L.splice_workspace_size(0, 1024, 4096, 64) == 0
+    assert L.splice_workspace_size(8192, 4096, 4096, 64) == 0     # prefill needs none
+
+
+def test_nvfp4_argument_errors(L):
+    assert L.nvfp4_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 4, None, 0, 0, None) \
+        == splice.ERR_INVALID_ARG
+    assert L.nvfp4_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 128, FAKE, 4, None, 0, 0, None) \
+        == splice.OK
+
+
+def test_quantize_argument_errors(L):
+    q = L.splice_quantize_nvfp4
+    assert q(FAKE, 4, 100, 100, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert q(FAKE, 4, 64, 32, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # lda < K
+    assert q(FAKE, 4, 64, 64, None, 1, FAKE, FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # idx
+    assert q(FAKE, 4, 64, 64, FAKE, 1, FAKE, FAKE, FAKE, None, None) == splice.ERR_INVALID_ARG   # side
+    assert q(FAKE, 4, 64, 64, FAKE, 0, None, FAKE, FAKE, None, None) == splice.ERR_INVALID_ARG   # alpha
+    assert q(FAKE, 4, 64, 68, FAKE, 0, FAKE, FAKE, FAKE, None, None) == splice.ERR_UNSUPPORTED   # lda % 8
+    assert q(FAKE + 2, 4, 64, 64, FAKE, 0, FAKE, FAKE, FAKE, None, None) == splice.ERR_UNSUPPORTED
+    assert q(FAKE, 0, 64, 64, FAKE, 0, FAKE, FAKE, FAKE, None, None) == splice.OK              # R = 0
+
+
+def test_select_argument_errors(L):
+    s = L.splice_select_channels
+    cnt = ctypes.c_int64(0)
+    assert s(FAKE, 16, 64, 64, 65, ctypes.byref(cnt), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) \
+        == splice.ERR_INVALID_ARG                                   # k > K
+    assert s(FAKE, 16, 64, 64, 4, None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) \
+        == splice.ERR_INVALID_ARG                                   # count
+    assert s(FAKE, 16, 64, 32, 4, ctypes.byref(cnt), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) \
+        == splice.ERR_INVALID_ARG                                   # ldx < K
+    assert s(FAKE, 16, 64, 64, 4, ctypes.byref(cnt), FAKE, FAKE, FAKE, None, None, None, 0, None) \
+        == splice.ERR_INVALID_ARG                                   # idx
+    neg = ctypes.c_int64(-3)
+    assert s(FAKE, 16, 64, 64, 4, ctypes.byref(neg), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) \
+        == splice.ERR_INVALID_ARG
+    assert L.splice_select_workspace_size(4096) == 0
+
+
+def test_alpha_argument_errors(L):
+    a = L.splice_compute_alpha
+    need = L.splice_alpha_workspace_size()
+    assert need > 0
+    assert a(FAKE, 4, 64, 64, FAKE, 0, FAKE, None, 0, None) == splice.ERR_WORKSPACE
+    assert a(FAKE, 4, 64, 64, FAKE, 0, FAKE, FAKE, need - 4, None) == splice.ERR_WORKSPACE
+    assert a(FAKE, 4, 64, 64, FAKE, 0, None, FAKE, need, None) == splice.ERR_INVALID_ARG
+    assert a(FAKE, 4, 60, 64, FAKE, 0, FAKE, FAKE, need, None) == splice.ERR_INVALID_ARG
+
+
+def test_grouped_argument_errors(L):
+    G = splice._Group
+    arr = (G * 2)()
+    arr[0] = G(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE)
+    arr[1] = G(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None)     # no Y
+    assert L.splice_gemm_grouped(arr, 2, 64, 256, 8, None, 0, None) == splice.ERR_INVALID_ARG
+    assert L.splice_gemm_grouped(arr, 0, 64, 256, 8, None, 0, None) == splice.OK
+    assert L.splice_gemm_grouped(None, 2, 64, 256, 8, None, 0, None) == splice.ERR_INVALID_ARG
+    empty = (G * 1)()
+    empty[0] = G(None, None, None, None, None, None, None, None, 0, None)    # M = 0 group
+    assert L.splice_gemm_grouped(empty, 1, 64, 256, 8, None, 0, None) == splice.OK

@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded bf16 inputs.
+
+Bit-exact: channel statistics (fp64 moments, absmax), selected indices, every
+tensor scale, NVFP4 codes, block scales and side buffers.  GEMM outputs: the
+tolerance in gpu_util (relative Frobenius 1e-5; per element 1e-3 relative with
+a 1e-6 absolute floor).  The oracle always quantizes the bf16 inputs itself;
+nothing computed on the GPU is fed to it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_gemm_sparse_amd import splice as S
+from fp4_gemm_sparse_amd import synth
+from gpu_util import assert_gemm_close, dev, host, scalar
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def special_rows(R, K, seed):
+    """normal data with outliers plus rows of zeros, negative zeros, tiny,
+    huge and mixed-magnitude blocks."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((R, K)) * (2.0 ** g.integers(-8, 8, (R, 1)))
+    ch = g.choice(K, size=min(K, 8), replace=False)
+    x[:, ch] *= 40.0
+    if R > 4:
+        x[0] = 0.0
+        x[1, : K // 2] = -0.0
+        x[2] *= 1e-30
+        x[3, :16] = 3e38
+        x[4, ::7] = 1e-38
+    return synth.to_bf16(x)
+
+
+# ------------------------------------------------------------------ quantize / alpha
+QCASES = [(1, 16, 0), (7, 48, 1), (64, 256, 5), (130, 1024, 64), (33, 4096, 64), (300, 1024, 256),
+          (16, 128, 128), (5, 12288, 64)]
+
+
+@pytest.mark.parametrize("R,K,k", QCASES)
+def test_alpha_and_quantize_bit_exact(R, K, k):
+    A = special_rows(R, K, R * 31 + K + k)
+    g = np.random.default_rng(K + k)
+    idx = np.sort(g.choice(K, size=k, replace=False)).astype(np.int32)
+    a_o = O.compute_alpha(A, idx)
+    Ad, idxd = dev(A), dev(idx)
+    a_g = S.compute_alpha(Ad, idxd)
+    assert scalar(a_g) == np.float32(a_o)
+    for alpha in (a_o, np.float32(1.0), np.float32(2.0 ** -20), np.float32(0.37)):
+        c_o, s_o, side_o = O.quantize_nvfp4(A, idx, alpha)
+        c_g, s_g, side_g = S.quantize_nvfp4(Ad, idxd, dev(np.array([alpha], np.float32)))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(s_g), s_o), "scales"
+        assert np.array_equal(host(c_g), c_o), "codes"
+        assert np.array_equal(host(side_g), side_o), "side"
+
+
+def test_quantize_all_protected_and_strided_rows():
+    A = special_rows(9, 64, 3)
+    idx = np.arange(64, dtype=np.int32)
+    c_g, s_g, side_g = S.quantize_nvfp4(dev(A), dev(idx), dev(np.array([0.5], np.float32)))
+    assert not host(c_g).any() and not host(s_g).any()
+    assert np.array_equal(host(side_g), A)
+    # a row stride larger than K (a view of every other 64-channel half)
+    B = special_rows(6, 128, 4)
+    Bd = dev(B)[:, :64]
+    idx = np.array([1, 17, 40], np.int32)
+    c_o, s_o, side_o = O.quantize_nvfp4(np.ascontiguousarray(B[:, :64]), idx, np.float32(0.01))
+    c_g, s_g, side_g = S.quantize_nvfp4(Bd, dev(idx), dev(np.array([0.01], np.float32)))
+    assert np.array_equal(host(c_g), c_o) and np.array_equal(host(s_g), s_o)
+    assert np.array_equal(host(side_g), side_o)
+
+
+# ------------------------------------------------------------------ stats / select
+@pytest.mark.parametrize("T,K,k", [(1, 16, 1), (63, 64, 8), (64, 1024, 64), (65, 1024, 0),
+                                   (512, 4096, 64), (1100, 1024, 256), (512, 12288, 64),
+                                   (100, 256, 256)])
+def test_stats_select_bit_exact(T, K, k):
+    X = synth.activations(7, T % 7, T, K, 2, "student", n_out=min(64, K // 4))
+    st_o = O.stats(X)
+    idx_o = O.select_topk(st_o.m2, k)
+    ax_o = O.alpha_from_absmax(st_o.absmax, idx_o)
+    idx_g, ax_g, st_g = S.select_channels(dev(X), k)
+    assert st_g.count == T
+    assert np.array_equal(host(st_g.mean).view(np.uint64), st_o.mean.view(np.uint64))
+    assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
+    assert np.array_equal(host(st_g.absmax), st_o.absmax)
+    assert np.array_equal(host(idx_g), idx_o)
+    assert scalar(ax_g) == np.float32(ax_o)
+
+
+def test_select_ties_and_running_merge():
+    g = np.random.default_rng(5)
+    K = 256
+    base = g.standard_normal((96, K // 4))
+    X = synth.to_bf16(np.repeat(base, 4, axis=1))        # every channel value appears 4 times
+    Y = synth.to_bf16(g.standard_normal((70, K)))
+    st_o = O.stats(X).update(Y)
+    idx_o = O.select_topk(st_o.m2, 30)
+    st_g = S.ChannelStats.empty(K)
+    S.select_channels(dev(X), 30, st_g)
+    idx_g, ax_g, st_g = S.select_channels(dev(Y), 30, st_g)
+    assert st_g.count == 166
+    assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
+    assert np.array_equal(host(idx_g), idx_o)
+    # the tie structure: first call alone has exact 4-way ties
+    st1 = O.stats(X)
+    idx1 = O.select_topk(st1.m2, 30)
+    idx1_g, _, _ = S.select_channels(dev(X), 30)
+    assert np.array_equal(host(idx1_g), idx1)
+
+
+def test_select_row_stride_subsamples():
+    X = synth.activations(7, 1, 200, 128, 2, "normal")
+    Xd = dev(X)
+    st_o = O.stats(X[::2])
+    idx_o = O.select_topk(st_o.m2, 16)
+    idx_g, _, st_g = S.select_channels(Xd, 16, ldx=256, T=100)
+    assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
+    assert np.array_equal(host(idx_g), idx_o)
+
+
+# ------------------------------------------------------------------ GEMM
+def oracle_pipeline(X_warm, X, W, k, rows=None, cols=None, idx=None):
+    """The oracle's own calibration, packs and product (optionally on a row /
+    column sample of the full problem)."""
+    if idx is None:
+        idx, ax, _ = O.select_channels(X_warm, k)
+    else:
+        ax = O.alpha_from_absmax(O.stats(X_warm).absmax, idx)
+    aw = O.compute_alpha(W, idx)
+    Xs_ = X if rows is None else X[rows]
+    Ws_ = W if cols is None else W[cols]
+    xq, xs, xS = O.quantize_nvfp4(Xs_, idx, ax)
+    wq, ws, wS = O.quantize_nvfp4(Ws_, idx, aw)
+    Y = O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
+    return dict(idx=idx, ax=ax, aw=aw, Y=Y, xq=xq, xs=xs, wq=wq, ws=ws)
+
+
+def gpu_pipeline(X_warm, X, W, k, path=S.PATH_AUTO):
+    Xw, Xd, Wd = dev(X_warm), dev(X), dev(W)
+    idx_g, ax_g, _ = S.select_channels(Xw, k)
+    aw_g = S.compute_alpha(Wd, idx_g)
+    xq, xs, xS = S.quantize_nvfp4(Xd, idx_g, ax_g)
+    wq, ws, wS = S.quantize_nvfp4(Wd, idx_g, aw_g)
+    Y = S.splice_gemm(xq, xs, ax_g, xS if k else None, wq, ws, aw_g, wS if k else None, path=path)
+    torch.cuda.synchronize()
+    return dict(idx=host(idx_g), ax=scalar(ax_g), aw=scalar(aw_g), Y=host(Y), xq=host(xq),
+                xs=host(xs), wq=host(wq), ws=host(ws))
+
+
+def test_tiny_config_end_to_end():
+    """M=128, K=N=1024, 64 protected channels from a 512-token warm-up."""
+    d = synth.tiny()
+    o = oracle_pipeline(d["X_warm"], d["X"], d["W"], 64)
+    g = gpu_pipeline(d["X_warm"], d["X"], d["W"], 64)
+    assert np.array_equal(g["idx"], o["idx"])
+    assert np.array_equal(g["idx"], d["outliers"])
+    assert g["ax"] == np.float32(o["ax"]) and g["aw"] == np.float32(o["aw"])
+    for key in ("xq", "xs", "wq", "ws"):
+        assert np.array_equal(g[key], o[key]), key
+    assert_gemm_close(g["Y"], o["Y"], "tiny prefill")
+    # the first 64 tokens through the decode path
+    g64 = gpu_pipeline(d["X_warm"], d["X"][:64], d["W"], 64, path=S.PATH_DECODE)
+    assert_gemm_close(g64["Y"], o["Y"][:64], "tiny decode")
+
+
+SHAPES = [(1, 16, 128, 0), (1, 100, 1024, 5), (8, 48, 256, 64), (16, 1000, 1024, 64),
+          (17, 64, 512, 31), (32, 1024, 1024, 1), (33, 80, 256, 64), (63, 130, 384, 64),
+          (64, 1024, 2048, 256), (65, 96, 256, 64), (128, 128, 1024, 0), (130, 1040, 1024, 64),
+          (200, 300, 640, 100), (257, 257, 128, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,k", SHAPES)
+def test_gemm_shapes_both_paths(M, N, K, k):
+    g = np.random.default_rng(M * 1000 + N + K + k)
+    X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
+    W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
+    idx = np.sort(g.choice(K, size=k, replace=False)).astype(np.int32)
+    ax, aw = np.float32(O.compute_alpha(X, idx)), np.float32(O.compute_alpha(W, idx))
+    xq, xs, xS = O.quantize_nvfp4(X, idx, ax)
+    wq, ws, wS = O.quantize_nvfp4(W, idx, aw)
+    Yo = O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
+    Xd, Wd, idxd = dev(X), dev(W), dev(idx)
+    axd, awd = S.compute_alpha(Xd, idxd), S.compute_alpha(Wd, idxd)
+    assert scalar(axd) == ax and scalar(awd) == aw
+    gx = S.quantize_nvfp4(Xd, idxd, axd)
+    gw = S.quantize_nvfp4(Wd, idxd, awd)
+    paths = [S.PATH_PREFILL] + ([S.PATH_DECODE] if M <= S.DECODE_MAX_M else [])
+    for path in paths:
+        Y = S.splice_gemm(gx[0], gx[1], axd, gx[2] if k else None, gw[0], gw[1], awd,
+                          gw[2] if k else None, path=path)
+        assert_gemm_close(host(Y), Yo, f"M={M} N={N} K={K} k={k} path={path}")
+    if k == 0:
+        Yn = S.nvfp4_gemm(gx[0], gx[1], axd, gw[0], gw[1], awd)
+        Ys = S.splice_gemm(gx[0], gx[1], axd, None, gw[0], gw[1], awd, None)
+        assert torch.equal(Yn, Ys)
+
+
+def test_output_row_stride():
+    g = np.random.default_rng(9)
+    M, N, K, k = 40, 64, 256, 16
+    X = synth.to_bf16(g.standard_normal((M, K)))
+    W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
+    idx = np.arange(0, 256, 16, dtype=np.int32)
+    o = oracle_pipeline(X, X, W, k, idx=idx)
+    Xd, Wd, idxd = dev(X), dev(W), dev(idx)
+    axd = S.compute_alpha(Xd, idxd)
+    awd = S.compute_alpha(Wd, idxd)
+    assert scalar(axd) == np.float32(o["ax"])
+    gx, gw = S.quantize_nvfp4(Xd, idxd, axd), S.quantize_nvfp4(Wd, idxd, awd)
+    for path in (S.PATH_DECODE, S.PATH_PREFILL):
+        big = torch.full((M, 100), 7.0, device="cuda")
+        S.splice_gemm(gx[0], gx[1], axd, gx[2], gw[0], gw[1], awd, gw[2], path=path, out=big[:, :N])
+        b = host(big)
+        assert_gemm_close(b[:, :N], o["Y"], f"ldy path {path}")
+        assert np.all(b[:, N:] == 7.0)
+
+
+# ------------------------------------------------------------------ full-size shapes, sampled
+@pytest.mark.parametrize("name", list(synth.QWEN3_8B))
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_decode_full_size_sampled(name, M):
+    p = synth.projection(synth.CFG_DECODE, name, M)
+    K, N = p["K"], p["N"]
+    cols = np.sort(np.random.default_rng(M).choice(N, size=128, replace=False))
+    o = oracle_pipeline(p["X_warm"], p["X"], p["W"], 64, cols=cols)
+    Xw, Xd, Wd = dev(p["X_warm"]), dev(p["X"]), dev(p["W"])
+    idx, ax, _ = S.select_channels(Xw, 64)
+    aw = S.compute_alpha(Wd, idx)
+    gx, gw = S.quantize_nvfp4(Xd, idx, ax), S.quantize_nvfp4(Wd, idx, aw)
+    Y = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
+    assert np.array_equal(host(idx), o["idx"])
+    assert scalar(ax) == np.float32(o["ax"]) and scalar(aw) == np.float32(o["aw"])
+    assert np.array_equal(host(gw[0])[cols], o["wq"]) and np.array_equal(host(gw[1])[cols], o["ws"])
+    assert_gemm_close(host(Y)[:, cols], o["Y"], f"{name} M={M}")
+
+
+@pytest.mark.parametrize("name", ["q", "k", "down"])
+def test_prefill_full_size_sampled(name):
+    M = 8192
+    p = synth.projection(synth.CFG_PREFILL, name, M)
+    K, N = p["K"], p["N"]
+    rs = np.random.default_rng(11)
+    rows = np.sort(rs.choice(M, size=48, replace=False))
+    cols = np.sort(rs.choice(N, size=96, replace=False))
+    o = oracle_pipeline(p["X_warm"], p["X"], p["W"], 64, rows=rows, cols=cols)
+    Xw, Xd, Wd = dev(p["X_warm"]), dev(p["X"]), dev(p["W"])
+    idx, ax, _ = S.select_channels(Xw, 64)
+    aw = S.compute_alpha(Wd, idx)
+    gx, gw = S.quantize_nvfp4(Xd, idx, ax), S.quantize_nvfp4(Wd, idx, aw)
+    Y = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
+    Yn = S.nvfp4_gemm(gx[0], gx[1], ax, gw[0], gw[1], aw)
+    assert np.array_equal(host(gx[0])[rows], o["xq"]) and np.array_equal(host(gx[1])[rows], o["xs"])
+    assert_gemm_close(host(Y)[np.ix_(rows, cols)], o["Y"], f"prefill {name}")
+    assert torch.isfinite(Yn).all()
+
+
+def test_grouped_moe_sampled():
+    counts = synth.moe_counts()
+    K, N, E = 4096, 2048, len(counts)
+    groups, refs = [], []
+    for e in range(E):
+        Me = int(counts[e])
+        Xw = synth.activations(synth.CFG_MOE, 100 + e, 512, K, 2, "student")
+        X = synth.activations(synth.CFG_MOE, 100 + e, Me, K, 3, "student")
+        W = synth.weights(synth.CFG_MOE, 200 + e, N, K)
+        Xwd, Xd, Wd = dev(Xw), dev(X), dev(W)
+        idx, ax, _ = S.select_channels(Xwd, 64)
+        aw = S.compute_alpha(Wd, idx)
+        gx = S.quantize_nvfp4(Xd, idx, ax) if Me else (Xd.new_zeros(0, K // 2, dtype=torch.uint8),
+                                                      Xd.new_zeros(0, K // 16, dtype=torch.uint8),
+                                                      Xd.new_zeros(0, 64, dtype=torch.int16))
+        gw = S.quantize_nvfp4(Wd, idx, aw)
+        Y = torch.full((Me, N), float("nan"), device="cuda")
+        groups.append(dict(Xq=gx[0], Xs=gx[1], alpha_x=ax, X_S=gx[2], Wq=gw[0], Ws=gw[1], alpha_w=aw,
+                           W_S=gw[2], Y=Y))
+        if e % 5 == 0 and Me:
+            cols = np.arange(0, N, 37)
+            refs.append((e, cols, oracle_pipeline(Xw, X, W, 64, cols=cols)))
+    S.splice_gemm_grouped(groups, N, K, 64)
+    torch.cuda.synchronize()
+    for e, cols, o in refs:
+        assert_gemm_close(host(groups[e]["Y"])[:, cols], o["Y"], f"expert {e}")
+    for g in groups:
+        assert torch.isfinite(g["Y"]).all()
