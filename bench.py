@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""SpliceGEMM benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (the value line): one Qwen3-8B-shaped layer in prefill, M = 8192
+tokens through the seven projections (q, k, v, o, gate, up, down) with 64
+protected BF16 channels each.  One step is the whole hot path over that batch:
+per projection, channel statistics and top-64 selection on a 512-token
+warm-up batch, the weight tensor scale, the weight pre-split (quantize + side
+gather), the activation preparation and the SpliceGEMM.  `value` is the
+step's useful work, sum of 2*M*N*K over the projections, divided by the step
+time (inputs resident in HBM).
+
+The same run also measures, each timed on its own: the projections' GEMMs
+against the plain NVFP4 GEMM on identical inputs (overhead), the decode
+shapes M in {1, 8, 32, 64} (HBM GB/s, weights rotated through more copies
+than the 256 MB last-level cache holds), the grouped MoE stand-in, and the
+fp64 CPU oracle on a bounded sample of the workload (cpu_baseline).
+All timing uses HIP events on the stream the kernels are launched on.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 matrix peak
+K_PROT = 64
+M_PREFILL = 8192
+DECODE_MS = (1, 8, 32, 64)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gemm_traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-iters", type=int, default=50)
+    ap.add_argument("--cpu-rows", type=int, default=16, help="token rows of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the value workload")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("common.hpp", "gemm.hip"):
+        h.update(open(os.path.join(ROOT, "fp4_gemm_sparse_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp4_gemm_sparse_amd import splice as S
+    from fp4_gemm_sparse_amd import synth
+
+    S.lib()                                   # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    names = list(synth.QWEN3_8B)
+
+    def gen(name):
+        return name, synth.projection(synth.CFG_PREFILL, name, M_PREFILL)
+
+    with ThreadPoolExecutor(8) as ex:
+        host = dict(ex.map(gen, names))
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+
+    P = {}
+    for n in names:
+        h = host[n]
+        K, N = h["K"], h["N"]
+        P[n] = dict(
+            K=K, N=N,
+            Xw=to_dev(h["X_warm"]), X=to_dev(h["X"]), W=to_dev(h["W"]),
+            stats=S.ChannelStats.empty(K),
+            idx=torch.empty(K_PROT, dtype=torch.int32, device=dev),
+            ax=torch.empty(1, dtype=torch.float32, device=dev),
+            aw=torch.empty(1, dtype=torch.float32, device=dev),
+            wpack=(torch.empty(N, K // 2, dtype=torch.uint8, device=dev),
+                   torch.empty(N, K // 16, dtype=torch.uint8, device=dev),
+                   torch.empty(N, K_PROT, dtype=torch.int16, device=dev)),
+            xpack=(torch.empty(M_PREFILL, K // 2, dtype=torch.uint8, device=dev),
+                   torch.empty(M_PREFILL, K // 16, dtype=torch.uint8, device=dev),
+                   torch.empty(M_PREFILL, K_PROT, dtype=torch.int16, device=dev)),
+            Y=torch.empty(M_PREFILL, N, dtype=torch.float32, device=dev),
+        )
+    alpha_ws = torch.empty(S.lib().splice_alpha_workspace_size(), dtype=torch.uint8, device=dev)
+    flops_step = sum(2.0 * M_PREFILL * P[n]["N"] * P[n]["K"] for n in names)
+
+    gemm_events = []
+
+    def step(record):
+        for n in names:
+            p = P[n]
+            p["stats"].count = 0
+            S.select_channels(p["Xw"], K_PROT, p["stats"], out=(p["idx"], p["ax"]))
+            S.compute_alpha(p["W"], p["idx"], out=p["aw"], ws=alpha_ws)
+            S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
+            S.quantize_nvfp4(p["X"], p["idx"], p["ax"], out=p["xpack"])
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            xq, xs, xS = p["xpack"]
+            wq, ws, wS = p["wpack"]
+            S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])
+            if record:
+                e1.record(stream)
+                gemm_events.append((n, e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s")
+
+    # dominant kernel: the prefill SpliceGEMM launches inside the timed steps
+    per = {n: [] for n in names}
+    for n, a, b in gemm_events:
+        per[n].append(a.elapsed_time(b))
+    gemm_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    flops = {n: 2.0 * M_PREFILL * P[n]["N"] * P[n]["K"] for n in names}
+    achieved = sum(flops.values()) / (sum(gemm_ms.values()) * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_sha") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+
+    result = {
+        "metric": "SpliceGEMM prefill TFLOP/s & decode HBM GB/s; % overhead vs plain NVFP4 GEMM",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "qwen3-8b-layer-prefill", "tokens": M_PREFILL,
+                   "projections": {n: [P[n]["K"], P[n]["N"]] for n in names},
+                   "protected_channels": K_PROT, "warmup_tokens": 512,
+                   "step": "stats+select, weight alpha+pre-split, activation prep, SpliceGEMM"},
+        "roofline": roofline,
+    }
+
+    if not args.no_extra:
+        result.update(extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream))
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args, host, names, flops_step / M_PREFILL)
+    print(json.dumps(result), flush=True)
+
+
+def timed(torch, stream, fn, iters):
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(iters):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
+    dev = torch.device("cuda:0")
+    out = {}
+    # ---------------- prefill overhead vs the plain NVFP4 GEMM on identical bf16 inputs
+    nv_ms, nv_full_ms, sp_full_ms = {}, {}, {}
+    empty = torch.zeros(0, dtype=torch.int32, device=dev)
+    for n in names:
+        p = P[n]
+        K, N = p["K"], p["N"]
+        ax0, aw0 = S.compute_alpha(p["X"], None), S.compute_alpha(p["W"], None)
+        xq0 = S.quantize_nvfp4(p["X"], empty, ax0)
+        wq0 = S.quantize_nvfp4(p["W"], empty, aw0)
+        Y0 = torch.empty_like(p["Y"])
+        for _ in range(3):
+            S.nvfp4_gemm(xq0[0], xq0[1], ax0, wq0[0], wq0[1], aw0, path=S.PATH_PREFILL, out=Y0)
+        nv_ms[n] = timed(torch, stream, lambda i: S.nvfp4_gemm(xq0[0], xq0[1], ax0, wq0[0], wq0[1], aw0,
+                                                              path=S.PATH_PREFILL, out=Y0), 10)
+        nv_full_ms[n] = timed(torch, stream, lambda i: (
+            S.quantize_nvfp4(p["X"], empty, ax0, out=xq0),
+            S.nvfp4_gemm(xq0[0], xq0[1], ax0, wq0[0], wq0[1], aw0, path=S.PATH_PREFILL, out=Y0)), 10)
+        xq, xs, xS = p["xpack"]
+        wq, ws, wS = p["wpack"]
+        sp_full_ms[n] = timed(torch, stream, lambda i: (
+            S.quantize_nvfp4(p["X"], p["idx"], p["ax"], out=p["xpack"]),
+            S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])), 10)
+        del xq0, wq0, Y0
+    tot_sp, tot_nv = sum(gemm_ms.values()), sum(nv_ms.values())
+    out["prefill"] = {
+        "gemm_tflops": round(sum(flops.values()) / (tot_sp * 1e-3) / 1e12, 2),
+        "nvfp4_gemm_tflops": round(sum(flops.values()) / (tot_nv * 1e-3) / 1e12, 2),
+        "overhead_gemm_pct": round(100.0 * (tot_sp - tot_nv) / tot_nv, 2),
+        "overhead_projection_pct": round(100.0 * (sum(sp_full_ms.values()) - sum(nv_full_ms.values()))
+                                         / sum(nv_full_ms.values()), 2),
+        "gemm_ms": {n: round(v, 4) for n, v in gemm_ms.items()},
+        "nvfp4_ms": {n: round(v, 4) for n, v in nv_ms.items()},
+    }
+    log("prefill", out["prefill"])
+
+    # ---------------- decode: weight-streaming path, weights rotated through copies
+    ncopy = 6                                   # ~650 MB of packed weights > 256 MB MALL
+    packs = {n: [tuple(t.clone() for t in P[n]["wpack"]) for _ in range(ncopy)] for n in names}
+    dec = {}
+    tot_b = tot_t = 0.0
+    tot_nv = 0.0
+    for M in DECODE_MS:
+        bM = tM = 0.0
+        nvM = 0.0
+        for n in names:
+            p = P[n]
+            K, N = p["K"], p["N"]
+            Xh = synth.activations(synth.CFG_DECODE, synth.INPUT_STREAM[n], M, K, 3, "student")
+            X = torch.from_numpy(Xh.view(np.int16)).to(dev)
+            xq = S.quantize_nvfp4(X, p["idx"], p["ax"])
+            Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+            wsz = S.workspace_size(M, N, K, K_PROT)
+            ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+            cp = packs[n]
+
+            def call(i):
+                w = cp[i % ncopy]
+                S.splice_gemm(xq[0], xq[1], p["ax"], xq[2], w[0], w[1], p["aw"], w[2], out=Y, ws=ws)
+
+            def call_nv(i):
+                w = cp[i % ncopy]
+                S.nvfp4_gemm(xq[0], xq[1], p["ax"], w[0], w[1], p["aw"], out=Y, ws=ws)
+            for i in range(10):
+                call(i)
+            t = timed(torch, stream, call, args.decode_iters)
+            tn = timed(torch, stream, call_nv, args.decode_iters)
+            b = N * K * (0.5 + 1 / 16) + 2 * N * K_PROT + M * K * (0.5 + 1 / 16) + 2 * M * K_PROT + 4 * M * N
+            dec[f"{n}@M{M}"] = {"us": round(t * 1e3, 2), "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                                "nvfp4_us": round(tn * 1e3, 2)}
+            bM += b
+            tM += t
+            nvM += tn
+        dec[f"M{M}"] = {"GBps": round(bM / (tM * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(bM / (tM * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "overhead_pct": round(100.0 * (tM - nvM) / nvM, 2)}
+        tot_b += bM
+        tot_t += tM
+        tot_nv += nvM
+        log(f"decode M={M}: {dec[f'M{M}']}")
+    out["decode"] = {"GBps": round(tot_b / (tot_t * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(tot_b / (tot_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "overhead_pct": round(100.0 * (tot_t - tot_nv) / tot_nv, 2),
+                     "timing": "HIP events around back-to-back calls, includes launch gaps",
+                     "shapes": dec}
+    del packs
+
+    # ---------------- grouped MoE stand-in
+    counts = synth.moe_counts()
+    K, N = 4096, 2048
+    groups = []
+    for e, Me in enumerate(counts):
+        Me = int(Me)
+        Xw = torch.from_numpy(synth.activations(synth.CFG_MOE, 100 + e, 512, K, 2, "student").view(np.int16)).to(dev)
+        X = torch.from_numpy(synth.activations(synth.CFG_MOE, 100 + e, max(Me, 1), K, 3, "student").view(np.int16)).to(dev)[:Me]
+        W = torch.from_numpy(synth.weights(synth.CFG_MOE, 200 + e, N, K).view(np.int16)).to(dev)
+        idx, ax, _ = S.select_channels(Xw, K_PROT)
+        aw = S.compute_alpha(W, idx)
+        xq = S.quantize_nvfp4(X, idx, ax) if Me else (torch.zeros(0, K // 2, dtype=torch.uint8, device=dev),
+                                                     torch.zeros(0, K // 16, dtype=torch.uint8, device=dev),
+                                                     torch.zeros(0, K_PROT, dtype=torch.int16, device=dev))
+        wq = S.quantize_nvfp4(W, idx, aw)
+        groups.append(dict(Xq=xq[0], Xs=xq[1], alpha_x=ax, X_S=xq[2], Wq=wq[0], Ws=wq[1], alpha_w=aw, W_S=wq[2],
+                           Y=torch.empty(Me, N, dtype=torch.float32, device=dev)))
+    for _ in range(3):
+        S.splice_gemm_grouped(groups, N, K, K_PROT)
+    tg = timed(torch, stream, lambda i: S.splice_gemm_grouped(groups, N, K, K_PROT), 20)
+    fl = 2.0 * int(counts.sum()) * N * K
+    wbytes = len(counts) * (N * K * (0.5 + 1 / 16) + 2 * N * K_PROT)
+    out["moe_grouped"] = {"experts": len(counts), "tokens": int(counts.sum()), "max_tokens": int(counts.max()),
+                          "ms": round(tg, 4), "TFLOPs": round(fl / (tg * 1e-3) / 1e12, 2),
+                          "weight_GBps": round(wbytes / (tg * 1e-3) / 1e9, 1)}
+    log("moe", out["moe_grouped"])
+
+    # ---------------- cold path: selection and weight pre-split per layer
+    def cold(i):
+        for n in names:
+            p = P[n]
+            p["stats"].count = 0
+            S.select_channels(p["Xw"], K_PROT, p["stats"], out=(p["idx"], p["ax"]))
+            S.compute_alpha(p["W"], p["idx"], out=p["aw"])
+            S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
+    out["reselect_layer_ms"] = round(timed(torch, stream, cold, 5), 4)
+    return out
+
+
+def cpu_baseline(args, host, names, flops_per_row):
+    """The fp64 oracle on the host cores: the same step for every projection
+    (statistics and selection on the warm-up batch, weight alpha and full
+    weight quantization, activation preparation and the product) on the first
+    `cpu_rows` token rows."""
+    import oracle as O
+    rows = args.cpu_rows
+    t0 = time.perf_counter()
+    for n in names:
+        h = host[n]
+        idx, ax, _ = O.select_channels(h["X_warm"], K_PROT)
+        aw = O.compute_alpha(h["W"], idx)
+        wq, ws, wS = O.quantize_nvfp4(h["W"], idx, aw)
+        xq, xs, xS = O.quantize_nvfp4(h["X"][:rows], idx, ax)
+        O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
+    dt = time.perf_counter() - t0
+    v = flops_per_row * rows / dt / 1e12
+    log(f"cpu oracle {dt:.1f}s for {rows} rows")
+    return {"value": v, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"the whole step for all 7 projections on {rows} of {M_PREFILL} token rows "
+                      f"(full warm-up statistics, full weight quantization), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -131,9 +131,10 @@ class ChannelStats:
                             torch.zeros(K, dtype=torch.float32, device=device))
 
 
-def select_channels(X, k, stats: ChannelStats | None = None, ldx=None, T=None):
+def select_channels(X, k, stats: ChannelStats | None = None, ldx=None, T=None, out=None):
     """Fold the rows of X (bf16 [T, K]) into `stats` and select the top-k
-    channels.  Returns (idx int32 [k] ascending, alpha_x float32 [1], stats)."""
+    channels.  Returns (idx int32 [k] ascending, alpha_x float32 [1], stats).
+    out: optional preallocated (idx, alpha_x)."""
     X = _bf16(X)
     K = X.shape[-1]
     if ldx is None:
@@ -142,8 +143,11 @@ def select_channels(X, k, stats: ChannelStats | None = None, ldx=None, T=None):
         T = X.shape[0]
     if stats is None:
         stats = ChannelStats.empty(K, X.device)
-    idx = torch.empty(k, dtype=torch.int32, device=X.device)
-    alpha = torch.empty(1, dtype=torch.float32, device=X.device)
+    if out is None:
+        idx = torch.empty(k, dtype=torch.int32, device=X.device)
+        alpha = torch.empty(1, dtype=torch.float32, device=X.device)
+    else:
+        idx, alpha = out
     cnt = _i64(stats.count)
     _check("splice_select_channels",
            lib().splice_select_channels(_p(X), T, K, ldx, k, ctypes.byref(cnt), _p(stats.mean),
@@ -153,12 +157,13 @@ def select_channels(X, k, stats: ChannelStats | None = None, ldx=None, T=None):
     return idx, alpha, stats
 
 
-def compute_alpha(A, idx=None, out=None):
+def compute_alpha(A, idx=None, out=None, ws=None):
     A = _bf16(A)
     R, K = A.shape
     idx = _idx(idx, A.device)
     alpha = out if out is not None else torch.empty(1, dtype=torch.float32, device=A.device)
-    ws = torch.empty(lib().splice_alpha_workspace_size(), dtype=torch.uint8, device=A.device)
+    if ws is None:
+        ws = torch.empty(lib().splice_alpha_workspace_size(), dtype=torch.uint8, device=A.device)
     _check("splice_compute_alpha",
            lib().splice_compute_alpha(_p(A), R, K, A.stride(0), _p(idx), idx.numel(), _p(alpha),
                                       _p(ws), ws.numel(), _stream()))
