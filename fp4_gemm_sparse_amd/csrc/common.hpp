@@ -57,6 +57,30 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// v_mfma_f32_32x32x16_{f16,bf16}: lane l holds row (l%32) of A and column
+// (l%32) of B at reduction indices 8*(l/32) .. +8; result element q of lane l
+// is row 8*(q/4) + 4*(l/32) + q%4 of column l%32.
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup barrier that makes this wave's LDS writes visible but, unlike
+// __syncthreads(), does not wait for outstanding global loads (the fence of
+// __syncthreads() would drain a prefetch issued for a later pipeline stage).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maximum
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // 8 bf16 values (16 bytes) of a side buffer row, zero past `valid` elements.
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p, int valid, bool aligned16)
 {
