@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-iters", type=int, default=50)
-    ap.add_argument("--cpu-rows", type=int, default=16, help="token rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="token rows of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the value workload")
     return ap.parse_args()
@@ -183,12 +183,34 @@ def main():
 
 
 def timed(torch, stream, fn, iters):
+    """ms per call of fn(i), i = 0..iters-1, launched back to back."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for i in range(iters):
         fn(i)
     b.record(stream)
     torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def graph_timed(torch, fn, iters):
+    """ms per call of fn(i) replayed from a captured HIP graph (removes host
+    launch overhead; each kernel still pays its own dispatch)."""
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
     return a.elapsed_time(b) / iters
 
 
@@ -257,10 +279,8 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             def call_nv(i):
                 w = cp[i % ncopy]
                 S.nvfp4_gemm(xq[0], xq[1], p["ax"], w[0], w[1], p["aw"], out=Y, ws=ws)
-            for i in range(10):
-                call(i)
-            t = timed(torch, stream, call, args.decode_iters)
-            tn = timed(torch, stream, call_nv, args.decode_iters)
+            t = graph_timed(torch, call, args.decode_iters)
+            tn = graph_timed(torch, call_nv, args.decode_iters)
             b = N * K * (0.5 + 1 / 16) + 2 * N * K_PROT + M * K * (0.5 + 1 / 16) + 2 * M * K_PROT + 4 * M * N
             dec[f"{n}@M{M}"] = {"us": round(t * 1e3, 2), "GBps": round(b / (t * 1e-3) / 1e9, 1),
                                 "nvfp4_us": round(tn * 1e3, 2)}
@@ -277,7 +297,8 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     out["decode"] = {"GBps": round(tot_b / (tot_t * 1e-3) / 1e9, 1),
                      "frac_hbm": round(tot_b / (tot_t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "overhead_pct": round(100.0 * (tot_t - tot_nv) / tot_nv, 2),
-                     "timing": "HIP events around back-to-back calls, includes launch gaps",
+                     "timing": "HIP-graph replay of back-to-back calls over rotated weight copies; "
+                               "includes each kernel's dispatch",
                      "shapes": dec}
     del packs
 
@@ -298,9 +319,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         wq = S.quantize_nvfp4(W, idx, aw)
         groups.append(dict(Xq=xq[0], Xs=xq[1], alpha_x=ax, X_S=xq[2], Wq=wq[0], Ws=wq[1], alpha_w=aw, W_S=wq[2],
                            Y=torch.empty(Me, N, dtype=torch.float32, device=dev)))
-    for _ in range(3):
-        S.splice_gemm_grouped(groups, N, K, K_PROT)
-    tg = timed(torch, stream, lambda i: S.splice_gemm_grouped(groups, N, K, K_PROT), 20)
+    tg = graph_timed(torch, lambda i: S.splice_gemm_grouped(groups, N, K, K_PROT), 10)
     fl = 2.0 * int(counts.sum()) * N * K
     wbytes = len(counts) * (N * K * (0.5 + 1 / 16) + 2 * N * K_PROT)
     out["moe_grouped"] = {"experts": len(counts), "tokens": int(counts.sum()), "max_tokens": int(counts.max()),

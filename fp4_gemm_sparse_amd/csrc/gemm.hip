@@ -218,224 +218,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a)
 }
 
 // ===========================================================================
-// Large-tile prefill path: 256x256 workgroup tile, 4 waves (2x2) of 128x128,
-// v_mfma_f32_32x32x16_f16, K step of 64 channels (4 NVFP4 blocks: 32 code
-// bytes and 4 scale bytes per row), register-staged double-buffered LDS.
-// Lane group g = l/32 owns channels [32g, 32g+32) of a step (one 16-byte code
-// chunk, two block scales); MFMA sub-step s takes its channels [32g+8s, +8).
-// ===========================================================================
-constexpr int BK2 = 64;
-constexpr int CODE_ROW2 = BK2 / 2;     // 32 code bytes per row per step
-constexpr int SCALE_ROW2 = BK2 / 16;   // 4 scale bytes per row per step
-
-struct Big {
-    static constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
-    static constexpr int XC = BM * CODE_ROW2, WC = BN * CODE_ROW2;
-    static constexpr int XSC = BM * SCALE_ROW2, WSC = BN * SCALE_ROW2;
-    static constexpr int STAGE = XC + WC + XSC + WSC;      // 18 KB
-};
-
-// 16-byte chunk h (0/1) of row r: 16 consecutive rows land on 16 distinct
-// 16-byte slots of the 256-byte bank window
-__device__ __forceinline__ int chunk2_off(int r, int h) { return r * CODE_ROW2 + ((h ^ ((r >> 3) & 1)) << 4); }
-
-template <bool TAIL>
-__global__ __launch_bounds__(256) void prefill_big_kernel(GemmArgs a)
-{
-    using C = Big;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
-    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int g = lane >> 5, rr = lane & 31;
-    const int64_t M = a.M, N = a.N, K = a.K;
-    const int tiles_m = (int)((M + C::BM - 1) / C::BM), tiles_n = (int)((N + C::BN - 1) / C::BN);
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-    const int64_t rowb = K / 2, rows = K / 16;
-    const int nk = (int)(K / BK2);
-
-    // staging: thread t moves code chunks t and t+256 of each operand (row c/2,
-    // half c%2) and the 4 scale bytes of row t of each operand
-    const int64_t xm0 = m0 + (tid >> 1), xm1 = m0 + ((tid + 256) >> 1);
-    const int64_t wn0 = n0 + (tid >> 1), wn1 = n0 + ((tid + 256) >> 1);
-    const int hh = tid & 1;
-    const uint8_t *px0 = a.Xq + (xm0 < M ? xm0 : 0) * rowb + hh * 16;
-    const uint8_t *px1 = a.Xq + (xm1 < M ? xm1 : 0) * rowb + hh * 16;
-    const uint8_t *pw0 = a.Wq + (wn0 < N ? wn0 : 0) * rowb + hh * 16;
-    const uint8_t *pw1 = a.Wq + (wn1 < N ? wn1 : 0) * rowb + hh * 16;
-    const bool okx0 = xm0 < M, okx1 = xm1 < M, okw0 = wn0 < N, okw1 = wn1 < N;
-    const int64_t xsr = m0 + tid, wsr = n0 + tid;
-    const uint8_t *pxs = a.Xs + (xsr < M ? xsr : 0) * rows;
-    const uint8_t *pws = a.Ws + (wsr < N ? wsr : 0) * rows;
-    const bool okxs = xsr < M, okws = wsr < N;
-    u32x4 sx0, sx1, sw0, sw1;
-    unsigned ssx, ssw;
-    auto gload = [&](int kt) {
-        const int64_t off = (int64_t)kt * CODE_ROW2, soff = (int64_t)kt * SCALE_ROW2;
-        sx0 = okx0 ? *reinterpret_cast<const u32x4 *>(px0 + off) : u32x4{0, 0, 0, 0};
-        sx1 = okx1 ? *reinterpret_cast<const u32x4 *>(px1 + off) : u32x4{0, 0, 0, 0};
-        sw0 = okw0 ? *reinterpret_cast<const u32x4 *>(pw0 + off) : u32x4{0, 0, 0, 0};
-        sw1 = okw1 ? *reinterpret_cast<const u32x4 *>(pw1 + off) : u32x4{0, 0, 0, 0};
-        ssx = okxs ? *reinterpret_cast<const unsigned *>(pxs + soff) : 0u;
-        ssw = okws ? *reinterpret_cast<const unsigned *>(pws + soff) : 0u;
-    };
-    auto lstore = [&](uint8_t *st) {
-        *reinterpret_cast<u32x4 *>(st + chunk2_off(tid >> 1, hh)) = sx0;
-        *reinterpret_cast<u32x4 *>(st + chunk2_off((tid + 256) >> 1, hh)) = sx1;
-        *reinterpret_cast<u32x4 *>(st + C::XC + chunk2_off(tid >> 1, hh)) = sw0;
-        *reinterpret_cast<u32x4 *>(st + C::XC + chunk2_off((tid + 256) >> 1, hh)) = sw1;
-        *reinterpret_cast<unsigned *>(st + C::XC + C::WC + tid * SCALE_ROW2) = ssx;
-        *reinterpret_cast<unsigned *>(st + C::XC + C::WC + C::XSC + tid * SCALE_ROW2) = ssw;
-    };
-
-    f32x16 acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++)
-#pragma unroll
-            for (int q = 0; q < 16; q++) acc[i][j][q] = 0.f;
-
-    // fragment codes/scales of one stage for this wave
-    u32x4 xc[C::FM], wc[C::FN];
-    unsigned xs[C::FM], ws[C::FN];
-    auto lfrag = [&](const uint8_t *st) {
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) {
-            const int r = wm * C::WM + i * 32 + rr;
-            xc[i] = *reinterpret_cast<const u32x4 *>(st + chunk2_off(r, g));
-            xs[i] = *reinterpret_cast<const uint16_t *>(st + C::XC + C::WC + r * SCALE_ROW2 + 2 * g);
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) {
-            const int r = wn * C::WN + j * 32 + rr;
-            wc[j] = *reinterpret_cast<const u32x4 *>(st + C::XC + chunk2_off(r, g));
-            ws[j] = *reinterpret_cast<const uint16_t *>(st + C::XC + C::WC + C::XSC + r * SCALE_ROW2 + 2 * g);
-        }
-    };
-    f16x2 xp[C::FM][2], wp[C::FN][2];
-    f16x8 af[C::FM], an[C::FM], bf;
-    // scale pairs and the first fragments (s = 0, j = 0) of the stage in xc/wc
-    auto head = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) {
-            xp[i][0] = e4m3_pair(xs[i] & 0xFFu);
-            xp[i][1] = e4m3_pair((xs[i] >> 8) & 0xFFu);
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) {
-            wp[j][0] = e4m3_pair(ws[j] & 0xFFu);
-            wp[j][1] = e4m3_pair((ws[j] >> 8) & 0xFFu);
-        }
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) af[i] = decode8(xc[i][0], xp[i][0]);
-        bf = decode8(wc[0][0], wp[0][0]);
-    };
-    // MFMA step t = 4*s + j of the stage, decoding the operands of step t+1
-    auto step = [&](int t) {
-        const int s = t >> 2, j = t & 3;
-        f16x8 bn = bf;
-        if (j + 1 < C::FN) bn = decode8(wc[j + 1][s], wp[j + 1][s >> 1]);
-        else if (s + 1 < 4) bn = decode8(wc[0][s + 1], wp[0][(s + 1) >> 1]);
-        if (s + 1 < 4) an[j] = decode8(xc[j][s + 1], xp[j][(s + 1) >> 1]);
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) acc[i][j] = mfma32_f16(af[i], bf, acc[i][j]);
-        bf = bn;
-        if (j == 3 && s + 1 < 4) {
-#pragma unroll
-            for (int i = 0; i < C::FM; i++) af[i] = an[i];
-        }
-    };
-
-    if (nk > 0) {
-        gload(0);
-        lstore(lds);
-        __syncthreads();
-        lfrag(lds);
-        head();
-    }
-    for (int kt = 0; kt < nk; kt++) {
-        const bool more = kt + 1 < nk;
-        if (more) gload(kt + 1);
-#pragma unroll
-        for (int t = 0; t < 14; t++) step(t);
-        // stage kt+1 into the other buffer; its fragments are read while the
-        // last MFMAs of this stage drain
-        if (more) lstore(lds + ((kt + 1) & 1) * C::STAGE);
-        __syncthreads();
-        f16x8 a_last[C::FM], b14 = bf;
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) a_last[i] = af[i];
-        const f16x8 b15 = decode8(wc[3][3], wp[3][1]);
-        if (more) lfrag(lds + ((kt + 1) & 1) * C::STAGE);
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) acc[i][2] = mfma32_f16(a_last[i], b14, acc[i][2]);
-        if (more) head();
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) acc[i][3] = mfma32_f16(a_last[i], b15, acc[i][3]);
-#pragma unroll
-        for (int q = 0; q < 56; q++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
-        }
-    }
-
-    const float alpha = (*a.alpha_x) * (*a.alpha_w);
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) acc[i][j] *= alpha;
-    if (TAIL) {
-        const int k = a.k;
-        const bool al = (k % 8) == 0;
-        for (int kk = 0; kk < k; kk += 16) {
-            const int c0 = kk + g * 8;
-            const int valid = max(0, min(8, k - c0));
-            bf16x8 af[C::FM];
-#pragma unroll
-            for (int i = 0; i < C::FM; i++) {
-                const int64_t m = m0 + wm * C::WM + i * 32 + rr;
-                af[i] = load_bf16x8(a.X_S + m * k + c0, (m < M) ? valid : 0, al);
-            }
-#pragma unroll
-            for (int j = 0; j < C::FN; j++) {
-                const int64_t n = n0 + wn * C::WN + j * 32 + rr;
-                const bf16x8 bf = load_bf16x8(a.W_S + n * k + c0, (n < N) ? valid : 0, al);
-#pragma unroll
-                for (int i = 0; i < C::FM; i++) acc[i][j] = mfma32_bf16(af[i], bf, acc[i][j]);
-            }
-        }
-    }
-    // store: lane writes column (n0 + wn*128 + j*32 + rr) of rows
-    // m0 + wm*128 + i*32 + 8*(q/4) + 4*g + q%4
-    const int64_t mb = m0 + wm * C::WM + g * 4, nb = n0 + wn * C::WN + rr;
-    float *yb = a.Y + mb * a.ldy + nb;
-    if (m0 + C::BM <= M && n0 + C::BN <= N) {
-#pragma unroll
-        for (int i = 0; i < C::FM; i++)
-#pragma unroll
-            for (int q = 0; q < 16; q++) {
-                float *yr = yb + (int64_t)(i * 32 + (q >> 2) * 8 + (q & 3)) * a.ldy;
-#pragma unroll
-                for (int j = 0; j < C::FN; j++) yr[j * 32] = acc[i][j][q];
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C::FM; i++)
-#pragma unroll
-            for (int q = 0; q < 16; q++) {
-                const int dm = i * 32 + (q >> 2) * 8 + (q & 3);
-                if (mb + dm >= M) continue;
-                float *yr = yb + (int64_t)dm * a.ldy;
-#pragma unroll
-                for (int j = 0; j < C::FN; j++)
-                    if (nb + j * 32 < N) yr[j * 32] = acc[i][j][q];
-            }
-    }
-}
-
-// ===========================================================================
 // LDS-decode prefill path: each workgroup decodes every NVFP4 element of its
 // 256x256 tile exactly once per K step into a swizzled FP16 tile in LDS
 // (double buffered, 2 x 64 KB); the four waves (2x2, 128x128 each) read their
@@ -645,15 +427,6 @@ static hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-static hipError_t run_prefill_big(const GemmArgs &a, hipStream_t s)
-{
-    const int64_t tiles = ((a.M + Big::BM - 1) / Big::BM) * ((a.N + Big::BN - 1) / Big::BN);
-    if (a.k > 0)
-        hipLaunchKernelGGL(prefill_big_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(prefill_big_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
 
 template <int BM, int BN, bool TAIL>
 static hipError_t launch_prefill(const GemmArgs &a, hipStream_t s)
@@ -679,69 +452,51 @@ static hipError_t run_prefill(const GemmArgs &a, hipStream_t s)
 }
 
 // ===========================================================================
-// Decode path (small M): weight streaming.  A workgroup of four waves owns CB
-// column blocks of 16 output channels and a slice of K; its waves split the
-// slice, each loading its weight chunks straight from HBM into registers (no
-// LDS staging) and the few activation rows from L2, decoding both and
-// multiplying on the matrix cores with M padded to MB*16 rows.  The four
-// partial accumulators are summed through LDS in wave order.  With one K
-// slice the workgroup then scales, adds the BF16 side product and stores Y;
-// with several, the unscaled partials go to the workspace and a second kernel
-// sums them in slice order.
+// Decode path, streaming form: a workgroup of NW waves owns CB column blocks
+// (16*CB output channels) and the whole K; wave w takes K chunks (128
+// channels each) w, w+NW, w+2NW, ... so the waves of a workgroup sweep each
+// weight row contiguously.  Each wave keeps two batches of BB chunks of
+// weight and activation codes in registers, loading one while it decodes and
+// multiplies the other, so every wave has several 16-byte loads per lane in
+// flight.  Partial accumulators are summed through LDS in wave order, then
+// scaled, completed with the BF16 side product and stored -- one launch, no
+// workspace.
 // ===========================================================================
-struct DecodePlan {
-    int MB, CB, SK;
+template <int MB, int CB, int NW, int BB>
+struct DecodeCfg {
+    static constexpr int T = MB * CB;                    // 16x16 tiles per wave
+    static constexpr int RED_TILES = (T * NW <= 128) ? T : (128 / NW);   // tiles per LDS round
 };
 
-static DecodePlan decode_plan(int64_t M, int64_t N, int64_t K)
+template <int MB, int CB, int NW, int BB, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
 {
-    DecodePlan p;
-    p.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.CB = p.MB == 1 ? 1 : 2;
-    const int64_t nwg = (N + 16 * p.CB - 1) / (16 * p.CB);
-    const int64_t chunks = K / BK;
-    // split K across workgroups only while the partial sums stay small next to
-    // the weight bytes (partials: 8*M*N*SK bytes; weights: 0.5625*N*K)
-    int sk = 1;
-    while (nwg * sk < 1024 && chunks / (2 * sk) >= 4 && 8.0 * M * (2 * sk) <= 0.1 * 0.5625 * K) sk *= 2;
-    p.SK = sk;
-    return p;
-}
-
-template <int MB, int CB, bool TAIL>
-__global__ __launch_bounds__(256) void decode_kernel(GemmArgs a, float *partial)
-{
-    __shared__ f32x4 red[4][MB * CB][WAVE];
+    using C = DecodeCfg<MB, CB, NW, BB>;
+    __shared__ f32x4 red[NW][C::RED_TILES][WAVE];
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t rowb = K / 2, rows = K / 16;
     const int64_t n0 = (int64_t)blockIdx.x * (16 * CB);
-    const int SK = gridDim.y;
     const int nchunk = (int)(K / BK);
-    const int s0 = (int)((int64_t)blockIdx.y * nchunk / SK), s1 = (int)((int64_t)(blockIdx.y + 1) * nchunk / SK);
-    const int cnt = s1 - s0;
-    const int c0 = s0 + wave * cnt / 4, c1 = s0 + (wave + 1) * cnt / 4;
 
     const uint8_t *wrow[CB];
     const uint8_t *wsrow[CB];
-    bool wok[CB];
 #pragma unroll
     for (int j = 0; j < CB; j++) {
         const int64_t n = n0 + j * 16 + rr;
-        wok[j] = n < N;
-        wrow[j] = a.Wq + (wok[j] ? n : 0) * rowb + g * 16;
-        wsrow[j] = a.Ws + (wok[j] ? n : 0) * rows + 2 * g;
+        const int64_t nn = n < N ? n : 0;            // edge rows read row 0; never stored
+        wrow[j] = a.Wq + nn * rowb + g * 16;
+        wsrow[j] = a.Ws + nn * rows + 2 * g;
     }
     const uint8_t *xrow[MB];
     const uint8_t *xsrow[MB];
-    bool xok[MB];
 #pragma unroll
     for (int i = 0; i < MB; i++) {
         const int64_t m = i * 16 + rr;
-        xok[i] = m < M;
-        xrow[i] = a.Xq + (xok[i] ? m : 0) * rowb + g * 16;
-        xsrow[i] = a.Xs + (xok[i] ? m : 0) * rows + 2 * g;
+        const int64_t mm = m < M ? m : 0;
+        xrow[i] = a.Xq + mm * rowb + g * 16;
+        xsrow[i] = a.Xs + mm * rows + 2 * g;
     }
 
     f32x4 acc[MB][CB];
@@ -750,132 +505,440 @@ __global__ __launch_bounds__(256) void decode_kernel(GemmArgs a, float *partial)
 #pragma unroll
         for (int j = 0; j < CB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wc[CB], xc[MB];
-    unsigned wsc[CB], xsc[MB];
-    auto load = [&](int c, u32x4 *wcv, unsigned *wscv, u32x4 *xcv, unsigned *xscv) {
+    u32x4 wc0[BB][CB], xc0[BB][MB], wc1[BB][CB], xc1[BB][MB];
+    unsigned ws0[BB][CB], xs0[BB][MB], ws1[BB][CB], xs1[BB][MB];
+    auto load = [&](int c, u32x4 (*wc)[CB], unsigned (*ws)[CB], u32x4 (*xc)[MB], unsigned (*xs)[MB]) {
 #pragma unroll
-        for (int j = 0; j < CB; j++) {
-            wcv[j] = wok[j] ? *reinterpret_cast<const u32x4 *>(wrow[j] + (int64_t)c * CODE_ROW) : u32x4{0, 0, 0, 0};
-            wscv[j] = wok[j] ? *reinterpret_cast<const uint16_t *>(wsrow[j] + (int64_t)c * SCALE_ROW) : 0u;
-        }
+        for (int b = 0; b < BB; b++) {
+            const int ci = min(c + b * NW, nchunk - 1);      // clamped; masked at use
 #pragma unroll
-        for (int i = 0; i < MB; i++) {
-            xcv[i] = xok[i] ? *reinterpret_cast<const u32x4 *>(xrow[i] + (int64_t)c * CODE_ROW) : u32x4{0, 0, 0, 0};
-            xscv[i] = xok[i] ? *reinterpret_cast<const uint16_t *>(xsrow[i] + (int64_t)c * SCALE_ROW) : 0u;
+            for (int j = 0; j < CB; j++) {
+                wc[b][j] = *reinterpret_cast<const u32x4 *>(wrow[j] + (int64_t)ci * CODE_ROW);
+                ws[b][j] = *reinterpret_cast<const uint16_t *>(wsrow[j] + (int64_t)ci * SCALE_ROW);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; i++) {
+                xc[b][i] = *reinterpret_cast<const u32x4 *>(xrow[i] + (int64_t)ci * CODE_ROW);
+                xs[b][i] = *reinterpret_cast<const uint16_t *>(xsrow[i] + (int64_t)ci * SCALE_ROW);
+            }
         }
     };
-    auto compute = [&](const u32x4 *wcv, const unsigned *wscv, const u32x4 *xcv, const unsigned *xscv) {
+    auto compute = [&](int c, u32x4 (*wc)[CB], unsigned (*ws)[CB], u32x4 (*xc)[MB], unsigned (*xs)[MB]) {
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            f16x8 af[MB], bf[CB];
+        for (int b = 0; b < BB; b++) {
+            const bool ok = c + b * NW < nchunk;
 #pragma unroll
-            for (int i = 0; i < MB; i++) af[i] = decode8(xcv[i][s], e4m3_pair((xscv[i] >> ((s >> 1) * 8)) & 0xFFu));
+            for (int s = 0; s < 4; s++) {
+                f16x8 af[MB];
 #pragma unroll
-            for (int j = 0; j < CB; j++) bf[j] = decode8(wcv[j][s], e4m3_pair((wscv[j] >> ((s >> 1) * 8)) & 0xFFu));
+                for (int i = 0; i < MB; i++) {
+                    const unsigned code = ok ? xc[b][i][s] : 0u;
+                    af[i] = decode8(code, e4m3_pair((xs[b][i] >> ((s >> 1) * 8)) & 0xFFu));
+                }
 #pragma unroll
-            for (int i = 0; i < MB; i++)
+                for (int j = 0; j < CB; j++) {
+                    const f16x8 bf = decode8(wc[b][j][s], e4m3_pair((ws[b][j] >> ((s >> 1) * 8)) & 0xFFu));
 #pragma unroll
-                for (int j = 0; j < CB; j++) acc[i][j] = mfma_f16(af[i], bf[j], acc[i][j]);
+                    for (int i = 0; i < MB; i++) acc[i][j] = mfma_f16(af[i], bf, acc[i][j]);
+                }
+            }
         }
     };
 
-    if (c0 < c1) load(c0, wc, wsc, xc, xsc);
-    int c = c0;
-    for (; c + 1 < c1; c += 2) {
-        u32x4 wc2[CB], xc2[MB];
-        unsigned wsc2[CB], xsc2[MB];
-        load(c + 1, wc2, wsc2, xc2, xsc2);
-        compute(wc, wsc, xc, xsc);
-        if (c + 2 < c1) load(c + 2, wc, wsc, xc, xsc);
-        compute(wc2, wsc2, xc2, xsc2);
+    int c = wave;
+    if (c < nchunk) load(c, wc0, ws0, xc0, xs0);
+    while (c < nchunk) {
+        const int c1 = c + BB * NW;
+        if (c1 < nchunk) load(c1, wc1, ws1, xc1, xs1);
+        compute(c, wc0, ws0, xc0, xs0);
+        if (c1 >= nchunk) break;
+        const int c2 = c1 + BB * NW;
+        if (c2 < nchunk) load(c2, wc0, ws0, xc0, xs0);
+        compute(c1, wc1, ws1, xc1, xs1);
+        c = c2;
     }
-    if (c < c1) compute(wc, wsc, xc, xsc);
 
-    // ---- sum the four waves' partials in wave order
-#pragma unroll
-    for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int j = 0; j < CB; j++) red[wave][i * CB + j][lane] = acc[i][j];
-    __syncthreads();
+    // ---- deterministic cross-wave sum through LDS, in rounds of RED_TILES tiles
     const float alpha = (*a.alpha_x) * (*a.alpha_w);
-    for (int t = wave; t < MB * CB; t += 4) {
-        const int i = t / CB, j = t % CB;
-        f32x4 v = red[0][t][lane];
-        v += red[1][t][lane];
-        v += red[2][t][lane];
-        v += red[3][t][lane];
-        const int64_t n = n0 + j * 16 + rr;
-        if (partial) {
-            float *P = partial + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int t0 = 0; t0 < C::T; t0 += C::RED_TILES) {
+        if (t0 > 0) __syncthreads();
+#pragma unroll
+        for (int t = 0; t < C::RED_TILES; t++)
+            if (t0 + t < C::T) red[wave][t][lane] = acc[(t0 + t) / CB][(t0 + t) % CB];
+        __syncthreads();
+        for (int t = wave; t < C::RED_TILES && t0 + t < C::T; t += NW) {
+            const int i = (t0 + t) / CB, j = (t0 + t) % CB;
+            f32x4 v = red[0][t][lane];
+#pragma unroll
+            for (int w = 1; w < NW; w++) v += red[w][t][lane];
+            v *= alpha;
+            const int64_t n = n0 + j * 16 + rr;
+            if (TAIL) {
+                const int k = a.k;
+                const bool al = (k % 8) == 0;
+                const int64_t mrow = i * 16 + rr;
+                for (int kk = 0; kk < k; kk += 32) {
+                    const int cc = kk + g * 8;
+                    const int valid = max(0, min(8, k - cc));
+                    bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
+                    bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                    v = mfma_bf16(af, bf, v);
+                }
+            }
             if (n < N)
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     const int64_t m = i * 16 + g * 4 + q;
-                    if (m < M) P[m * N + n] = v[q];
+                    if (m < M) a.Y[m * a.ldy + n] = v[q];
                 }
-            continue;
         }
-        v *= alpha;
-        if (TAIL) {
-            const int k = a.k;
-            const bool al = (k % 8) == 0;
+    }
+}
+
+template <int MB, int CB, int NW, int BB>
+static hipError_t run_decode2(const GemmArgs &a, hipStream_t s)
+{
+    dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
+    if (a.k > 0)
+        hipLaunchKernelGGL((decode2_kernel<MB, CB, NW, BB, true>), grid, dim3(64 * NW), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode2_kernel<MB, CB, NW, BB, false>), grid, dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+// ===========================================================================
+// Decode path, single-round form.  A workgroup of NW waves owns CB column
+// blocks (16*CB output channels) and the whole K; wave w owns K chunks (128
+// channels each) w, w+NW, ..., at most CPW of them.  Every wave issues all of
+// its weight and activation loads at once -- and, for the waves that finish
+// output tiles, the BF16 side operands too -- so the kernel costs about one
+// memory round trip plus the transfer itself.  Partials are summed through
+// LDS in wave order, then scaled, completed with the side product and stored.
+// ===========================================================================
+template <int MB, int CB, int NW, int CPW, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
+{
+    constexpr int T = MB * CB;
+    constexpr int RT = (T * NW <= 128) ? T : (128 / NW);      // tiles per LDS round
+    __shared__ f32x4 red[NW][RT][WAVE];
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);   // uniform: scalar branches
+    const int g = lane >> 4, rr = lane & 15;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t rowb = K / 2, rows = K / 16;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * CB);
+    const int nchunk = (int)(K / BK);
+
+    // All loads are unconditional (chunk index clamped, edge rows redirected
+    // to row 0) and issued before any use; validity is applied when the data
+    // is consumed, so no load waits on another.
+    u32x4 wc[CPW][CB], xc[CPW][MB];
+    unsigned ws[CPW][CB], xs[CPW][MB];
+#pragma unroll
+    for (int j = 0; j < CB; j++) {
+        const int64_t n = n0 + j * 16 + rr;
+        const int64_t nn = n < N ? n : 0;                      // edge rows: never stored
+        const uint8_t *pw = a.Wq + nn * rowb + g * 16;
+        const uint8_t *ps = a.Ws + nn * rows + 2 * g;
+#pragma unroll
+        for (int c = 0; c < CPW; c++) {
+            const int64_t ci = min(wave + c * NW, nchunk - 1);
+            wc[c][j] = *reinterpret_cast<const u32x4 *>(pw + ci * CODE_ROW);
+            ws[c][j] = *reinterpret_cast<const uint16_t *>(ps + ci * SCALE_ROW);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; i++) {
+        const int64_t m = i * 16 + rr;
+        const int64_t mm = m < M ? m : 0;                      // padding rows: never stored
+        const uint8_t *px = a.Xq + mm * rowb + g * 16;
+        const uint8_t *pxs = a.Xs + mm * rows + 2 * g;
+#pragma unroll
+        for (int c = 0; c < CPW; c++) {
+            const int64_t ci = min(wave + c * NW, nchunk - 1);
+            xc[c][i] = *reinterpret_cast<const u32x4 *>(px + ci * CODE_ROW);
+            xs[c][i] = *reinterpret_cast<const uint16_t *>(pxs + ci * SCALE_ROW);
+        }
+    }
+    // side operands of the tiles this wave finishes, for k = 32 or 64
+    constexpr int TPW = (T + NW - 1) / NW;
+    const int k = a.k;
+    const bool side_pre = TAIL && (k == 32 || k == 64);
+    bf16x8 ta[TPW][2], tb[TPW][2];
+    if (side_pre) {
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const int t = min(wave + u * NW, T - 1);
+            const int i = t / CB, j = t % CB;
+            const int64_t mrow = i * 16 + rr, n = n0 + j * 16 + rr;
+            const uint16_t *xa = a.X_S + (mrow < M ? mrow : 0) * k + g * 8;
+            const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int hh = (h * 32 < k) ? h : 0;          // k = 32: second half re-reads the first
+                ta[u][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + hh * 32));
+                tb[u][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
+            }
+        }
+    }
+
+    f32x4 acc[MB][CB];
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int j = 0; j < CB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CPW; c++) {
+        if (wave + c * NW < nchunk) {                          // uniform branch
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                f16x8 af[MB];
+#pragma unroll
+                for (int i = 0; i < MB; i++)
+                    af[i] = decode8(xc[c][i][s], e4m3_pair((xs[c][i] >> ((s >> 1) * 8)) & 0xFFu));
+#pragma unroll
+                for (int j = 0; j < CB; j++) {
+                    const f16x8 bf = decode8(wc[c][j][s], e4m3_pair((ws[c][j] >> ((s >> 1) * 8)) & 0xFFu));
+#pragma unroll
+                    for (int i = 0; i < MB; i++) acc[i][j] = mfma_f16(af[i], bf, acc[i][j]);
+                }
+            }
+        }
+    }
+
+    const float alpha = (*a.alpha_x) * (*a.alpha_w);
+#pragma unroll
+    for (int t0 = 0; t0 < T; t0 += RT) {
+        if (t0 > 0) __syncthreads();
+#pragma unroll
+        for (int t = 0; t < RT; t++)
+            if (t0 + t < T) red[wave][t][lane] = acc[(t0 + t) / CB][(t0 + t) % CB];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const int tt = wave + u * NW;                      // global tile index
+            if (tt < t0 || tt >= t0 + RT || tt >= T) continue;
+            const int t = tt - t0;
+            const int i = tt / CB, j = tt % CB;
+            f32x4 v = red[0][t][lane];
+#pragma unroll
+            for (int w = 1; w < NW; w++) v += red[w][t][lane];
+            v *= alpha;
+            const int64_t n = n0 + j * 16 + rr;
             const int64_t mrow = i * 16 + rr;
-            for (int kk = 0; kk < k; kk += 32) {
-                const int cc = kk + g * 8;
-                const int valid = max(0, min(8, k - cc));
-                bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
-                bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
-                v = mfma_bf16(af, bf, v);
+            if (TAIL) {
+                if (side_pre) {
+                    const bf16x8 z = {};
+                    const bool okm = mrow < M, okn = n < N;
+                    v = mfma_bf16(okm ? ta[u][0] : z, okn ? tb[u][0] : z, v);
+                    if (k == 64) v = mfma_bf16(okm ? ta[u][1] : z, okn ? tb[u][1] : z, v);
+                } else {
+                    const bool al = (k % 8) == 0;
+                    for (int kk = 0; kk < k; kk += 32) {
+                        const int cc = kk + g * 8;
+                        const int valid = max(0, min(8, k - cc));
+                        bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
+                        bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                        v = mfma_bf16(af, bf, v);
+                    }
+                }
+            }
+            if (n < N)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int64_t m = i * 16 + g * 4 + q;
+                    if (m < M) a.Y[m * a.ldy + n] = v[q];
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Variant for few activation rows (M*K*2 bytes fit in LDS): the workgroup
+// decodes the M real activation rows once into an FP16 LDS copy, and every
+// wave reads its A fragments from there instead of decoding 16 rows (most of
+// them padding) per chunk.  Weight handling is the single-round scheme above.
+// ---------------------------------------------------------------------------
+constexpr int XLDS_MAX = 64 * 1024;        // bytes of FP16 activations kept in LDS
+
+template <int NW, int CPW, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [M][K] f16, then reduction space
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int g = lane >> 4, rr = lane & 15;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t rowb = K / 2, rows = K / 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int nchunk = (int)(K / BK);
+
+    // weights of this wave: chunks [c0, c0 + CPW) of each of its 16 rows,
+    // so the waves of the workgroup sweep every row contiguously.  Scales come
+    // 16 bytes (two chunks) per load; all loads are issued before any use.
+    const int c0 = wave * CPW;
+    u32x4 wc[CPW];
+    u32x4 wsv[CPW / 2];
+    {
+        const int64_t n = n0 + rr;
+        const int64_t nn = n < N ? n : 0;
+        const uint8_t *pw = a.Wq + nn * rowb + g * 16;
+        const uint8_t *ps = a.Ws + nn * rows;
+#pragma unroll
+        for (int c = 0; c < CPW; c++) {
+            const int64_t ci = min(c0 + c, nchunk - 1);
+            wc[c] = *reinterpret_cast<const u32x4 *>(pw + ci * CODE_ROW);
+        }
+#pragma unroll
+        for (int c = 0; c < CPW / 2; c++) {
+            const int64_t ci = min(c0 + 2 * c, nchunk - 2);
+            wsv[c] = *reinterpret_cast<const u32x4 *>(ps + ci * SCALE_ROW);
+        }
+    }
+    bf16x8 ta[2], tb[2];
+    const int k = a.k;
+    const bool side_pre = TAIL && (k == 32 || k == 64);
+    if (side_pre && wave == 0) {
+        const int64_t mrow = rr, n = n0 + rr;
+        const uint16_t *xa = a.X_S + (mrow < M ? mrow : 0) * k + g * 8;
+        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int hh = (h * 32 < k) ? h : 0;
+            ta[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + hh * 32));
+            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
+        }
+    }
+
+    // decode the M activation rows into LDS: one 16-channel block per item
+    {
+        const int64_t nb = K / 16;
+        for (int64_t it = tid; it < M * nb; it += 64 * NW) {
+            const int64_t m = it / nb, b = it - m * nb;
+            const u32x2 c = *reinterpret_cast<const u32x2 *>(a.Xq + m * rowb + b * 8);
+            const f16x2 sc = e4m3_pair(a.Xs[m * rows + b]);
+            f16x8 *dst = reinterpret_cast<f16x8 *>(xl + (m * K + b * 16) * 2);
+            dst[0] = decode8(c.x, sc);
+            dst[1] = decode8(c.y, sc);
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool xrow = rr < M;
+    const uint8_t *xbase = xl + (int64_t)(xrow ? rr : 0) * K * 2 + g * 64;   // lane's 32 channels of a chunk
+#pragma unroll
+    for (int c = 0; c < CPW; c++) {
+        const int ci = c0 + c;
+        if (ci < nchunk) {
+            // scale bytes 2g, 2g+1 of chunk ci inside the 16-byte scale vector
+            const int cl = min(c0 + 2 * (c / 2), nchunk - 2);           // first chunk of the vector
+            const int off = (ci - cl) * 8 + 2 * g;                        // byte offset, 0..14
+            const unsigned word = wsv[c / 2][off >> 2];
+            const unsigned sb = (word >> ((off & 3) * 8)) & 0xFFFFu;
+            const f16x2 s0 = e4m3_pair(sb & 0xFFu), s1 = e4m3_pair(sb >> 8);
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                f16x8 af = *reinterpret_cast<const f16x8 *>(xbase + (int64_t)ci * BK * 2 + s * 16);
+                if (!xrow) af = f16x8{};
+                const f16x8 bf = decode8(wc[c][s], s < 2 ? s0 : s1);
+                acc = mfma_f16(af, bf, acc);
+            }
+        }
+    }
+
+    // wave-order reduction through LDS (reuses the space after the activations)
+    f32x4 *red = reinterpret_cast<f32x4 *>(xl + ((M * K * 2 + 15) & ~(int64_t)15));
+    red[wave * WAVE + lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 v = red[lane];
+#pragma unroll
+        for (int w = 1; w < NW; w++) v += red[w * WAVE + lane];
+        v *= (*a.alpha_x) * (*a.alpha_w);
+        const int64_t n = n0 + rr;
+        if (TAIL) {
+            if (side_pre) {
+                const bf16x8 z = {};
+                const bool okm = rr < M, okn = n < N;
+                v = mfma_bf16(okm ? ta[0] : z, okn ? tb[0] : z, v);
+                if (k == 64) v = mfma_bf16(okm ? ta[1] : z, okn ? tb[1] : z, v);
+            } else {
+                const bool al = (k % 8) == 0;
+                const int64_t mrow = rr;
+                for (int kk = 0; kk < k; kk += 32) {
+                    const int cc = kk + g * 8;
+                    const int valid = max(0, min(8, k - cc));
+                    bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
+                    bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                    v = mfma_bf16(af, bf, v);
+                }
             }
         }
         if (n < N)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const int64_t m = i * 16 + g * 4 + q;
+                const int64_t m = g * 4 + q;
                 if (m < M) a.Y[m * a.ldy + n] = v[q];
             }
     }
 }
 
-// Y = alpha * (sum of the K-slice partials in slice order) + X_S W_S^T
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, const float *partial, int SK)
+template <int NW, int CPW>
+static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
 {
-    const int64_t M = a.M, N = a.N;
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= M * N) return;
-    const int64_t m = e / N, n = e - m * N;
-    float v = 0.f;
-    for (int s = 0; s < SK; s++) v += partial[(int64_t)s * M * N + e];
-    v *= (*a.alpha_x) * (*a.alpha_w);
-    const int k = a.k;
-    for (int i = 0; i < k; i++)
-        v = fmaf(__uint_as_float((unsigned)a.X_S[m * k + i] << 16),
-                 __uint_as_float((unsigned)a.W_S[n * k + i] << 16), v);
-    a.Y[m * a.ldy + n] = v;
-}
-
-template <int MB, int CB>
-static hipError_t run_decode(const GemmArgs &a, int SK, float *partial, hipStream_t s)
-{
-    dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)), (unsigned)SK);
-    if (SK > 1 || a.k == 0)
-        hipLaunchKernelGGL((decode_kernel<MB, CB, false>), grid, dim3(256), 0, s, a, SK > 1 ? partial : nullptr);
-    else
-        hipLaunchKernelGGL((decode_kernel<MB, CB, true>), grid, dim3(256), 0, s, a, (float *)nullptr);
-    if (SK > 1) {
-        const int64_t total = a.M * a.N;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                           a, partial, SK);
+    const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16;
+    dim3 grid((unsigned)((a.N + 15) / 16));
+    if (a.k > 0) {
+        static bool attr = false;
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
+            if (e != hipSuccess) return e;
+            attr = true;
+        }
+        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, true>), grid, dim3(64 * NW), lds, s, a);
+    } else {
+        static bool attr = false;
+        if (!attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
+            if (e != hipSuccess) return e;
+            attr = true;
+        }
+        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, false>), grid, dim3(64 * NW), lds, s, a);
     }
     return hipGetLastError();
 }
 
-// ===========================================================================
-size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K)
+template <int MB, int CB, int NW, int CPW>
+static hipError_t run_decode3(const GemmArgs &a, hipStream_t s)
 {
-    if (p != Path::Decode || M == 0 || N == 0) return 0;
-    const DecodePlan d = decode_plan(M, N, K);
-    return d.SK > 1 ? (size_t)d.SK * M * N * sizeof(float) : 0;
+    dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
+    if (a.k > 0)
+        hipLaunchKernelGGL((decode3_kernel<MB, CB, NW, CPW, true>), grid, dim3(64 * NW), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode3_kernel<MB, CB, NW, CPW, false>), grid, dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+// waves per workgroup so that each wave holds at most CPW chunks; false when
+// even MAXNW waves would need more (then the looping form is used)
+template <int MB, int CB, int CPW, int MAXNW>
+static bool run_decode3_k(const GemmArgs &a, hipStream_t s, hipError_t &e)
+{
+    const int nchunk = (int)(a.K / BK);
+    if (nchunk <= 4 * CPW) { e = run_decode3<MB, CB, 4, CPW>(a, s); return true; }
+    if (nchunk <= 8 * CPW) { e = run_decode3<MB, CB, 8, CPW>(a, s); return true; }
+    if (MAXNW >= 16 && nchunk <= 16 * CPW) { e = run_decode3<MB, CB, (MAXNW >= 16 ? 16 : 8), CPW>(a, s); return true; }
+    return false;
+}
+
+// ===========================================================================
+size_t gemm_ws_bytes(Path, int64_t, int64_t, int64_t)
+{
+    return 0;        // neither datapath needs scratch memory
 }
 
 hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t s)
@@ -889,13 +952,28 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
         if (t256 >= 240) return a.k > 0 ? launch_prefill_lds<true>(a, s) : launch_prefill_lds<false>(a, s);
         return run_prefill<128, 128>(a, s);
     }
-    const DecodePlan d = decode_plan(a.M, a.N, a.K);
-    float *partial = static_cast<float *>(ws);
-    switch (d.MB) {
-    case 1: return run_decode<1, 1>(a, d.SK, partial, s);
-    case 2: return run_decode<2, 2>(a, d.SK, partial, s);
-    default: return run_decode<4, 2>(a, d.SK, partial, s);
+    // weight-streaming decode path; configurations chosen from measured sweeps
+    // on MI355X (Qwen3-8B projection shapes, M = 1, 8, 32, 64)
+    hipError_t e = hipSuccess;
+    const int nchunk = (int)(a.K / BK);
+    const int64_t colblocks = (a.N + 15) / 16;
+    if (a.M <= 16) {
+        if (a.M <= 4 && a.M * a.K * 2 <= XLDS_MAX && nchunk >= 2 && nchunk % 2 == 0) {   // 16-byte aligned scale pairs
+            if (nchunk <= 4 * 8) return run_decode_xlds<4, 8>(a, s);
+            if (nchunk <= 8 * 8) return run_decode_xlds<8, 8>(a, s);
+            if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, s);
+        }
+        if (colblocks >= 512 && run_decode3_k<1, 3, 4, 8>(a, s, e)) return e;
+        if (run_decode3_k<1, 1, 8, 16>(a, s, e)) return e;
+        return run_decode2<1, 1, 8, 2>(a, s);
     }
+    if (a.M <= 32) {
+        if (colblocks >= 512 && run_decode3_k<2, 3, 4, 8>(a, s, e)) return e;
+        if (run_decode3_k<2, 2, 4, 8>(a, s, e)) return e;
+        return run_decode2<2, 2, 8, 2>(a, s);
+    }
+    if (run_decode3_k<4, 2, 4, 8>(a, s, e)) return e;
+    return run_decode2<4, 2, 8, 1>(a, s);
 }
 
 }  // namespace splice

@@ -178,7 +178,8 @@ def test_tiny_config_end_to_end():
 SHAPES = [(1, 16, 128, 0), (1, 100, 1024, 5), (8, 48, 256, 64), (16, 1000, 1024, 64),
           (17, 64, 512, 31), (32, 1024, 1024, 1), (33, 80, 256, 64), (63, 130, 384, 64),
           (64, 1024, 2048, 256), (65, 96, 256, 64), (128, 128, 1024, 0), (130, 1040, 1024, 64),
-          (200, 300, 640, 100), (257, 257, 128, 128)]
+          (200, 300, 640, 100), (257, 257, 128, 128),
+          (5, 40, 17408, 16), (40, 24, 8192, 64), (3, 48, 384, 64), (16, 272, 256, 32)]
 
 
 @pytest.mark.parametrize("M,N,K,k", SHAPES)
