@@ -19,12 +19,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(unsigned b) { return __uint_as
 // ===========================================================================
 // Channel statistics: Welford over 64-row tiles, tiles folded left to right
 // with the pairwise update of Chan, Golub & LeVeque, then merged into the
-// running moments.  One workgroup owns 64 channels (one per lane); its four
-// waves take tiles round-robin and park their tile moments in LDS, and wave 0
-// folds them in tile order, so the result does not depend on scheduling.
+// running moments.  One workgroup owns 64 channels (one per lane).  Its eight
+// waves each take one tile of a round of eight: a wave issues the loads of 16
+// rows before it starts their (serial) Welford steps, parks the tile moments
+// in LDS, and wave 0 folds the round in tile order, so the result does not
+// depend on scheduling.
 // ===========================================================================
 constexpr int ST_TILE = 64;
-constexpr int ST_GROUP = 16;   // tiles parked in LDS per fold round
+constexpr int ST_WAVES = 8;    // tiles per fold round, one per wave
+constexpr int ST_BATCH = 16;   // rows loaded ahead of their Welford steps
 
 struct Moments { double n, mean, m2; };
 
@@ -41,45 +44,53 @@ __device__ __forceinline__ Moments chan_merge(Moments a, Moments b)
     return r;
 }
 
-__global__ __launch_bounds__(256) void stats_kernel(const uint16_t *__restrict__ X, int64_t T,
-                                                    int64_t K, int64_t ldx, int64_t count_prev,
-                                                    double *mean, double *m2, float *absmax)
+__global__ __launch_bounds__(ST_WAVES * WAVE) void stats_kernel(
+    const uint16_t *__restrict__ X, int64_t T, int64_t K, int64_t ldx, int64_t count_prev,
+    double *mean, double *m2, float *absmax)
 {
-    __shared__ double s_mean[ST_GROUP][WAVE];
-    __shared__ double s_m2[ST_GROUP][WAVE];
-    __shared__ double s_n[ST_GROUP];
-    __shared__ float s_amax[4][WAVE];
-    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+    __shared__ double s_mean[ST_WAVES][WAVE];
+    __shared__ double s_m2[ST_WAVES][WAVE];
+    __shared__ float s_amax[ST_WAVES][WAVE];
+    const int lane = threadIdx.x % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int64_t j = (int64_t)blockIdx.x * WAVE + lane;
     const bool valid = j < K;
+    const int64_t jc = valid ? j : K - 1;          // lanes past K read a valid column, unused
     Moments acc = {0.0, 0.0, 0.0};
     float amax = 0.0f;
     const int64_t ntiles = (T + ST_TILE - 1) / ST_TILE;
-    for (int64_t g0 = 0; g0 < ntiles; g0 += ST_GROUP) {
-        const int gt = (int)min((int64_t)ST_GROUP, ntiles - g0);
-        for (int t = wave; t < gt; t += 4) {
-            const int64_t r0 = (g0 + t) * ST_TILE;
-            const int64_t r1 = min(r0 + ST_TILE, T);
+    for (int64_t g0 = 0; g0 < ntiles; g0 += ST_WAVES) {
+        const int gt = (int)min((int64_t)ST_WAVES, ntiles - g0);
+        if (wave < gt) {
+            const int64_t r0 = (g0 + wave) * ST_TILE;
+            const int rows = (int)min((int64_t)ST_TILE, T - r0);
+            const uint16_t *p = X + r0 * ldx + jc;
             double n = 0.0, mu = 0.0, M2 = 0.0;
-            if (valid) {
-                for (int64_t r = r0; r < r1; r++) {
-                    const float xf = bf16_bits_to_f32(X[r * ldx + j]);
-                    const double x = (double)xf;
-                    n += 1.0;
-                    const double d = x - mu;
-                    mu += d / n;
-                    M2 += d * (x - mu);
-                    amax = fmaxf(amax, fabsf(xf));
+            for (int c = 0; c < rows; c += ST_BATCH) {
+                float v[ST_BATCH];
+#pragma unroll
+                for (int u = 0; u < ST_BATCH; u++)
+                    v[u] = bf16_bits_to_f32(p[(int64_t)min(c + u, rows - 1) * ldx]);
+#pragma unroll
+                for (int u = 0; u < ST_BATCH; u++) {
+                    if (c + u < rows) {
+                        const double x = (double)v[u];
+                        n += 1.0;
+                        const double d = x - mu;
+                        mu += d / n;
+                        M2 += d * (x - mu);
+                        amax = fmaxf(amax, fabsf(v[u]));
+                    }
                 }
             }
-            s_mean[t][lane] = mu;
-            s_m2[t][lane] = M2;
-            if (lane == 0) s_n[t] = (double)(r1 - r0);
+            s_mean[wave][lane] = mu;
+            s_m2[wave][lane] = M2;
         }
         __syncthreads();
         if (wave == 0) {
             for (int t = 0; t < gt; t++) {
-                Moments tile = {s_n[t], s_mean[t][lane], s_m2[t][lane]};
+                const double nt = (double)min((int64_t)ST_TILE, T - (g0 + t) * ST_TILE);
+                Moments tile = {nt, s_mean[t][lane], s_m2[t][lane]};
                 acc = chan_merge(acc, tile);
             }
         }
@@ -88,7 +99,8 @@ __global__ __launch_bounds__(256) void stats_kernel(const uint16_t *__restrict__
     s_amax[wave][lane] = amax;
     __syncthreads();
     if (wave == 0 && valid) {
-        float a = fmaxf(fmaxf(s_amax[0][lane], s_amax[1][lane]), fmaxf(s_amax[2][lane], s_amax[3][lane]));
+        float a = 0.0f;
+        for (int w = 0; w < ST_WAVES; w++) a = fmaxf(a, s_amax[w][lane]);
         Moments run = {0.0, 0.0, 0.0};
         float prev = 0.0f;
         if (count_prev > 0) {
@@ -109,8 +121,8 @@ hipError_t launch_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, in
 {
     if (K == 0) return hipSuccess;
     dim3 grid((unsigned)((K + WAVE - 1) / WAVE));
-    hipLaunchKernelGGL(stats_kernel, grid, dim3(256), 0, s, X, T, K, ldx, count_prev, mean, m2,
-                       absmax);
+    hipLaunchKernelGGL(stats_kernel, grid, dim3(ST_WAVES * WAVE), 0, s, X, T, K, ldx, count_prev,
+                       mean, m2, absmax);
     return hipGetLastError();
 }
 
@@ -123,6 +135,7 @@ hipError_t launch_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, in
 // taken (the lowest-indexed ones); two scans then compact the selection.
 // ===========================================================================
 constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / WAVE;
 
 __device__ __forceinline__ uint64_t order_key(double v)
 {
@@ -130,23 +143,83 @@ __device__ __forceinline__ uint64_t order_key(double v)
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// exclusive scan of one int64 per thread over the workgroup
-__device__ int64_t block_exclusive_scan(int64_t v, int64_t *buf)
+// Exclusive scan of one int64 per thread over the workgroup: a shuffle scan in
+// each wave, then a scan of the wave totals.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t *wtot)
 {
-    const int tid = threadIdx.x;
-    buf[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < SEL_THREADS; off <<= 1) {
-        int64_t t = (tid >= off) ? buf[tid - off] : 0;
-        __syncthreads();
-        buf[tid] += t;
-        __syncthreads();
+    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+    int64_t incl = v;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const int64_t t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
     }
-    int64_t incl = buf[tid];
+    if (lane == WAVE - 1) wtot[wave] = incl;
     __syncthreads();
-    return incl - v;
+    if (wave == 0) {
+        int64_t x = lane < SEL_WAVES ? wtot[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < SEL_WAVES; off <<= 1) {
+            const int64_t t = __shfl_up(x, off);
+            if (lane >= off) x += t;
+        }
+        if (lane < SEL_WAVES) wtot[SEL_WAVES + lane] = x - wtot[lane];
+    }
+    __syncthreads();
+    const int64_t r = wtot[SEL_WAVES + wave] + incl - v;
+    __syncthreads();
+    return r;
 }
 
+// hist[d] += 1 for every active lane: lanes holding the wave's most common
+// digits are counted with one atomic per digit (a few rounds), the rest with
+// one atomic each.
+__device__ __forceinline__ void hist_add(unsigned *hist, unsigned d, bool active)
+{
+    const int lane = threadIdx.x % WAVE;
+    for (int round = 0; round < 4; round++) {
+        const uint64_t act = __ballot(active);
+        if (act == 0) return;
+        const int lead = __builtin_ctzll(act);
+        const unsigned dl = (unsigned)__shfl((int)d, lead);
+        const bool same = active && d == dl;
+        const uint64_t m = __ballot(same);
+        if (lane == lead) atomicAdd(&hist[dl], (unsigned)__popcll(m));
+        if (same) active = false;
+    }
+    if (active) atomicAdd(&hist[d], 1u);
+}
+
+// The order keys of a thread's channels c0 .. c1-1: held in registers when
+// PER > 0 (at most PER per thread), re-read from m2 otherwise.
+template <int PER>
+struct KeySource {
+    uint64_t reg[PER > 0 ? PER : 1];
+    const double *m2;
+    int64_t c0, c1;
+    __device__ __forceinline__ void init(const double *m, int64_t a, int64_t b)
+    {
+        m2 = m;
+        c0 = a;
+        c1 = b;
+        if (PER > 0) {
+#pragma unroll
+            for (int i = 0; i < (PER > 0 ? PER : 1); i++) reg[i] = (c0 + i < c1) ? order_key(m2[c0 + i]) : 0;
+        }
+    }
+    __device__ __forceinline__ uint64_t operator()(int i) const
+    {
+        if (PER > 0) {
+            uint64_t v = 0;
+#pragma unroll
+            for (int q = 0; q < (PER > 0 ? PER : 1); q++) v = (q == i) ? reg[q] : v;
+            return v;
+        }
+        return order_key(m2[c0 + i]);
+    }
+};
+
+template <int PER>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__restrict__ m2,
                                                              const float *__restrict__ absmax,
                                                              int64_t K, int32_t k, int32_t *idx,
@@ -155,11 +228,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__res
     __shared__ unsigned hist[256];
     __shared__ uint64_t s_prefix;
     __shared__ int64_t s_need;
-    __shared__ int64_t s_buf[SEL_THREADS];
-    __shared__ float s_max[SEL_THREADS / WAVE];
-    const int tid = threadIdx.x;
-    const int64_t per = (K + SEL_THREADS - 1) / SEL_THREADS;
+    __shared__ int64_t s_wtot[2 * SEL_WAVES];
+    __shared__ float s_max[SEL_WAVES];
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int per = (int)((K + SEL_THREADS - 1) / SEL_THREADS);
     const int64_t c0 = min(K, (int64_t)tid * per), c1 = min(K, c0 + per);
+    const int n = (int)(c1 - c0);
+    KeySource<PER> keys;
+    keys.init(m2, c0, c1);
 
     uint64_t thr = 0;       // key of the k-th largest channel
     int64_t need = 0;       // how many channels with key == thr are taken
@@ -167,22 +243,38 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__res
         uint64_t prefix = 0, pmask = 0;
         int64_t remaining = k;
         for (int shift = 56; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
+            if (tid < 256) hist[tid] = 0;
             __syncthreads();
-            for (int64_t j = c0; j < c1; j++) {
-                uint64_t key = order_key(m2[j]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            for (int i = 0; i < per; i++) {                   // same trip count in every lane
+                const bool in = i < n;
+                const uint64_t key = in ? keys(i) : 0;
+                hist_add(hist, (unsigned)(key >> shift) & 255u, in && (key & pmask) == prefix);
             }
             __syncthreads();
-            if (tid == 0) {
-                int64_t cum = 0;
-                int d = 255;
-                for (; d > 0; d--) {
-                    if (cum + (int64_t)hist[d] >= remaining) break;
-                    cum += hist[d];
+            if (tid < WAVE) {
+                // lane l covers digits 255-4l .. 252-4l; find the digit d where the
+                // count of keys with a larger digit first reaches `remaining`
+                unsigned h[4], sum = 0;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    h[q] = hist[255 - 4 * lane - q];
+                    sum += h[q];
                 }
-                s_prefix = prefix | ((uint64_t)d << shift);
-                s_need = remaining - cum;
+                unsigned incl = sum;
+#pragma unroll
+                for (int off = 1; off < WAVE; off <<= 1) {
+                    const unsigned t = __shfl_up(incl, off);
+                    if (lane >= off) incl += t;
+                }
+                int64_t before = (int64_t)(incl - sum);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    if (before < remaining && before + (int64_t)h[q] >= remaining) {
+                        s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << shift);
+                        s_need = remaining - before;
+                    }
+                    before += h[q];
+                }
             }
             __syncthreads();
             prefix = s_prefix;
@@ -196,44 +288,44 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__res
 
     int64_t my_eq = 0;
     if (k > 0)
-        for (int64_t j = c0; j < c1; j++) my_eq += (order_key(m2[j]) == thr);
-    const int64_t eq_before = block_exclusive_scan(my_eq, s_buf);
+        for (int i = 0; i < n; i++) my_eq += (keys(i) == thr);
+    const int64_t eq_before = block_exclusive_scan(my_eq, s_wtot);
 
     int64_t my_sel = 0;
     {
         int64_t e = eq_before;
         if (k > 0)
-            for (int64_t j = c0; j < c1; j++) {
-                const uint64_t key = order_key(m2[j]);
+            for (int i = 0; i < n; i++) {
+                const uint64_t key = keys(i);
                 const bool eq = key == thr;
                 my_sel += (key > thr) || (eq && e < need);
                 e += eq;
             }
     }
-    int64_t p = block_exclusive_scan(my_sel, s_buf);
+    int64_t p = block_exclusive_scan(my_sel, s_wtot);
 
     float am = 0.0f;
     {
         int64_t e = eq_before;
-        for (int64_t j = c0; j < c1; j++) {
+        for (int i = 0; i < n; i++) {
             bool sel = false;
             if (k > 0) {
-                const uint64_t key = order_key(m2[j]);
+                const uint64_t key = keys(i);
                 const bool eq = key == thr;
                 sel = (key > thr) || (eq && e < need);
                 e += eq;
             }
-            if (sel) idx[p++] = (int32_t)j;
-            else am = fmaxf(am, absmax[j]);
+            if (sel) idx[p++] = (int32_t)(c0 + i);
+            else am = fmaxf(am, absmax[c0 + i]);
         }
     }
     if (alpha_x) {
         for (int off = WAVE / 2; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-        if (tid % WAVE == 0) s_max[tid / WAVE] = am;
+        if (lane == 0) s_max[tid / WAVE] = am;
         __syncthreads();
         if (tid == 0) {
             float a = 0.0f;
-            for (int w = 0; w < SEL_THREADS / WAVE; w++) a = fmaxf(a, s_max[w]);
+            for (int w = 0; w < SEL_WAVES; w++) a = fmaxf(a, s_max[w]);
             *alpha_x = (a == 0.0f) ? 1.0f : __fdiv_rn(a, 2688.0f);
         }
     }
@@ -242,8 +334,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__res
 hipError_t launch_select(const double *m2, const float *absmax, int64_t K, int32_t k, int32_t *idx,
                          float *alpha_x, hipStream_t s)
 {
-    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k, idx,
-                       alpha_x);
+    const int64_t per = (K + SEL_THREADS - 1) / SEL_THREADS;
+    if (per <= 4)
+        hipLaunchKernelGGL(select_kernel<4>, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k,
+                           idx, alpha_x);
+    else if (per <= 16)
+        hipLaunchKernelGGL(select_kernel<16>, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k,
+                           idx, alpha_x);
+    else
+        hipLaunchKernelGGL(select_kernel<0>, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k,
+                           idx, alpha_x);
     return hipGetLastError();
 }
 
@@ -270,36 +370,103 @@ __device__ __forceinline__ unsigned block_mask16(const uint32_t *smask, int64_t 
     return (smask[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu;
 }
 
+// The 16 elements of one NVFP4 block as 8 words of two bf16 each (element 2t
+// in the low half of word t).
+struct Block16 { unsigned w[8]; };
+
+__device__ __forceinline__ Block16 load_block(const uint16_t *p)
+{
+    const u32x4 v0 = reinterpret_cast<const u32x4 *>(p)[0];
+    const u32x4 v1 = reinterpret_cast<const u32x4 *>(p)[1];
+    return Block16{{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w}};
+}
+
+// Sets the protected elements (bit e of m) to +0.
+__device__ __forceinline__ void clear_protected(Block16 &x, unsigned m)
+{
+    // bit 2t of m stays at 2t, bit 2t+1 moves to 2t+16
+    const unsigned spread = (m & 0x5555u) | ((m & 0xAAAAu) << 15);
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        const unsigned b = (spread >> (2 * t)) & 0x00010001u;
+        x.w[t] &= ~((b << 16) - b);                  // 0xFFFF in each flagged half
+    }
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+
+// Largest bf16 magnitude bit pattern of the block.
+__device__ __forceinline__ unsigned block_amax_bits(const Block16 &x)
+{
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, x.w[t] & 0x7FFF7FFFu));
+    return max((unsigned)m.x, (unsigned)m.y);
+}
+
+// Walks the (row, block) pairs of one thread: rows blockIdx.x, +gridDim.x, ...
+// and blocks threadIdx.x, +ROW_THREADS, ... of each row.  Loops take U pairs
+// per step and issue all their loads before using any (rows past the end are
+// clamped to the last row, so every load is in bounds; their results are
+// discarded).
+constexpr int ROW_THREADS = 256;
+
+struct RowBlockWalk {
+    int64_t r;
+    int b;
+    __device__ __forceinline__ void next(int nb)
+    {
+        b += ROW_THREADS;
+        if (b >= nb) {
+            b = threadIdx.x;
+            r += gridDim.x;
+        }
+    }
+};
+
 // ===========================================================================
 // Masked amax -> alpha = fp32(amax / 2688), 1 when amax is 0.
 // ===========================================================================
-constexpr int AMAX_GRID = 1024;
+constexpr int AMAX_GRID = 2048;
 size_t alpha_ws_bytes() { return AMAX_GRID * sizeof(unsigned); }
 
-__global__ __launch_bounds__(256) void amax_kernel(const uint16_t *__restrict__ A, int64_t R,
-                                                   int64_t K, int64_t lda,
-                                                   const int32_t *__restrict__ idx, int32_t k,
-                                                   unsigned *partial)
+// One workgroup per row (grid-stride over rows), one thread per block.
+template <bool PROT>
+__global__ __launch_bounds__(ROW_THREADS) void amax_kernel(const uint16_t *__restrict__ A, int64_t R,
+                                                           int64_t K, int64_t lda,
+                                                           const int32_t *__restrict__ idx,
+                                                           int32_t k, unsigned *partial)
 {
     __shared__ uint32_t smask[MAX_K / 32];
-    __shared__ unsigned s_red[4];
-    if (k > 0) build_mask(smask, K, idx, k);
-    const int64_t nb = K / NVFP4_BLOCK;
-    const int64_t total = R * nb;
+    __shared__ unsigned s_red[ROW_THREADS / WAVE];
+    if (PROT) build_mask(smask, K, idx, k);
+    const int nb = (int)(K / NVFP4_BLOCK);
     unsigned amax = 0;
-    for (int64_t task = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; task < total;
-         task += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = task / nb, b = task - r * nb;
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(A + r * lda + b * NVFP4_BLOCK);
-        const u32x4 v0 = p[0], v1 = p[1];
-        const unsigned m = (k > 0) ? block_mask16(smask, b) : 0u;
-        const unsigned w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    constexpr int U = 4;
+    RowBlockWalk it{(int64_t)blockIdx.x, (int)threadIdx.x};
+    if (it.b < nb)
+        while (it.r < R) {
+            RowBlockWalk w[U];
+            Block16 x[U];
 #pragma unroll
-        for (int t = 0; t < 16; t++) {
-            const unsigned x = (w[t >> 1] >> ((t & 1) * 16)) & 0x7FFFu;
-            amax = ((m >> t) & 1u) ? amax : max(amax, x);
+            for (int u = 0; u < U; u++) {
+                w[u] = it;
+                it.next(nb);
+                x[u] = load_block(A + min(w[u].r, R - 1) * lda + w[u].b * NVFP4_BLOCK);
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (w[u].r < R) {
+                    if (PROT) {
+                        const unsigned m = block_mask16(smask, w[u].b);
+                        if (m) clear_protected(x[u], m);
+                    }
+                    amax = max(amax, block_amax_bits(x[u]));
+                }
+            }
         }
-    }
     for (int off = WAVE / 2; off > 0; off >>= 1) amax = max(amax, (unsigned)__shfl_xor((int)amax, off));
     if (threadIdx.x % WAVE == 0) s_red[threadIdx.x / WAVE] = amax;
     __syncthreads();
@@ -326,18 +493,24 @@ hipError_t launch_alpha(const uint16_t *A, int64_t R, int64_t K, int64_t lda, co
                         int32_t k, float *alpha, void *ws, hipStream_t s)
 {
     unsigned *partial = static_cast<unsigned *>(ws);
-    hipLaunchKernelGGL(amax_kernel, dim3(AMAX_GRID), dim3(256), 0, s, A, R, K, lda, idx, k,
-                       partial);
-    hipLaunchKernelGGL(alpha_final_kernel, dim3(1), dim3(256), 0, s, partial, AMAX_GRID, alpha);
+    const int grid = (int)max((int64_t)1, min(R, (int64_t)AMAX_GRID));
+    if (k > 0)
+        hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(ROW_THREADS), 0, s, A, R, K, lda,
+                           idx, k, partial);
+    else
+        hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(ROW_THREADS), 0, s, A, R, K, lda,
+                           idx, k, partial);
+    hipLaunchKernelGGL(alpha_final_kernel, dim3(1), dim3(256), 0, s, partial, grid, alpha);
     return hipGetLastError();
 }
 
 // ===========================================================================
 // NVFP4 quantization of the masked residual, plus the side-buffer gather.
-// One thread per 16-element block: two 16-byte loads, the block amax with the
-// protected lanes read as +0, the E4M3 scale, sixteen E2M1 codes, one 8-byte
-// store of codes, one scale byte, and the protected values copied to their
-// slot of the compact side buffer.
+// One workgroup per row (grid-stride over rows), one thread per 16-element
+// block: two 16-byte loads, the block amax with the protected lanes read as
+// +0, the E4M3 scale, sixteen E2M1 codes, one 8-byte store of codes and one
+// scale byte; then the row's protected values are copied to its slice of the
+// compact side buffer.
 //
 // Exact decisions:
 //  - scale: v = a_b / (6 alpha) in fp64 (6 alpha exact; the quotient of an
@@ -345,10 +518,13 @@ hipError_t launch_alpha(const uint16_t *A, int64_t R, int64_t K, int64_t lda, co
 //    midpoint unless it equals it), then round-to-nearest-even onto E4M3FN
 //    with saturation at 448;
 //  - codes: the seven midpoints m_i of the E2M1 grid times s_b*alpha are exact
-//    in fp64 (3 x 4 x 24 bits); each is turned into the fp32 bit pattern the
-//    bf16 inputs are compared against (rounded down when not representable,
-//    one step lower for the midpoints whose ties round up to the even code),
-//    so that code = number of patterns below |x|'s pattern, exactly.
+//    in fp64 (3 x 4 x 24 bits).  Each becomes a 16-bit key: the largest bf16
+//    magnitude pattern whose value lies below the midpoint (at or below it
+//    for the midpoints whose ties go to the lower, even code).  The code of
+//    an element is then the number of keys below its magnitude pattern,
+//    found for two elements at once by a three-step binary search on packed
+//    16-bit lanes (keys are non-decreasing, patterns and keys < 2^15, so the
+//    sign bit of key - pattern says pattern > key).
 // ===========================================================================
 
 // Round v >= 0 to E4M3FN, nearest, ties to even mantissa, saturating at 448.
@@ -367,109 +543,103 @@ __device__ __forceinline__ double e4m3_value(unsigned b)
     return e ? ldexp(1.0 + (double)m * 0.125, e - 7) : ldexp((double)m, -9);
 }
 
-// fp32 bit pattern of the largest float <= t (t > 0), and whether it equals t.
-__device__ __forceinline__ unsigned f32_bits_round_down(double t, bool &exact)
+// Key of threshold t > 0 (exact in fp64), duplicated into both 16-bit halves.
+// A bf16 magnitude pattern p is above the key iff its value is > t, or >= t
+// when tie_up.  fp32 bits of the largest float below t (or <= t) are formed
+// first; a bf16 pattern p exceeds them iff p exceeds their upper 16 bits.
+__device__ __forceinline__ unsigned key_pair(double t, bool tie_up)
 {
-    const uint64_t u = (uint64_t)__double_as_longlong(t);
-    const int ed = (int)((u >> 52) & 0x7FF);
-    const uint64_t mant = u & 0xFFFFFFFFFFFFFull;
-    if (ed - 1023 >= 128) { exact = false; return 0x7F7FFFFFu; }  // beyond FLT_MAX
-    if (ed - 1023 >= -126) {                                       // fp32 normal range
-        exact = (mant & ((1ull << 29) - 1)) == 0;
-        return ((unsigned)(ed - 1023 + 127) << 23) | (unsigned)(mant >> 29);
+    unsigned kb;
+    if (t >= 0x1p-126) {
+        const float f = (float)t;                                 // nearest, t < FLT_MAX
+        const double fd = (double)f;
+        kb = __float_as_uint(f) - ((tie_up ? fd >= t : fd > t) ? 1u : 0u);
+    } else {                                                      // fp32 subnormal range
+        const double q = ldexp(t, 149);
+        const double f = floor(q);
+        kb = (unsigned)f - ((tie_up && f == q) ? 1u : 0u);        // t >= 2^-160: q > 0
     }
-    const double q = ldexp(t, 149);                                // fp32 subnormal units
-    const double f = floor(q);
-    exact = (f == q);
-    return (unsigned)f;
+    return (kb >> 16) | (kb & 0xFFFF0000u);
 }
 
-__global__ __launch_bounds__(256) void quantize_kernel(
+// 0xFFFF in each half where the pattern half of p2 is above the key half of
+// k2: packed 16-bit subtract, then an arithmetic shift of each half by 15.
+// (Written as two instructions: left to the compiler, the shift is turned
+// into per-half compares and selects.)
+__device__ __forceinline__ unsigned pk_above(unsigned p2, unsigned k2)
+{
+    unsigned d;
+    asm("v_pk_sub_u16 %0, %1, %2\n\tv_pk_ashrrev_i16 %0, %3, %0"
+        : "=&v"(d) : "v"(k2), "v"(p2), "v"(0x000F000Fu));
+    return d;
+}
+
+__device__ __forceinline__ unsigned pick(unsigned m, unsigned a, unsigned b) { return (m & a) | (~m & b); }
+
+// Four words of two nibbles each (bits 3:0 and 19:16) -> one word of eight
+// nibbles in element order.
+__device__ __forceinline__ unsigned pack_nibbles(unsigned a, unsigned b, unsigned c, unsigned d)
+{
+    const unsigned x = a | (b << 8), y = c | (d << 8);
+    return ((x | (x >> 12)) & 0xFFFFu) | (((y | (y >> 12)) & 0xFFFFu) << 16);
+}
+
+// Codes and scale byte of one block whose protected lanes are already +0.
+__device__ __forceinline__ void quantize_block(const Block16 &x, double alpha, double six_alpha,
+                                               uint8_t *code_dst, uint8_t *scale_dst)
+{
+    const unsigned sc = e4m3_rne_sat((double)bf16_bits_to_f32(block_amax_bits(x)) / six_alpha);
+    unsigned k0 = 0x7FFF7FFFu, k1 = k0, k2 = k0, k3 = k0, k4 = k0, k5 = k0, k6 = k0;
+    if (sc != 0) {
+        const double phys = e4m3_value(sc) * alpha;                   // exact
+        k0 = key_pair(0.25 * phys, false);
+        k1 = key_pair(0.75 * phys, true);
+        k2 = key_pair(1.25 * phys, false);
+        k3 = key_pair(1.75 * phys, true);
+        k4 = key_pair(2.5 * phys, false);
+        k5 = key_pair(3.5 * phys, true);
+        k6 = key_pair(5.0 * phys, false);
+    }
+    unsigned nib[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        const unsigned p2 = x.w[t] & 0x7FFF7FFFu;
+        const unsigned a4 = pk_above(p2, k3);
+        const unsigned a2 = pk_above(p2, pick(a4, k5, k1));
+        const unsigned a1 = pk_above(p2, pick(a4, pick(a2, k6, k4), pick(a2, k2, k0)));
+        nib[t] = (a4 & 0x00040004u) | (a2 & 0x00020002u) | (a1 & 0x00010001u) |
+                 ((x.w[t] >> 12) & 0x00080008u);
+    }
+    *reinterpret_cast<u32x2 *>(code_dst) = u32x2{pack_nibbles(nib[0], nib[1], nib[2], nib[3]),
+                                                 pack_nibbles(nib[4], nib[5], nib[6], nib[7])};
+    *scale_dst = (uint8_t)sc;
+}
+
+template <bool PROT>
+__global__ __launch_bounds__(ROW_THREADS) void quantize_kernel(
     const uint16_t *__restrict__ A, int64_t R, int64_t K, int64_t lda,
     const int32_t *__restrict__ idx, int32_t k, const float *__restrict__ alpha_p,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint16_t *__restrict__ side)
 {
     __shared__ uint32_t smask[MAX_K / 32];
-    __shared__ uint32_t spre[MAX_K / NVFP4_BLOCK];
-    __shared__ int64_t s_scan[256];
-    const int64_t nb = K / NVFP4_BLOCK;
-    if (k > 0) {
-        build_mask(smask, K, idx, k);
-        // exclusive prefix (over blocks) of the number of protected channels
-        const int64_t cpt = (nb + 255) / 256;
-        const int64_t b0 = min(nb, (int64_t)threadIdx.x * cpt), b1 = min(nb, b0 + cpt);
-        int64_t local = 0;
-        for (int64_t b = b0; b < b1; b++) local += __popc(block_mask16(smask, b));
-        s_scan[threadIdx.x] = local;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            int64_t t = (threadIdx.x >= (unsigned)off) ? s_scan[threadIdx.x - off] : 0;
-            __syncthreads();
-            s_scan[threadIdx.x] += t;
-            __syncthreads();
-        }
-        int64_t base = s_scan[threadIdx.x] - local;
-        for (int64_t b = b0; b < b1; b++) {
-            spre[b] = (uint32_t)base;
-            base += __popc(block_mask16(smask, b));
-        }
-        __syncthreads();
-    }
+    if (PROT) build_mask(smask, K, idx, k);
     const double alpha = (double)*alpha_p;
     const double six_alpha = 6.0 * alpha;
-    const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-    const int64_t total = R * nb;
-    for (int64_t task = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; task < total;
-         task += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = task / nb, b = task - r * nb;
-        const uint16_t *src = A + r * lda + b * NVFP4_BLOCK;
-        const u32x4 v0 = reinterpret_cast<const u32x4 *>(src)[0];
-        const u32x4 v1 = reinterpret_cast<const u32x4 *>(src)[1];
-        const unsigned w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const unsigned m = (k > 0) ? block_mask16(smask, b) : 0u;
-        unsigned amax = 0;
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-            const unsigned x = (w[t >> 1] >> ((t & 1) * 16)) & 0x7FFFu;
-            amax = ((m >> t) & 1u) ? amax : max(amax, x);
-        }
-        const unsigned sc = e4m3_rne_sat((double)bf16_bits_to_f32(amax) / six_alpha);
-        unsigned key[7];
-        if (sc != 0) {
-            const double phys = e4m3_value(sc) * alpha;               // exact
-#pragma unroll
-            for (int i = 0; i < 7; i++) {
-                bool exact;
-                unsigned kb = f32_bits_round_down(mids[i] * phys, exact);
-                key[i] = (exact && (i & 1)) ? kb - 1u : kb;
+    const int nb = (int)(K / NVFP4_BLOCK);
+    for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+        const uint16_t *row = A + r * lda;
+        uint8_t *crow = codes + r * (K / 2);
+        uint8_t *srow = scales + r * nb;
+        for (int b = threadIdx.x; b < nb; b += ROW_THREADS) {
+            Block16 x = load_block(row + b * NVFP4_BLOCK);
+            if (PROT) {
+                const unsigned m = block_mask16(smask, b);
+                if (m) clear_protected(x, m);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 7; i++) key[i] = 0xFFFFFFFFu;          // every code 0
+            quantize_block(x, alpha, six_alpha, crow + b * 8, srow + b);
         }
-        unsigned lo = 0, hi = 0;
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-            const unsigned raw = (w[t >> 1] >> ((t & 1) * 16)) & 0xFFFFu;
-            const bool prot = (m >> t) & 1u;
-            const unsigned xk = prot ? 0u : (raw & 0x7FFFu) << 16;
-            unsigned c = 0;
-#pragma unroll
-            for (int i = 0; i < 7; i++) c += (xk > key[i]) ? 1u : 0u;
-            const unsigned nib = (prot ? 0u : ((raw >> 15) << 3)) | c;
-            if (t < 8) lo |= nib << (4 * t);
-            else hi |= nib << (4 * (t - 8));
-        }
-        *reinterpret_cast<u32x2 *>(codes + r * (K / 2) + b * 8) = u32x2{lo, hi};
-        scales[r * nb + b] = (uint8_t)sc;
-        if (m) {
-            const unsigned base = spre[b];
-#pragma unroll
-            for (int t = 0; t < 16; t++)
-                if ((m >> t) & 1u)
-                    side[r * (int64_t)k + base + __popc(m & ((1u << t) - 1u))] =
-                        (uint16_t)((w[t >> 1] >> ((t & 1) * 16)) & 0xFFFFu);
-        }
+        if (PROT)
+            for (int j = threadIdx.x; j < k; j += ROW_THREADS) side[r * k + j] = row[idx[j]];
     }
 }
 
@@ -477,11 +647,14 @@ hipError_t launch_quantize(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
                            const int32_t *idx, int32_t k, const float *alpha, uint8_t *codes,
                            uint8_t *scales, uint16_t *side, hipStream_t s)
 {
-    const int64_t total = R * (K / NVFP4_BLOCK);
-    if (total == 0) return hipSuccess;
-    const int64_t blocks = min((total + 255) / 256, (int64_t)2048);
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, A, R, K, lda, idx,
-                       k, alpha, codes, scales, side);
+    if (R == 0 || K == 0) return hipSuccess;
+    const unsigned grid = (unsigned)min(R, (int64_t)2048);
+    if (k > 0)
+        hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(ROW_THREADS), 0, s, A, R, K, lda,
+                           idx, k, alpha, codes, scales, side);
+    else
+        hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(ROW_THREADS), 0, s, A, R, K,
+                           lda, idx, k, alpha, codes, scales, side);
     return hipGetLastError();
 }
 

@@ -44,7 +44,10 @@ def special_rows(R, K, seed):
 
 # ------------------------------------------------------------------ quantize / alpha
 QCASES = [(1, 16, 0), (7, 48, 1), (64, 256, 5), (130, 1024, 64), (33, 4096, 64), (300, 1024, 256),
-          (16, 128, 128), (5, 12288, 64)]
+          (16, 128, 128), (5, 12288, 64),
+          (2100, 64, 3),        # more rows than workgroups: several rows per workgroup
+          (40, 4800, 64),       # 300 blocks a row: uneven blocks per thread
+          (2, 65536, 64)]       # largest K
 
 
 @pytest.mark.parametrize("R,K,k", QCASES)
@@ -84,7 +87,10 @@ def test_quantize_all_protected_and_strided_rows():
 # ------------------------------------------------------------------ stats / select
 @pytest.mark.parametrize("T,K,k", [(1, 16, 1), (63, 64, 8), (64, 1024, 64), (65, 1024, 0),
                                    (512, 4096, 64), (1100, 1024, 256), (512, 12288, 64),
-                                   (100, 256, 256)])
+                                   (100, 256, 256),
+                                   (20, 20480, 64),      # more than 16 channels per select thread
+                                   (3, 65536, 100),      # largest K
+                                   (16, 16384, 4096)])   # large k
 def test_stats_select_bit_exact(T, K, k):
     X = synth.activations(7, T % 7, T, K, 2, "student", n_out=min(64, K // 4))
     st_o = O.stats(X)
