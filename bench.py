@@ -37,7 +37,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 matrix peak
 K_PROT = 64
 M_PREFILL = 8192
 DECODE_MS = (1, 8, 32, 64)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gemm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_splice_gemm_traffic_qwen3_8b.md")
+COPY_ELEMS = 128 << 20            # fp32 elements of the calibration copy (512 MiB each way)
 
 
 def log(*a):
@@ -50,9 +51,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-iters", type=int, default=50)
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="token rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=1536, help="token rows of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the value workload")
+    ap.add_argument("--profile-workload", action="store_true",
+                    help="only the calibration copy and 3 prefill SpliceGEMMs per projection "
+                         "(the run that rocprofv3 --pmc passes profile)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"),
+                    help="write the profiles/ summaries from rocprofv3 result databases")
     return ap.parse_args()
 
 
@@ -65,6 +71,9 @@ def kernel_source_hash():
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -88,6 +97,9 @@ def main():
     with ThreadPoolExecutor(8) as ex:
         host = dict(ex.map(gen, names))
     log(f"inputs generated in {time.time() - t0:.1f}s")
+    if args.profile_workload:
+        profile_workload(torch, S, host, names, dev)
+        return
 
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
@@ -154,11 +166,7 @@ def main():
     gemm_ms = {n: float(np.mean(v)) for n, v in per.items()}
     flops = {n: 2.0 * M_PREFILL * P[n]["N"] * P[n]["K"] for n in names}
     achieved = sum(flops.values()) / (sum(gemm_ms.values()) * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_source_sha") == kernel_source_hash():
-            traffic = tr.get("bytes_per_launch")
+    traffic = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                 "traffic": traffic}
@@ -360,6 +368,125 @@ def cpu_baseline(args, host, names, flops_per_row):
     return {"value": v, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"the whole step for all 7 projections on {rows} of {M_PREFILL} token rows "
                       f"(full warm-up statistics, full weight quantization), {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ profiling helpers
+def read_traffic():
+    """HBM bytes per prefill SpliceGEMM launch from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def profile_workload(torch, S, host, names, dev):
+    """A plain fp32 multiply-by-one over COPY_ELEMS elements (reads and writes
+    exactly 4*COPY_ELEMS bytes each) for counter calibration, then three
+    prefill SpliceGEMMs per projection in the launch configuration the
+    timed step uses."""
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    for n in names:
+        h = host[n]
+        X = torch.from_numpy(h["X"].view(np.int16)).to(dev)
+        W = torch.from_numpy(h["W"].view(np.int16)).to(dev)
+        Xw = torch.from_numpy(h["X_warm"].view(np.int16)).to(dev)
+        idx, ax, _ = S.select_channels(Xw, K_PROT)
+        aw = S.compute_alpha(W, idx)
+        xq, xs, xS = S.quantize_nvfp4(X, idx, ax)
+        wq, ws, wS = S.quantize_nvfp4(W, idx, aw)
+        Y = torch.empty(X.shape[0], W.shape[0], dtype=torch.float32, device=dev)
+        for _ in range(3):
+            S.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS, path=S.PATH_PREFILL, out=Y)
+        torch.cuda.synchronize()
+        log(f"profile workload: {n} done")
+
+
+def _db_rows(db, sql):
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return con.execute(sql).fetchall()
+    finally:
+        con.close()
+
+
+def summarize(trace_db, fetch_db, write_db):
+    """Writes the kernel-time summary of a bench run and the HBM traffic of
+    the prefill SpliceGEMM (FETCH_SIZE and WRITE_SIZE in KiB per dispatch,
+    each scaled by the reading of the same counter for the calibration copy
+    of known size)."""
+    rows = _db_rows(trace_db, "select name, count(*), avg(duration), sum(duration), "
+                              "min(duration), max(duration) from kernels group by name "
+                              "order by sum(duration) desc")
+    out = ["# Kernel times: bench step, Qwen3-8B layer prefill (M = 8192, k = 64)", "",
+           "Command (repo root, MI355X):", "",
+           "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run -- "
+           "python3 bench.py --steps 3 --warmup 1 --no-cpu --no-extra", "",
+           "Four passes of the step (one warm-up, three timed) over the seven projections.", "",
+           "| kernel | calls | avg us | total ms | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
+    for name, n, avg, tot, mn, mx in rows:
+        out.append(f"| `{name[:90]}` | {n} | {avg / 1e3:.2f} | {tot / 1e6:.3f} | {mn / 1e3:.2f} | "
+                   f"{mx / 1e3:.2f} |")
+    path = os.path.join(ROOT, "profiles", "bench_step_kernels_qwen3_8b_prefill.md")
+    open(path, "w").write("\n".join(out) + "\n")
+    print("wrote", path)
+
+    def per_dispatch(db, counter):
+        r = _db_rows(db, "select kernel_name, dispatch_id, sum(value) from counters_collection "
+                         f"where counter_name = '{counter}' group by kernel_name, dispatch_id")
+        agg = {}
+        for name, _, v in r:
+            agg.setdefault(name, []).append(v)
+        return agg
+
+    fetch, write = per_dispatch(fetch_db, "FETCH_SIZE"), per_dispatch(write_db, "WRITE_SIZE")
+
+    def pick(agg, key):
+        return [v for name, vs in agg.items() if key in name for v in vs]
+
+    copy_kib = COPY_ELEMS * 4 / 1024
+    cf = copy_kib / float(np.mean(pick(fetch, "MulFunctor")))
+    cw = copy_kib / float(np.mean(pick(write, "MulFunctor")))
+    gf = pick(fetch, "prefill")
+    gw = pick(write, "prefill")
+    # algorithmic bytes of the seven projections: codes, scales and side columns
+    # of X and W read once, Y written once
+    from fp4_gemm_sparse_amd.synth import QWEN3_8B
+    alg = [M_PREFILL * K * (0.5 + 1 / 16) + 2 * M_PREFILL * K_PROT + N * K * (0.5 + 1 / 16)
+           + 2 * N * K_PROT + 4 * M_PREFILL * N for K, N in QWEN3_8B.values()]
+    f_b = float(np.mean(gf)) * cf * 1024
+    w_b = float(np.mean(gw)) * cw * 1024
+    out = ["# HBM traffic: prefill SpliceGEMM, Qwen3-8B layer projections (M = 8192, k = 64)", "",
+           "Commands (repo root, MI355X), one counter pass each:", "",
+           "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -- python3 bench.py "
+           "--profile-workload",
+           "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -- python3 bench.py "
+           "--profile-workload",
+           "    python3 bench.py --summarize <trace db> gpurun_out/pmc_fetch/run_results.db "
+           "gpurun_out/pmc_write/run_results.db", "",
+           f"Calibration: fp32 multiply-by-one over {COPY_ELEMS} elements ({copy_kib:.0f} KiB read, "
+           f"{copy_kib:.0f} KiB written); FETCH_SIZE scale {cf:.4f}, WRITE_SIZE scale {cw:.4f}.",
+           f"Prefill SpliceGEMM dispatches: {len(gf)} (3 per projection, 7 projections).", "",
+           f"- fetch_bytes_per_launch: {f_b:.0f}",
+           f"- write_bytes_per_launch: {w_b:.0f}",
+           f"- hbm_bytes_per_launch: {f_b + w_b:.0f}",
+           f"- algorithmic_bytes_per_launch: {float(np.mean(alg)):.0f}",
+           f"- kernel_source_sha: {kernel_source_hash()}", ""]
+    path = TRAFFIC_FILE
+    open(path, "w").write("\n".join(out) + "\n")
+    print("wrote", path)
 
 
 if __name__ == "__main__":
