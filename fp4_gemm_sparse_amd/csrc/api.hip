@@ -3,6 +3,8 @@
 #include "../../include/splice.h"
 #include "kernels.hpp"
 
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 using namespace splice;
@@ -164,38 +166,26 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const
     return run_gemm(a, ws, ws_bytes, path, hs(stream));
 }
 
-size_t splice_grouped_workspace_size(const splice_group *groups, int32_t G, int64_t N, int64_t K,
-                                     int32_t)
+size_t splice_grouped_workspace_size(const splice_group *, int32_t, int64_t, int64_t, int32_t)
 {
-    size_t need = 0;
-    if (!groups || G <= 0 || N <= 0 || K <= 0) return 0;
-    for (int32_t i = 0; i < G; i++) {
-        const int64_t M = groups[i].M;
-        if (M <= 0) continue;
-        const size_t b = gemm_ws_bytes(M <= SPLICE_DECODE_MAX_M ? Path::Decode : Path::Prefill, M, N, K);
-        need = b > need ? b : need;
-    }
-    return need;
+    return 0;
 }
 
 int splice_gemm_grouped(const splice_group *groups, int32_t G, int64_t N, int64_t K, int32_t k,
-                        void *ws, size_t ws_bytes, splice_stream_t stream)
+                        void *, size_t, splice_stream_t stream)
 {
     if (G < 0 || (G > 0 && !groups)) return SPLICE_ERR_INVALID_ARG;
+    std::vector<GemmArgs> args;
+    args.reserve(G);
     for (int32_t i = 0; i < G; i++) {
         const splice_group &g = groups[i];
         GemmArgs a{g.Xq, g.Xs, g.alpha_x, g.X_S, g.Wq, g.Ws, g.alpha_w, g.W_S, g.M, N, K, k, g.Y, N};
-        int rc = check_gemm(a, SPLICE_PATH_AUTO);
+        int rc = check_gemm(a, SPLICE_PATH_PREFILL);
         if (rc) return rc;
+        args.push_back(a);
     }
-    if (splice_grouped_workspace_size(groups, G, N, K, k) > ws_bytes) return SPLICE_ERR_WORKSPACE;
-    for (int32_t i = 0; i < G; i++) {
-        const splice_group &g = groups[i];
-        GemmArgs a{g.Xq, g.Xs, g.alpha_x, g.X_S, g.Wq, g.Ws, g.alpha_w, g.W_S, g.M, N, K, k, g.Y, N};
-        int rc = run_gemm(a, ws, ws_bytes, SPLICE_PATH_AUTO, hs(stream));
-        if (rc) return rc;
-    }
-    return SPLICE_OK;
+    if (G == 0 || N == 0) return SPLICE_OK;
+    return hip_status(launch_gemm_grouped(args.data(), G, hs(stream)));
 }
 
 }  // extern "C"

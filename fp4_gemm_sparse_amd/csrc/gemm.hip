@@ -61,18 +61,15 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
     tn = in / gsz;
 }
 
+// One BM x BN output tile (tm, tn) of the product described by `a`.
 template <int BM, int BN, bool TAIL>
-__global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a)
+__device__ __forceinline__ void prefill_tile(const GemmArgs &a, int tm, int tn, uint8_t *lds)
 {
     using C = Prefill<BM, BN>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t rowb = K / 2, rows = K / 16;
     const int nk = (int)(K / BK);
@@ -215,6 +212,58 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a)
                 if (m < M) a.Y[m * a.ldy + n] = acc[i][j][q];
             }
         }
+}
+
+template <int BM, int BN, bool TAIL>
+__global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    prefill_tile<BM, BN, TAIL>(a, tm, tn, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped form (independent products sharing N, K and k, e.g. the experts of
+// a MoE layer): one launch covers the tiles of up to GROUP_MAX groups.  The
+// group descriptors travel by value in the kernel arguments, so the launch
+// needs no device-side table (and can be captured in a graph); workgroup w
+// belongs to the group whose tile range [tile_start[e], tile_start[e+1])
+// holds w.
+// ---------------------------------------------------------------------------
+constexpr int GROUP_MAX = 32;
+
+struct GroupDesc {
+    const uint8_t *Xq, *Xs;
+    const float *alpha_x;
+    const uint16_t *X_S;
+    const uint8_t *Wq, *Ws;
+    const float *alpha_w;
+    const uint16_t *W_S;
+    float *Y;
+    int64_t M;
+};
+
+struct GroupedArgs {
+    GroupDesc g[GROUP_MAX];
+    int tile_start[GROUP_MAX + 1];
+    int64_t N, K;
+    int k, tiles_n, G;
+};
+
+template <int BM, int BN, bool TAIL>
+__global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int w = blockIdx.x;
+    int e = 0;
+    while (e + 1 < ga.G && w >= ga.tile_start[e + 1]) e++;
+    const int local = w - ga.tile_start[e];
+    const GroupDesc &d = ga.g[e];
+    const GemmArgs a{d.Xq, d.Xs, d.alpha_x, d.X_S, d.Wq, d.Ws, d.alpha_w, d.W_S,
+                     d.M, ga.N, ga.K, ga.k, d.Y, ga.N};
+    prefill_tile<BM, BN, TAIL>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
 }
 
 // ===========================================================================
@@ -449,6 +498,56 @@ template <int BM, int BN>
 static hipError_t run_prefill(const GemmArgs &a, hipStream_t s)
 {
     return a.k > 0 ? launch_prefill<BM, BN, true>(a, s) : launch_prefill<BM, BN, false>(a, s);
+}
+
+template <bool TAIL>
+static hipError_t launch_grouped_chunk(const GroupedArgs &ga, int tiles, hipStream_t s)
+{
+    constexpr int BM = 128, BN = 128;
+    const size_t lds = 2 * Prefill<BM, BN>::STAGE;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&grouped_prefill_kernel<BM, BN, TAIL>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL((grouped_prefill_kernel<BM, BN, TAIL>), dim3((unsigned)tiles), dim3(256), lds,
+                       s, ga);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s)
+{
+    constexpr int BM = 128, BN = 128;
+    if (G <= 0) return hipSuccess;
+    const int64_t N = groups[0].N, K = groups[0].K;
+    const int k = groups[0].k;
+    if (N <= 0 || K <= 0) return hipSuccess;
+    GroupedArgs ga{};
+    ga.N = N;
+    ga.K = K;
+    ga.k = k;
+    ga.tiles_n = (int)((N + BN - 1) / BN);
+    for (int g0 = 0; g0 < G; g0 += GROUP_MAX) {
+        const int cnt = G - g0 < GROUP_MAX ? G - g0 : GROUP_MAX;
+        int tiles = 0;
+        for (int i = 0; i < cnt; i++) {
+            const GemmArgs &a = groups[g0 + i];
+            ga.g[i] = GroupDesc{a.Xq, a.Xs, a.alpha_x, a.X_S, a.Wq, a.Ws, a.alpha_w, a.W_S, a.Y,
+                                a.M > 0 ? a.M : 0};
+            ga.tile_start[i] = tiles;
+            tiles += (int)((ga.g[i].M + BM - 1) / BM) * ga.tiles_n;
+        }
+        ga.tile_start[cnt] = tiles;
+        ga.G = cnt;
+        if (tiles == 0) continue;
+        hipError_t e = k > 0 ? launch_grouped_chunk<true>(ga, tiles, s)
+                             : launch_grouped_chunk<false>(ga, tiles, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // ===========================================================================

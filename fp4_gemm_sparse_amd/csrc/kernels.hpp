@@ -38,5 +38,8 @@ struct GemmArgs {
 enum class Path { Decode, Prefill };
 size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+// independent products sharing N, K and k (groups[i].N/K/k equal), one launch
+// per 32 groups; groups with M == 0 are skipped
+hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s);
 
 }  // namespace splice

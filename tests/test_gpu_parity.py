@@ -301,3 +301,36 @@ def test_grouped_moe_sampled():
         assert_gemm_close(host(groups[e]["Y"])[:, cols], o["Y"], f"expert {e}")
     for g in groups:
         assert torch.isfinite(g["Y"]).all()
+
+
+@pytest.mark.parametrize("k", [0, 8])
+def test_grouped_many_ragged_groups(k):
+    """40 groups (more than one launch's worth), ragged N and M, empty groups,
+    each group against the oracle on its own inputs."""
+    K, N, G = 256, 160, 40
+    g = np.random.default_rng(11 + k)
+    Ms = g.choice([0, 1, 5, 64, 130, 300], size=G)
+    groups, refs = [], []
+    for e in range(G):
+        Me = int(Ms[e])
+        Xw = synth.activations(9, e % 4, 128, K, 2 + 10 * e, "student", n_out=8)
+        X = synth.activations(9, e % 4, max(Me, 1), K, 3 + 10 * e, "student", n_out=8)[:Me]
+        W = synth.weights(9, 50 + e, N, K)
+        Xwd, Xd, Wd = dev(Xw), dev(np.ascontiguousarray(X)), dev(W)
+        idx, ax, _ = S.select_channels(Xwd, k)
+        aw = S.compute_alpha(Wd, idx)
+        if Me:
+            gx = S.quantize_nvfp4(Xd, idx, ax)
+        else:
+            gx = (Wd.new_zeros(0, K // 2, dtype=torch.uint8), Wd.new_zeros(0, K // 16, dtype=torch.uint8),
+                  Wd.new_zeros(0, k, dtype=torch.int16))
+        gw = S.quantize_nvfp4(Wd, idx, aw)
+        Y = torch.full((Me, N), float("nan"), device="cuda")
+        groups.append(dict(Xq=gx[0], Xs=gx[1], alpha_x=ax, X_S=gx[2], Wq=gw[0], Ws=gw[1], alpha_w=aw,
+                           W_S=gw[2], Y=Y))
+        refs.append(oracle_pipeline(Xw, np.ascontiguousarray(X), W, k)["Y"] if Me else None)
+    S.splice_gemm_grouped(groups, N, K, k)
+    torch.cuda.synchronize()
+    for e in range(G):
+        if refs[e] is not None:
+            assert_gemm_close(host(groups[e]["Y"]), refs[e], f"group {e} M={int(Ms[e])}")
