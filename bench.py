@@ -226,7 +226,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     dev = torch.device("cuda:0")
     out = {}
     # ---------------- prefill overhead vs the plain NVFP4 GEMM on identical bf16 inputs
-    nv_ms, nv_full_ms, sp_full_ms = {}, {}, {}
+    nv_ms, sp_ms, nv_full_ms, sp_full_ms = {}, {}, {}, {}
     empty = torch.zeros(0, dtype=torch.int32, device=dev)
     for n in names:
         p = P[n]
@@ -239,23 +239,30 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             S.nvfp4_gemm(xq0[0], xq0[1], ax0, wq0[0], wq0[1], aw0, path=S.PATH_PREFILL, out=Y0)
         nv_ms[n] = timed(torch, stream, lambda i: S.nvfp4_gemm(xq0[0], xq0[1], ax0, wq0[0], wq0[1], aw0,
                                                               path=S.PATH_PREFILL, out=Y0), 10)
+        xq, xs, xS = p["xpack"]
+        wq, ws, wS = p["wpack"]
+        for _ in range(3):
+            S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])
+        sp_ms[n] = timed(torch, stream, lambda i: S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS,
+                                                               path=S.PATH_PREFILL, out=p["Y"]), 10)
         nv_full_ms[n] = timed(torch, stream, lambda i: (
             S.quantize_nvfp4(p["X"], empty, ax0, out=xq0),
             S.nvfp4_gemm(xq0[0], xq0[1], ax0, wq0[0], wq0[1], aw0, path=S.PATH_PREFILL, out=Y0)), 10)
-        xq, xs, xS = p["xpack"]
-        wq, ws, wS = p["wpack"]
         sp_full_ms[n] = timed(torch, stream, lambda i: (
             S.quantize_nvfp4(p["X"], p["idx"], p["ax"], out=p["xpack"]),
             S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])), 10)
         del xq0, wq0, Y0
-    tot_sp, tot_nv = sum(gemm_ms.values()), sum(nv_ms.values())
+    tot_sp, tot_nv = sum(sp_ms.values()), sum(nv_ms.values())
     out["prefill"] = {
+        "timing": "each GEMM back to back on resident inputs (HIP events); gemm_ms_in_step are the "
+                  "same launches inside the timed step, after the preparation kernels",
         "gemm_tflops": round(sum(flops.values()) / (tot_sp * 1e-3) / 1e12, 2),
         "nvfp4_gemm_tflops": round(sum(flops.values()) / (tot_nv * 1e-3) / 1e12, 2),
         "overhead_gemm_pct": round(100.0 * (tot_sp - tot_nv) / tot_nv, 2),
         "overhead_projection_pct": round(100.0 * (sum(sp_full_ms.values()) - sum(nv_full_ms.values()))
                                          / sum(nv_full_ms.values()), 2),
-        "gemm_ms": {n: round(v, 4) for n, v in gemm_ms.items()},
+        "gemm_ms": {n: round(v, 4) for n, v in sp_ms.items()},
+        "gemm_ms_in_step": {n: round(v, 4) for n, v in gemm_ms.items()},
         "nvfp4_ms": {n: round(v, 4) for n, v in nv_ms.items()},
     }
     log("prefill", out["prefill"])
@@ -335,6 +342,10 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                           "weight_GBps": round(wbytes / (tg * 1e-3) / 1e9, 1)}
     log("moe", out["moe_grouped"])
 
+    # ---------------- protected-channel sweep: error vs the BF16 product, time per k
+    out["sweep"] = sweep_measurements(torch, S, synth, dev)
+    log("sweep", out["sweep"])
+
     # ---------------- cold path: selection and weight pre-split per layer
     def cold(i):
         for n in names:
@@ -345,6 +356,51 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
     out["reselect_layer_ms"] = round(timed(torch, stream, cold, 5), 4)
     return out
+
+
+def sweep_measurements(torch, S, synth, dev):
+    """K=4096, N=12288, M in {64, 4096}: top-k protection for k in {0, 64, 128,
+    256} and 64 random channels.  Error is the relative Frobenius distance of
+    the SpliceGEMM output to the fp64 product of the bf16 inputs; time is the
+    GEMM alone (HIP-graph replay)."""
+    K, N = synth.SWEEP_KN
+    res = {}
+    for M in synth.SWEEP_MS:
+        d = synth.sweep(M)
+        Xw = torch.from_numpy(d["X_warm"].view(np.int16)).to(dev)
+        X = torch.from_numpy(d["X"].view(np.int16)).to(dev)
+        W = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+        Xf = X.view(torch.bfloat16).to(torch.float64)
+        Wf = W.view(torch.bfloat16).to(torch.float64)
+        Yref = Xf @ Wf.T
+        nref = torch.linalg.norm(Yref).item()
+        del Xf, Wf
+        t0 = None
+        for case in ("k0", "top64", "top128", "top256", "rand64"):
+            if case == "rand64":
+                idx = torch.from_numpy(d["random64"]).to(dev)
+                ax = S.compute_alpha(Xw, idx)
+                k = 64
+            else:
+                k = 0 if case == "k0" else int(case[3:])
+                idx, ax, _ = S.select_channels(Xw, k)
+            aw = S.compute_alpha(W, idx)
+            xq, xs, xS = S.quantize_nvfp4(X, idx, ax)
+            wq, ws, wS = S.quantize_nvfp4(W, idx, aw)
+            Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+
+            def call(i):
+                S.splice_gemm(xq, xs, ax, xS if k else None, wq, ws, aw, wS if k else None, out=Y)
+            t = graph_timed(torch, call, 20)
+            call(0)
+            torch.cuda.synchronize()
+            err = torch.linalg.norm(Y.to(torch.float64) - Yref).item() / nref
+            t0 = t if case == "k0" else t0
+            res[f"M{M}_{case}"] = {"rel_err_vs_bf16": round(err, 6), "us": round(t * 1e3, 2),
+                                   "TFLOPs": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 2),
+                                   "overhead_vs_k0_pct": round(100.0 * (t - t0) / t0, 2)}
+        del Yref
+    return res
 
 
 def cpu_baseline(args, host, names, flops_per_row):

@@ -181,22 +181,55 @@ __device__ __forceinline__ void prefill_tile(const GemmArgs &a, int tm, int tn, 
         for (int j = 0; j < C::FN; j++) acc[i][j] *= alpha;
     if (TAIL) {
         const int k = a.k;
-        const bool al = (k % 8) == 0;
-        for (int kk = 0; kk < k; kk += 32) {
-            const int c0 = kk + g * 8;
-            const int valid = max(0, min(8, k - c0));
-            bf16x8 af[C::FM];
+        if (k % 32 == 0) {
+            // clamped rows (they only feed outputs that are not stored); the side
+            // loads of up to 64 channels are issued before the first MFMA
+            const uint16_t *xs[C::FM], *wsp[C::FN];
 #pragma unroll
-            for (int i = 0; i < C::FM; i++) {
-                const int64_t m = m0 + wm * C::WM + i * 16 + rr;
-                af[i] = load_bf16x8(a.X_S + m * k + c0, (m < M) ? valid : 0, al);
+            for (int i = 0; i < C::FM; i++)
+                xs[i] = a.X_S + min(m0 + wm * C::WM + i * 16 + rr, M - 1) * k + g * 8;
+#pragma unroll
+            for (int j = 0; j < C::FN; j++)
+                wsp[j] = a.W_S + min(n0 + wn * C::WN + j * 16 + rr, N - 1) * k + g * 8;
+            for (int kc = 0; kc < k; kc += 64) {
+                bf16x8 af[2][C::FM], bfr[2][C::FN];
+#pragma unroll
+                for (int s = 0; s < 2; s++) {
+                    const int c = min(kc + 32 * s, k - 32);
+#pragma unroll
+                    for (int i = 0; i < C::FM; i++)
+                        af[s][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs[i] + c));
+#pragma unroll
+                    for (int j = 0; j < C::FN; j++)
+                        bfr[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wsp[j] + c));
+                }
+#pragma unroll
+                for (int s = 0; s < 2; s++) {
+                    if (kc + 32 * s >= k) break;
+#pragma unroll
+                    for (int j = 0; j < C::FN; j++)
+#pragma unroll
+                        for (int i = 0; i < C::FM; i++) acc[i][j] = mfma_bf16(af[s][i], bfr[s][j], acc[i][j]);
+                }
             }
+        } else {
+            const bool al = (k % 8) == 0;
+            for (int kk = 0; kk < k; kk += 32) {
+                const int c0 = kk + g * 8;
+                const int valid = max(0, min(8, k - c0));
+                bf16x8 af[C::FM];
 #pragma unroll
-            for (int j = 0; j < C::FN; j++) {
-                const int64_t n = n0 + wn * C::WN + j * 16 + rr;
-                const bf16x8 bf = load_bf16x8(a.W_S + n * k + c0, (n < N) ? valid : 0, al);
+                for (int i = 0; i < C::FM; i++) {
+                    const int64_t m = m0 + wm * C::WM + i * 16 + rr;
+                    af[i] = load_bf16x8(a.X_S + m * k + c0, (m < M) ? valid : 0, al);
+                }
 #pragma unroll
-                for (int i = 0; i < C::FM; i++) acc[i][j] = mfma_bf16(af[i], bf, acc[i][j]);
+                for (int j = 0; j < C::FN; j++) {
+                    const int64_t n = n0 + wn * C::WN + j * 16 + rr;
+                    const bf16x8 bf = load_bf16x8(a.W_S + n * k + c0, (n < N) ? valid : 0, al);
+#pragma unroll
+                    for (int i = 0; i < C::FM; i++) acc[i][j] = mfma_bf16(af[i], bf, acc[i][j]);
+                }
             }
         }
     }
@@ -408,46 +441,23 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
         lds_barrier();      // the prefetch of step kt+2 stays in flight
     }
 
+    // ---- epilogue: Y = alpha_x*alpha_w * acc + X_S W_S^T
     const float alpha = (*a.alpha_x) * (*a.alpha_w);
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) acc[i][j] *= alpha;
-    if (TAIL) {
-        const int k = a.k;
-        const bool al = (k % 8) == 0;
-        for (int kk = 0; kk < k; kk += 16) {
-            const int c0 = kk + g * 8;
-            const int valid = max(0, min(8, k - c0));
-            bf16x8 af[C::FM];
-#pragma unroll
-            for (int i = 0; i < C::FM; i++) {
-                const int64_t m = m0 + wm * C::WM + i * 32 + rr;
-                af[i] = load_bf16x8(a.X_S + m * k + c0, (m < M) ? valid : 0, al);
-            }
-#pragma unroll
-            for (int j = 0; j < C::FN; j++) {
-                const int64_t n = n0 + wn * C::WN + j * 32 + rr;
-                const bf16x8 bf = load_bf16x8(a.W_S + n * k + c0, (n < N) ? valid : 0, al);
-#pragma unroll
-                for (int i = 0; i < C::FM; i++) acc[i][j] = mfma32_bf16(af[i], bf, acc[i][j]);
-            }
-        }
-    }
+    const int k = TAIL ? a.k : 0;
     const int64_t mb = m0 + wm * C::WM + g * 4, nb = n0 + wn * C::WN + rr;
     float *yb = a.Y + mb * a.ldy + nb;
-    if (m0 + C::BM <= M && n0 + C::BN <= N) {
-#pragma unroll
-        for (int i = 0; i < C::FM; i++)
+    const bool full = m0 + C::BM <= M && n0 + C::BN <= N;
+    // stores (or, with add, adds into Y) row fragment i of v; rows past M and
+    // columns past N are skipped
+    auto store_rows = [&](int i, const f32x16 (&v)[C::FN], bool add) {
+        if (full) {
 #pragma unroll
             for (int q = 0; q < 16; q++) {
                 float *yr = yb + (int64_t)(i * 32 + (q >> 2) * 8 + (q & 3)) * a.ldy;
 #pragma unroll
-                for (int j = 0; j < C::FN; j++) yr[j * 32] = acc[i][j][q];
+                for (int j = 0; j < C::FN; j++) yr[j * 32] = add ? yr[j * 32] + v[j][q] : v[j][q];
             }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C::FM; i++)
+        } else {
 #pragma unroll
             for (int q = 0; q < 16; q++) {
                 const int dm = i * 32 + (q >> 2) * 8 + (q & 3);
@@ -455,9 +465,99 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
                 float *yr = yb + (int64_t)dm * a.ldy;
 #pragma unroll
                 for (int j = 0; j < C::FN; j++)
-                    if (nb + j * 32 < N) yr[j * 32] = acc[i][j][q];
+                    if (nb + j * 32 < N) yr[j * 32] = add ? yr[j * 32] + v[j][q] : v[j][q];
             }
+        }
+    };
+    // Side operands (k a multiple of 16): staged through the idle LDS stage
+    // buffers in passes of up to 128 channels, 64 per buffer, in the
+    // 128-byte-row swizzled layout of the FP16 tiles.  All loads of a buffer
+    // are issued before its stores; rows past M or N are clamped and channels
+    // past k re-read the last ones (neither reaches a stored output).  Per
+    // 32-row fragment the side product goes into a small separate
+    // accumulator and the first pass stores Y = fma(alpha, acc, side), so the
+    // FP4 accumulator is only read, never rewritten; later passes (k > 128)
+    // add their side products into Y.
+    const bool staged = TAIL && k > 0 && k % 16 == 0;
+    auto stage = [&](int kp, int kn) {
+        const int r0 = tid >> 3, cc = tid & 7;              // rows r0 + 32u, chunk cc
+        const uint16_t *xp = a.X_S + cc * 8, *wp = a.W_S + cc * 8;
+        for (int ch = 0; ch * C::BKL < kn; ch++) {
+            const int c = min(kp + ch * C::BKL + cc * 8, k - 8) - cc * 8;
+            u32x4 v[16];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                v[u] = *reinterpret_cast<const u32x4 *>(xp + min(m0 + r0 + 32 * u, M - 1) * k + c);
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                v[8 + u] = *reinterpret_cast<const u32x4 *>(wp + min(n0 + r0 + 32 * u, N - 1) * k + c);
+#pragma unroll
+            for (int u = 0; u < 16; u++)
+                *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + 32 * u, cc)) = v[u];
+        }
+        lds_barrier();
+    };
+    // side product of row fragment i over the kn staged channels
+    auto side_staged = [&](int i, int kn, f32x16 (&side)[C::FN]) {
+        for (int s = 0; s < kn / 16; s++) {
+            const uint8_t *tile = lds + (s >> 2) * C::TILE;
+            const int c = 2 * (s & 3) + g;
+            const bf16x8 af = *reinterpret_cast<const bf16x8 *>(tile + f16_off(arow + i * 32, c));
+#pragma unroll
+            for (int j = 0; j < C::FN; j++) {
+                const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(tile + f16_off(brow + j * 32, c));
+                side[j] = mfma32_bf16(af, bf, side[j]);
+            }
+        }
+    };
+    const int kn0 = staged ? min(2 * C::BKL, k) : 0;
+    if (staged) stage(0, kn0);
+#pragma unroll
+    for (int i = 0; i < C::FM; i++) {
+        f32x16 side[C::FN];
+#pragma unroll
+        for (int j = 0; j < C::FN; j++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) side[j][q] = 0.f;
+        if (staged) {
+            side_staged(i, kn0, side);
+        } else if (TAIL && k > 0) {     // k not a multiple of 16: direct loads, masked
+            const bool al = (k % 8) == 0;
+            const int64_t m = m0 + wm * C::WM + i * 32 + rr;
+            for (int kk = 0; kk < k; kk += 16) {
+                const int c0 = kk + g * 8;
+                const int valid = max(0, min(8, k - c0));
+                const bf16x8 af = load_bf16x8(a.X_S + m * k + c0, (m < M) ? valid : 0, al);
+#pragma unroll
+                for (int j = 0; j < C::FN; j++) {
+                    const int64_t n = n0 + wn * C::WN + j * 32 + rr;
+                    const bf16x8 bf = load_bf16x8(a.W_S + n * k + c0, (n < N) ? valid : 0, al);
+                    side[j] = mfma32_bf16(af, bf, side[j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; j++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) side[j][q] = __builtin_fmaf(alpha, acc[i][j][q], side[j][q]);
+        store_rows(i, side, false);
     }
+    // channels beyond the first 128: further passes add into the stored Y
+    if (staged)
+        for (int kp = 2 * C::BKL; kp < k; kp += 2 * C::BKL) {
+            const int kn = min(2 * C::BKL, k - kp);
+            lds_barrier();                                  // previous pass fully read
+            stage(kp, kn);
+            for (int i = 0; i < C::FM; i++) {
+                f32x16 side[C::FN];
+#pragma unroll
+                for (int j = 0; j < C::FN; j++)
+#pragma unroll
+                    for (int q = 0; q < 16; q++) side[j][q] = 0.f;
+                side_staged(i, kn, side);
+                store_rows(i, side, true);
+            }
+        }
 }
 
 template <bool TAIL>

@@ -101,6 +101,26 @@ def tiny():
     }
 
 
+SWEEP_KN = (4096, 12288)
+SWEEP_MS = (64, 4096)
+SWEEP_KS = (0, 64, 128, 256)
+
+
+def sweep(M: int):
+    """Protected-channel sweep inputs: K=4096, N=12288; X ~ N(0,1) with 64
+    channels x32; W ~ N(0, 0.02); 512-token warm-up; the 64 random channels of
+    the control case."""
+    K, N = SWEEP_KN
+    return {
+        "X_warm": activations(CFG_SWEEP, 0, 512, K, 2, "normal"),
+        "X": activations(CFG_SWEEP, 0, M, K, 3, "normal"),
+        "W": weights(CFG_SWEEP, 0, N, K),
+        "random64": random_channels(CFG_SWEEP, 0, K, 64),
+        "K": K,
+        "N": N,
+    }
+
+
 def projection(cfg: int, name: str, M: int, kind: str = "student", warm: int = 512):
     """Inputs of one Qwen3-8B-shaped projection: warm-up X, measured X, W."""
     K, N = QWEN3_8B[name]

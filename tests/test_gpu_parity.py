@@ -334,3 +334,34 @@ def test_grouped_many_ragged_groups(k):
     for e in range(G):
         if refs[e] is not None:
             assert_gemm_close(host(groups[e]["Y"]), refs[e], f"group {e} M={int(Ms[e])}")
+
+
+@pytest.mark.parametrize("M", synth.SWEEP_MS)
+@pytest.mark.parametrize("case", ["k0", "top64", "top128", "top256", "rand64"])
+def test_sweep_sampled(M, case):
+    """Protected-channel sweep shapes (K=4096, N=12288): top-k for every k of
+    the sweep and the random-channel control, full launch, sampled outputs."""
+    d = synth.sweep(M)
+    K = d["K"]
+    if case == "rand64":
+        idx = d["random64"]
+        idx_d = dev(idx)
+        ax = S.compute_alpha(dev(d["X_warm"]), idx_d)
+        k = 64
+    else:
+        k = int(case[3:]) if case != "k0" else 0
+        idx_d, ax, _ = S.select_channels(dev(d["X_warm"]), k)
+        idx = None
+    Wd = dev(d["W"])
+    aw = S.compute_alpha(Wd, idx_d)
+    xq, xs, xS = S.quantize_nvfp4(dev(d["X"]), idx_d, ax)
+    wq, ws, wS = S.quantize_nvfp4(Wd, idx_d, aw)
+    Y = S.splice_gemm(xq, xs, ax, xS if k else None, wq, ws, aw, wS if k else None)
+    torch.cuda.synchronize()
+    rows = np.arange(0, M, max(1, M // 48))
+    cols = np.arange(5, d["N"], 97)
+    o = oracle_pipeline(d["X_warm"], d["X"], d["W"], k, rows=rows, cols=cols, idx=idx)
+    if idx is None:
+        assert np.array_equal(host(idx_d), o["idx"])
+    assert scalar(ax) == np.float32(o["ax"]) and scalar(aw) == np.float32(o["aw"])
+    assert_gemm_close(host(Y)[np.ix_(rows, cols)], o["Y"], f"sweep M={M} {case}")
