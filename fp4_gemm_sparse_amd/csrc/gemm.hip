@@ -1166,13 +1166,18 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
         if (run_decode3_k<1, 1, 8, 16>(a, s, e)) return e;
         return run_decode2<1, 1, 8, 2>(a, s);
     }
+    // M in 17..64: wide N takes the single-round form with 48 columns per
+    // workgroup (one workgroup per CU at N = 12288); otherwise the looping
+    // form with 16 columns per workgroup and 8 waves over K
     if (a.M <= 32) {
         if (colblocks >= 512 && run_decode3_k<2, 3, 4, 8>(a, s, e)) return e;
-        if (run_decode3_k<2, 2, 4, 8>(a, s, e)) return e;
-        return run_decode2<2, 2, 8, 2>(a, s);
+        return run_decode2<2, 1, 8, 2>(a, s);
     }
-    if (run_decode3_k<4, 2, 4, 8>(a, s, e)) return e;
-    return run_decode2<4, 2, 8, 1>(a, s);
+    if (colblocks >= 512) {
+        if (run_decode3_k<4, 3, 4, 8>(a, s, e)) return e;
+        return run_decode2<4, 3, 8, 1>(a, s);
+    }
+    return run_decode2<4, 1, 8, 2>(a, s);
 }
 
 }  // namespace splice
