@@ -301,19 +301,19 @@ __global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
 
 // ===========================================================================
 // LDS-decode prefill path: each workgroup decodes every NVFP4 element of its
-// 256x256 tile exactly once per K step into a swizzled FP16 tile in LDS
-// (double buffered, 2 x 64 KB); the four waves (2x2, 128x128 each) read their
-// MFMA fragments from it with ds_read_b128 and run v_mfma_f32_32x32x16_f16.
-// While a wave multiplies stage kt it decodes its share of stage kt+1 from
-// registers (fetched one step earlier) into the other buffer, so decode VALU
-// work, global loads and LDS traffic all hide under the matrix cores.
-// Decode share per thread and step: 4 units of (row, 32-channel half) = 16
-// code bytes + 2 scale bytes -> 32 FP16 values.
+// 256x256 tile exactly once per K step (64 channels) into a swizzled FP16 tile
+// in LDS (double buffered, 2 x 64 KB); eight waves (2 x 4, 128 x 64 each, two
+// per SIMD) read their MFMA fragments from it with ds_read_b128 and run
+// v_mfma_f32_32x32x16_f16.  While a wave multiplies stage kt it decodes its
+// share of stage kt+1 from registers (fetched one step earlier) into the other
+// buffer; the second wave on each SIMD keeps the matrix core busy while the
+// first decodes, waits for LDS or sits at a barrier.
+// Decode share per thread and step: 2 units of (row, 32-channel half) = 32
+// code bytes + 4 scale bytes -> 64 FP16 values.
 // ===========================================================================
 struct LdsCfg {
-    static constexpr int BM = 256, BN = 256, BKL = 64, WM = 128, WN = 128, FM = 4, FN = 4;
+    static constexpr int BKL = 64;
     static constexpr int ROWB = BKL * 2;                 // 128 bytes of FP16 per row
-    static constexpr int TILE = (BM + BN) * ROWB;         // 64 KB per stage
 };
 
 // byte offset of 16-byte chunk c (8 channels) of row r in an FP16 tile.
@@ -326,13 +326,21 @@ __device__ __forceinline__ int f16_off(int r, int c)
     return r * LdsCfg::ROWB + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
 }
 
+// Each thread decodes one 8-channel piece of each of its two units per
+// sub-step.
+struct LdsTile {
+    static constexpr int BM = 256, BN = 256, BKL = 64, WM = 128, WN = 64, FM = 4, FN = 2;
+    static constexpr int TILE = (BM + BN) * LdsCfg::ROWB;   // 64 KB per stage
+};
+
 template <bool TAIL>
-__global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
+__global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
 {
-    using C = LdsCfg;
+    using C = LdsTile;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int wm = wave >> 2, wn = wave & 3;
     const int g = lane >> 5, rr = lane & 31;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int tiles_m = (int)((M + C::BM - 1) / C::BM), tiles_n = (int)((N + C::BN - 1) / C::BN);
@@ -342,42 +350,36 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
     const int64_t rowb = K / 2, rows = K / 16;
     const int nk = (int)(K / C::BKL);
 
-    // decode units of this thread: u = tid + 256*i; i = 0,1 -> X rows, 2,3 -> W rows
-    const int half = tid & 1;
-    int urow[4];
-    const uint8_t *ucode[4];
-    const uint8_t *uscale[4];
+    // decode units of this thread: unit 0 = X row tid/2, unit 1 = W row tid/2,
+    // channel half tid%2.  Rows past the edge read row 0 (never stored).
+    const int half = tid & 1, r = tid >> 1;
+    int urow[2];
+    const uint8_t *ucode[2];
+    const uint8_t *uscale[2];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int r = ((tid + 256 * (i & 1)) >> 1);            // 0..255 within the operand tile
-        const bool isx = i < 2;
+    for (int i = 0; i < 2; i++) {
+        const bool isx = i == 0;
         const int64_t gr = (isx ? m0 : n0) + r;
         const int64_t rr0 = gr < (isx ? M : N) ? gr : 0;
-        urow[i] = (isx ? 0 : C::BM) + r;                        // row in the combined LDS tile
+        urow[i] = (isx ? 0 : C::BM) + r;
         ucode[i] = (isx ? a.Xq : a.Wq) + rr0 * rowb + half * 16;
         uscale[i] = (isx ? a.Xs : a.Ws) + rr0 * rows + half * 2;
     }
-    u32x4 pc[4];
-    unsigned ps[4];
-    // Rows past the edge of the operand read its row 0 instead: an A row only
-    // reaches output row m and a B row only output column n, and those rows
-    // and columns are never stored, so no masking (and no wait) is needed.
+    u32x4 pc[2];
+    unsigned ps[2];
     auto gload = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 2; i++) {
             pc[i] = *reinterpret_cast<const u32x4 *>(ucode[i] + (int64_t)kt * 32);
             ps[i] = *reinterpret_cast<const uint16_t *>(uscale[i] + (int64_t)kt * 4);
         }
     };
-    auto decode_store = [&](uint8_t *tile) {
+    // piece d (8 channels) of both units into `tile`
+    auto decode_piece = [&](uint8_t *tile, int d) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const f16x2 s0 = e4m3_pair(ps[i] & 0xFFu), s1 = e4m3_pair((ps[i] >> 8) & 0xFFu);
-#pragma unroll
-            for (int d = 0; d < 4; d++) {
-                const f16x8 v = decode8(pc[i][d], d < 2 ? s0 : s1);
-                *reinterpret_cast<f16x8 *>(tile + f16_off(urow[i], half * 4 + d)) = v;
-            }
+        for (int i = 0; i < 2; i++) {
+            const f16x2 sc = e4m3_pair(d < 2 ? (ps[i] & 0xFFu) : ((ps[i] >> 8) & 0xFFu));
+            *reinterpret_cast<f16x8 *>(tile + f16_off(urow[i], half * 4 + d)) = decode8(pc[i][d], sc);
         }
     };
 
@@ -391,17 +393,12 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
 
     if (nk > 0) {
         gload(0);
-        decode_store(lds);
+#pragma unroll
+        for (int d = 0; d < 4; d++) decode_piece(lds, d);
         gload(min(1, nk - 1));
     }
     __syncthreads();
     const int arow = wm * C::WM + rr, brow = C::BM + wn * C::WN + rr;
-    auto decode_unit = [&](uint8_t *tile, int i) {
-        const f16x2 s0 = e4m3_pair(ps[i] & 0xFFu), s1 = e4m3_pair((ps[i] >> 8) & 0xFFu);
-#pragma unroll
-        for (int d = 0; d < 4; d++)
-            *reinterpret_cast<f16x8 *>(tile + f16_off(urow[i], half * 4 + d)) = decode8(pc[i][d], d < 2 ? s0 : s1);
-    };
     for (int kt = 0; kt < nk; kt++) {
         const uint8_t *cur = lds + (kt & 1) * C::TILE;
         uint8_t *nxt = lds + ((kt + 1) & 1) * C::TILE;
@@ -410,10 +407,6 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
         for (int i = 0; i < C::FM; i++) a0[i] = *reinterpret_cast<const f16x8 *>(cur + f16_off(arow + i * 32, g));
 #pragma unroll
         for (int j = 0; j < C::FN; j++) b0[j] = *reinterpret_cast<const f16x8 *>(cur + f16_off(brow + j * 32, g));
-        // Per sub-step: issue the fragment reads of sub-step s+1 first, then the
-        // LDS stores of this sub-step's decode unit, then the MFMAs.  LDS
-        // operations retire in order, so a wait for those reads never waits
-        // for stores queued behind them.
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             if (s < 3) {
@@ -424,7 +417,7 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
                 for (int j = 0; j < C::FN; j++)
                     b1[j] = *reinterpret_cast<const f16x8 *>(cur + f16_off(brow + j * 32, (s + 1) * 2 + g));
             }
-            decode_unit(nxt, s);      // on the last step this fills the idle buffer
+            decode_piece(nxt, s);     // on the last step this fills the idle buffer
 #pragma unroll
             for (int j = 0; j < C::FN; j++)
 #pragma unroll
@@ -442,13 +435,19 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
     }
 
     // ---- epilogue: Y = alpha_x*alpha_w * acc + X_S W_S^T
+    // The side operands (k a multiple of 16) go through the idle LDS stage
+    // buffers in passes of up to 128 channels, 64 per buffer, in the same
+    // swizzled 128-byte-row layout; all loads of a buffer are issued before its
+    // stores (rows past M or N clamped, channels past k re-reading the last
+    // ones: neither reaches a stored output).  Per 32-row fragment the side
+    // product goes into a small separate accumulator and the first pass stores
+    // Y = fma(alpha, acc, side), so the FP4 accumulator is only read; further
+    // passes (k > 128) add their side products into Y.
     const float alpha = (*a.alpha_x) * (*a.alpha_w);
     const int k = TAIL ? a.k : 0;
     const int64_t mb = m0 + wm * C::WM + g * 4, nb = n0 + wn * C::WN + rr;
     float *yb = a.Y + mb * a.ldy + nb;
     const bool full = m0 + C::BM <= M && n0 + C::BN <= N;
-    // stores (or, with add, adds into Y) row fragment i of v; rows past M and
-    // columns past N are skipped
     auto store_rows = [&](int i, const f32x16 (&v)[C::FN], bool add) {
         if (full) {
 #pragma unroll
@@ -469,35 +468,25 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
             }
         }
     };
-    // Side operands (k a multiple of 16): staged through the idle LDS stage
-    // buffers in passes of up to 128 channels, 64 per buffer, in the
-    // 128-byte-row swizzled layout of the FP16 tiles.  All loads of a buffer
-    // are issued before its stores; rows past M or N are clamped and channels
-    // past k re-read the last ones (neither reaches a stored output).  Per
-    // 32-row fragment the side product goes into a small separate
-    // accumulator and the first pass stores Y = fma(alpha, acc, side), so the
-    // FP4 accumulator is only read, never rewritten; later passes (k > 128)
-    // add their side products into Y.
     const bool staged = TAIL && k > 0 && k % 16 == 0;
     auto stage = [&](int kp, int kn) {
-        const int r0 = tid >> 3, cc = tid & 7;              // rows r0 + 32u, chunk cc
+        const int r0 = tid >> 3, cc = tid & 7;              // rows r0 + 64u, chunk cc
         const uint16_t *xp = a.X_S + cc * 8, *wp = a.W_S + cc * 8;
         for (int ch = 0; ch * C::BKL < kn; ch++) {
             const int c = min(kp + ch * C::BKL + cc * 8, k - 8) - cc * 8;
-            u32x4 v[16];
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                v[u] = *reinterpret_cast<const u32x4 *>(xp + min(m0 + r0 + 64 * u, M - 1) * k + c);
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                v[4 + u] = *reinterpret_cast<const u32x4 *>(wp + min(n0 + r0 + 64 * u, N - 1) * k + c);
 #pragma unroll
             for (int u = 0; u < 8; u++)
-                v[u] = *reinterpret_cast<const u32x4 *>(xp + min(m0 + r0 + 32 * u, M - 1) * k + c);
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-                v[8 + u] = *reinterpret_cast<const u32x4 *>(wp + min(n0 + r0 + 32 * u, N - 1) * k + c);
-#pragma unroll
-            for (int u = 0; u < 16; u++)
-                *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + 32 * u, cc)) = v[u];
+                *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + 64 * u, cc)) = v[u];
         }
         lds_barrier();
     };
-    // side product of row fragment i over the kn staged channels
     auto side_staged = [&](int i, int kn, f32x16 (&side)[C::FN]) {
         for (int s = 0; s < kn / 16; s++) {
             const uint8_t *tile = lds + (s >> 2) * C::TILE;
@@ -542,7 +531,6 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
             for (int q = 0; q < 16; q++) side[j][q] = __builtin_fmaf(alpha, acc[i][j][q], side[j][q]);
         store_rows(i, side, false);
     }
-    // channels beyond the first 128: further passes add into the stored Y
     if (staged)
         for (int kp = 2 * C::BKL; kp < k; kp += 2 * C::BKL) {
             const int kn = min(2 * C::BKL, k - kp);
@@ -563,19 +551,19 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(GemmArgs a)
 template <bool TAIL>
 static hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
 {
-    const int64_t tiles = ((a.M + LdsCfg::BM - 1) / LdsCfg::BM) * ((a.N + LdsCfg::BN - 1) / LdsCfg::BN);
-    const size_t lds = 2 * LdsCfg::TILE;
-    static bool attr = false;
+    using C = LdsTile;
+    const int64_t tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+    const size_t lds = 2 * C::TILE;
+    static bool attr = false;       // raise the dynamic-LDS limit once per instantiation
     if (!attr) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_lds_kernel<TAIL>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(512), lds, s, a);
     return hipGetLastError();
 }
-
 
 template <int BM, int BN, bool TAIL>
 static hipError_t launch_prefill(const GemmArgs &a, hipStream_t s)
