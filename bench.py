@@ -6,11 +6,12 @@
 Workload (the value line): one Qwen3-8B-shaped layer in prefill, M = 8192
 tokens through the seven projections (q, k, v, o, gate, up, down) with 64
 protected BF16 channels each.  One step is the whole hot path over that batch:
-per projection, channel statistics and top-64 selection on a 512-token
-warm-up batch, the weight tensor scale, the weight pre-split (quantize + side
-gather), the activation preparation and the SpliceGEMM.  `value` is the
-step's useful work, sum of 2*M*N*K over the projections, divided by the step
-time (inputs resident in HBM).
+per distinct layer input (q, k and v read one hidden state, gate and up
+another, o and down their own), channel statistics and top-64 selection on a
+512-token warm-up batch and the activation preparation; per projection, the
+weight tensor scale, the weight pre-split (quantize + side gather) and the
+SpliceGEMM.  `value` is the step's useful work, sum of 2*M*N*K over the
+projections, divided by the step time (inputs resident in HBM).
 
 The same run also measures, each timed on its own: the projections' GEMMs
 against the plain NVFP4 GEMM on identical inputs (overhead), the decode
@@ -104,23 +105,36 @@ def main():
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
 
+    # activation-side work (statistics, selection, activation preparation) is
+    # done once per distinct layer input: q, k and v read the same hidden
+    # state, and so do gate and up.  Weight-side work is per projection.
+    groups = {}
+    for n in names:
+        sid = synth.INPUT_STREAM[n]
+        if sid in groups:
+            continue
+        h = host[n]
+        K = h["K"]
+        groups[sid] = dict(
+            K=K, Xw=to_dev(h["X_warm"]), X=to_dev(h["X"]),
+            stats=S.ChannelStats.empty(K),
+            idx=torch.empty(K_PROT, dtype=torch.int32, device=dev),
+            ax=torch.empty(1, dtype=torch.float32, device=dev),
+            xpack=(torch.empty(M_PREFILL, K // 2, dtype=torch.uint8, device=dev),
+                   torch.empty(M_PREFILL, K // 16, dtype=torch.uint8, device=dev),
+                   torch.empty(M_PREFILL, K_PROT, dtype=torch.int16, device=dev)))
     P = {}
     for n in names:
         h = host[n]
         K, N = h["K"], h["N"]
+        g = groups[synth.INPUT_STREAM[n]]
         P[n] = dict(
-            K=K, N=N,
-            Xw=to_dev(h["X_warm"]), X=to_dev(h["X"]), W=to_dev(h["W"]),
-            stats=S.ChannelStats.empty(K),
-            idx=torch.empty(K_PROT, dtype=torch.int32, device=dev),
-            ax=torch.empty(1, dtype=torch.float32, device=dev),
+            K=K, N=N, grp=g, W=to_dev(h["W"]),
+            Xw=g["Xw"], X=g["X"], stats=g["stats"], idx=g["idx"], ax=g["ax"], xpack=g["xpack"],
             aw=torch.empty(1, dtype=torch.float32, device=dev),
             wpack=(torch.empty(N, K // 2, dtype=torch.uint8, device=dev),
                    torch.empty(N, K // 16, dtype=torch.uint8, device=dev),
                    torch.empty(N, K_PROT, dtype=torch.int16, device=dev)),
-            xpack=(torch.empty(M_PREFILL, K // 2, dtype=torch.uint8, device=dev),
-                   torch.empty(M_PREFILL, K // 16, dtype=torch.uint8, device=dev),
-                   torch.empty(M_PREFILL, K_PROT, dtype=torch.int16, device=dev)),
             Y=torch.empty(M_PREFILL, N, dtype=torch.float32, device=dev),
         )
     alpha_ws = torch.empty(S.lib().splice_alpha_workspace_size(), dtype=torch.uint8, device=dev)
@@ -129,13 +143,17 @@ def main():
     gemm_events = []
 
     def step(record):
+        done = set()
         for n in names:
             p = P[n]
-            p["stats"].count = 0
-            S.select_channels(p["Xw"], K_PROT, p["stats"], out=(p["idx"], p["ax"]))
+            g = p["grp"]
+            if id(g) not in done:
+                done.add(id(g))
+                g["stats"].count = 0
+                S.select_channels(g["Xw"], K_PROT, g["stats"], out=(g["idx"], g["ax"]))
+                S.quantize_nvfp4(g["X"], g["idx"], g["ax"], out=g["xpack"])
             S.compute_alpha(p["W"], p["idx"], out=p["aw"], ws=alpha_ws)
             S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
-            S.quantize_nvfp4(p["X"], p["idx"], p["ax"], out=p["xpack"])
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -179,7 +197,8 @@ def main():
         "config": {"workload": "qwen3-8b-layer-prefill", "tokens": M_PREFILL,
                    "projections": {n: [P[n]["K"], P[n]["N"]] for n in names},
                    "protected_channels": K_PROT, "warmup_tokens": 512,
-                   "step": "stats+select, weight alpha+pre-split, activation prep, SpliceGEMM"},
+                   "step": "per distinct layer input (q/k/v share one, gate/up share one): stats+select "
+                           "and activation prep; per projection: weight alpha+pre-split and SpliceGEMM"},
         "roofline": roofline,
     }
 
@@ -348,10 +367,14 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
 
     # ---------------- cold path: selection and weight pre-split per layer
     def cold(i):
+        done = set()
         for n in names:
             p = P[n]
-            p["stats"].count = 0
-            S.select_channels(p["Xw"], K_PROT, p["stats"], out=(p["idx"], p["ax"]))
+            g = p["grp"]
+            if id(g) not in done:
+                done.add(id(g))
+                g["stats"].count = 0
+                S.select_channels(g["Xw"], K_PROT, g["stats"], out=(g["idx"], g["ax"]))
             S.compute_alpha(p["W"], p["idx"], out=p["aw"])
             S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
     out["reselect_layer_ms"] = round(timed(torch, stream, cold, 5), 4)
@@ -404,19 +427,24 @@ def sweep_measurements(torch, S, synth, dev):
 
 
 def cpu_baseline(args, host, names, flops_per_row):
-    """The fp64 oracle on the host cores: the same step for every projection
-    (statistics and selection on the warm-up batch, weight alpha and full
-    weight quantization, activation preparation and the product) on the first
-    `cpu_rows` token rows."""
+    """The fp64 oracle on the host cores: the same step as the GPU's
+    (statistics, selection and activation preparation once per distinct layer
+    input; weight alpha, full weight quantization and the product per
+    projection) on the first `cpu_rows` token rows."""
     import oracle as O
+    from fp4_gemm_sparse_amd import synth
     rows = args.cpu_rows
     t0 = time.perf_counter()
+    act = {}
     for n in names:
         h = host[n]
-        idx, ax, _ = O.select_channels(h["X_warm"], K_PROT)
+        sid = synth.INPUT_STREAM[n]
+        if sid not in act:
+            idx, ax, _ = O.select_channels(h["X_warm"], K_PROT)
+            act[sid] = (idx, ax, O.quantize_nvfp4(h["X"][:rows], idx, ax))
+        idx, ax, (xq, xs, xS) = act[sid]
         aw = O.compute_alpha(h["W"], idx)
         wq, ws, wS = O.quantize_nvfp4(h["W"], idx, aw)
-        xq, xs, xS = O.quantize_nvfp4(h["X"][:rows], idx, ax)
         O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
     dt = time.perf_counter() - t0
     v = flops_per_row * rows / dt / 1e12
