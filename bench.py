@@ -64,9 +64,15 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the GEMM kernel sources with comments and blank space removed,
+    so a comment edit does not void counter figures taken on the same code."""
+    import re
     h = hashlib.sha256()
     for f in ("common.hpp", "gemm.hip"):
-        h.update(open(os.path.join(ROOT, "fp4_gemm_sparse_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "fp4_gemm_sparse_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

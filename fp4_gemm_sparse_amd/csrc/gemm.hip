@@ -3,18 +3,17 @@
 //
 //   Y = (alpha_x * alpha_w) * sum_j deq(Xq)[m,j] deq(Wq)[n,j]  +  X_S W_S^T
 //
-// Datapath: NVFP4 codes are decoded in registers, exactly, to FP16 (an E2M1
-// value times an E4M3 scale has at most 6 significant bits) and multiplied on
-// the FP16 matrix cores (v_mfma_f32_16x16x32_f16) into fp32 accumulators.
-// The accumulator is then scaled by alpha_x*alpha_w and the BF16 side product
-// X_S W_S^T (exact, unscaled protected columns) is accumulated into the same
-// registers with v_mfma_f32_16x16x32_bf16 before the single store of Y.
+// Datapath: NVFP4 codes are decoded exactly to FP16 (an E2M1 value times an
+// E4M3 scale has at most 6 significant bits) and multiplied on the FP16 matrix
+// cores (v_mfma_f32_32x32x16_f16 in the 256x256 prefill tile,
+// v_mfma_f32_16x16x32_f16 elsewhere) into fp32 accumulators.  The BF16 side
+// product X_S W_S^T of the exact, unscaled protected columns runs on the BF16
+// matrix cores and is added to alpha_x*alpha_w times the FP4 accumulator
+// before the single store of Y.
 //
-// Reduction order inside a K step of 128: lane group g (lanes 16g..16g+15)
-// owns channels [32g, 32g+32) of the step, i.e. one 16-byte chunk of codes
-// and two block scales per row; MFMA sub-step s consumes its channels
-// [32g+8s, 32g+8s+8).  A and B use the same mapping, so this only permutes
-// the order of the sum.
+// Reduction order: each MFMA consumes whole 8-channel pieces of one or two
+// NVFP4 blocks, A and B with the same channel mapping, so the hardware order
+// only permutes the terms of each dot product; K steps are summed in order.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -131,9 +131,10 @@ int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
  * Xq/Xs: [M, K/2] / [M, K/16];  Wq/Ws: [N, K/2] / [N, K/16];
  * X_S: bf16 [M, k], W_S: bf16 [N, k] (unscaled, bit copies of the protected
  * columns); Y: fp32 [M, N] out with row stride ldy.
- * The NVFP4 products are decoded exactly to BF16 and multiplied on the BF16
- * matrix cores with fp32 accumulation; the accumulator is scaled by
- * alpha_x*alpha_w before the BF16 side product is added into it.
+ * The NVFP4 operands are decoded exactly to FP16 (an E2M1 value times an
+ * E4M3 scale has at most 6 significant bits) and multiplied on the FP16
+ * matrix cores with fp32 accumulation; the BF16 side product is computed on
+ * the BF16 matrix cores and added to alpha_x*alpha_w times that accumulator.
  * path: SPLICE_PATH_AUTO (decode path when M <= SPLICE_DECODE_MAX_M),
  *       SPLICE_PATH_DECODE (requires M <= SPLICE_DECODE_MAX_M) or
  *       SPLICE_PATH_PREFILL.
