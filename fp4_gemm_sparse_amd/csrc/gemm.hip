@@ -19,29 +19,13 @@
 
 namespace splice {
 
-constexpr int BK = 128;              // channels per K step
-constexpr int CODE_ROW = BK / 2;     // 64 code bytes per row per step
-constexpr int SCALE_ROW = BK / 16;   // 8 scale bytes per row per step
+constexpr int BK = 128;              // channels per decode-path K chunk
+constexpr int CODE_ROW = BK / 2;     // 64 code bytes per row per chunk
+constexpr int SCALE_ROW = BK / 16;   // 8 scale bytes per row per chunk
 
 // ===========================================================================
-// Prefill path: 256-thread workgroups (2x2 waves) over BM x BN output tiles,
-// codes and scales staged through double-buffered LDS, each wave decoding its
-// own fragments from the packed codes.
+// Prefill path
 // ===========================================================================
-template <int BM, int BN>
-struct Prefill {
-    static constexpr int WM = BM / 2, WN = BN / 2;
-    static constexpr int FM = WM / 16, FN = WN / 16;
-    static constexpr int XC = BM * CODE_ROW, WC = BN * CODE_ROW;
-    static constexpr int XSC = BM * SCALE_ROW, WSC = BN * SCALE_ROW;
-    static constexpr int STAGE = XC + WC + XSC + WSC;
-    static constexpr int XCH = BM * 4 / 256, WCH = BN * 4 / 256;        // 16-B code chunks / thread
-    static constexpr int SCR = (BM + BN + 255) / 256;                   // scale rows / thread
-};
-
-// position of 16-byte chunk c of row r in LDS (XOR swizzle against bank conflicts)
-__device__ __forceinline__ int chunk_off(int r, int c) { return r * CODE_ROW + ((c ^ ((r >> 1) & 3)) << 4); }
-
 // XCD-aware tile order: consecutive workgroups go to different XCDs round
 // robin, so each XCD is handed a contiguous range of tiles; inside it tiles
 // walk GM tile-rows at a time so neighbours share operand rows in L2.
@@ -60,255 +44,19 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
     tn = in / gsz;
 }
 
-// One BM x BN output tile (tm, tn) of the product described by `a`.
-template <int BM, int BN, bool TAIL>
-__device__ __forceinline__ void prefill_tile(const GemmArgs &a, int tm, int tn, uint8_t *lds)
-{
-    using C = Prefill<BM, BN>;
-    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int g = lane >> 4, rr = lane & 15;
-    const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int64_t rowb = K / 2, rows = K / 16;
-    const int nk = (int)(K / BK);
-
-    // ---- global -> register staging of one K step
-    u32x4 xr[C::XCH], wr[C::WCH];
-    u32x2 sr[C::SCR];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < C::XCH; i++) {
-            const int c = tid + 256 * i, r = c >> 2, cc = c & 3;
-            const int64_t m = m0 + r;
-            xr[i] = (m < M) ? *reinterpret_cast<const u32x4 *>(a.Xq + m * rowb + (int64_t)kt * CODE_ROW + cc * 16)
-                            : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < C::WCH; i++) {
-            const int c = tid + 256 * i, r = c >> 2, cc = c & 3;
-            const int64_t n = n0 + r;
-            wr[i] = (n < N) ? *reinterpret_cast<const u32x4 *>(a.Wq + n * rowb + (int64_t)kt * CODE_ROW + cc * 16)
-                            : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < C::SCR; i++) {
-            const int r = tid + 256 * i;
-            u32x2 v = {0, 0};
-            if (r < BM) {
-                const int64_t m = m0 + r;
-                if (m < M) v = *reinterpret_cast<const u32x2 *>(a.Xs + m * rows + (int64_t)kt * SCALE_ROW);
-            } else if (r < BM + BN) {
-                const int64_t n = n0 + (r - BM);
-                if (n < N) v = *reinterpret_cast<const u32x2 *>(a.Ws + n * rows + (int64_t)kt * SCALE_ROW);
-            }
-            sr[i] = v;
-        }
-    };
-    auto lstore = [&](uint8_t *st) {
-#pragma unroll
-        for (int i = 0; i < C::XCH; i++) {
-            const int c = tid + 256 * i, r = c >> 2, cc = c & 3;
-            *reinterpret_cast<u32x4 *>(st + chunk_off(r, cc)) = xr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::WCH; i++) {
-            const int c = tid + 256 * i, r = c >> 2, cc = c & 3;
-            *reinterpret_cast<u32x4 *>(st + C::XC + chunk_off(r, cc)) = wr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::SCR; i++) {
-            const int r = tid + 256 * i;
-            if (r < BM + BN)
-                *reinterpret_cast<u32x2 *>(st + C::XC + C::WC + r * SCALE_ROW) = sr[i];
-        }
-    };
-
-    f32x4 acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (nk > 0) {
-        gload(0);
-        lstore(lds);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        uint8_t *cur = lds + (kt & 1) * C::STAGE;
-        if (kt + 1 < nk) gload(kt + 1);
-        // fragments of this wave
-        u32x4 xc[C::FM], wc[C::FN];
-        unsigned xs[C::FM], ws[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; i++) {
-            const int r = wm * C::WM + i * 16 + rr;
-            xc[i] = *reinterpret_cast<const u32x4 *>(cur + chunk_off(r, g));
-            xs[i] = *reinterpret_cast<const uint16_t *>(cur + C::XC + C::WC + r * SCALE_ROW + 2 * g);
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) {
-            const int r = wn * C::WN + j * 16 + rr;
-            wc[j] = *reinterpret_cast<const u32x4 *>(cur + C::XC + chunk_off(r, g));
-            ws[j] = *reinterpret_cast<const uint16_t *>(cur + C::XC + C::WC + C::XSC + r * SCALE_ROW + 2 * g);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            // A fragments of this sub-step stay live; B fragments are decoded
-            // one at a time and used at once.
-            f16x8 af[C::FM];
-#pragma unroll
-            for (int i = 0; i < C::FM; i++)
-                af[i] = decode8(xc[i][s], e4m3_pair((xs[i] >> ((s >> 1) * 8)) & 0xFFu));
-#pragma unroll
-            for (int j = 0; j < C::FN; j++) {
-                const f16x8 bf = decode8(wc[j][s], e4m3_pair((ws[j] >> ((s >> 1) * 8)) & 0xFFu));
-#pragma unroll
-                for (int i = 0; i < C::FM; i++) acc[i][j] = mfma_f16(af[i], bf, acc[i][j]);
-            }
-        }
-        if (kt + 1 < nk) lstore(lds + ((kt + 1) & 1) * C::STAGE);
-        __syncthreads();
-    }
-
-    // ---- epilogue: scale, BF16 side product, store
-    const float alpha = (*a.alpha_x) * (*a.alpha_w);
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) acc[i][j] *= alpha;
-    if (TAIL) {
-        const int k = a.k;
-        if (k % 32 == 0) {
-            // clamped rows (they only feed outputs that are not stored); the side
-            // loads of up to 64 channels are issued before the first MFMA
-            const uint16_t *xs[C::FM], *wsp[C::FN];
-#pragma unroll
-            for (int i = 0; i < C::FM; i++)
-                xs[i] = a.X_S + min(m0 + wm * C::WM + i * 16 + rr, M - 1) * k + g * 8;
-#pragma unroll
-            for (int j = 0; j < C::FN; j++)
-                wsp[j] = a.W_S + min(n0 + wn * C::WN + j * 16 + rr, N - 1) * k + g * 8;
-            for (int kc = 0; kc < k; kc += 64) {
-                bf16x8 af[2][C::FM], bfr[2][C::FN];
-#pragma unroll
-                for (int s = 0; s < 2; s++) {
-                    const int c = min(kc + 32 * s, k - 32);
-#pragma unroll
-                    for (int i = 0; i < C::FM; i++)
-                        af[s][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs[i] + c));
-#pragma unroll
-                    for (int j = 0; j < C::FN; j++)
-                        bfr[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wsp[j] + c));
-                }
-#pragma unroll
-                for (int s = 0; s < 2; s++) {
-                    if (kc + 32 * s >= k) break;
-#pragma unroll
-                    for (int j = 0; j < C::FN; j++)
-#pragma unroll
-                        for (int i = 0; i < C::FM; i++) acc[i][j] = mfma_bf16(af[s][i], bfr[s][j], acc[i][j]);
-                }
-            }
-        } else {
-            const bool al = (k % 8) == 0;
-            for (int kk = 0; kk < k; kk += 32) {
-                const int c0 = kk + g * 8;
-                const int valid = max(0, min(8, k - c0));
-                bf16x8 af[C::FM];
-#pragma unroll
-                for (int i = 0; i < C::FM; i++) {
-                    const int64_t m = m0 + wm * C::WM + i * 16 + rr;
-                    af[i] = load_bf16x8(a.X_S + m * k + c0, (m < M) ? valid : 0, al);
-                }
-#pragma unroll
-                for (int j = 0; j < C::FN; j++) {
-                    const int64_t n = n0 + wn * C::WN + j * 16 + rr;
-                    const bf16x8 bf = load_bf16x8(a.W_S + n * k + c0, (n < N) ? valid : 0, al);
-#pragma unroll
-                    for (int i = 0; i < C::FM; i++) acc[i][j] = mfma_bf16(af[i], bf, acc[i][j]);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-        for (int j = 0; j < C::FN; j++) {
-            const int64_t n = n0 + wn * C::WN + j * 16 + rr;
-            if (n >= N) continue;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int64_t m = m0 + wm * C::WM + i * 16 + g * 4 + q;
-                if (m < M) a.Y[m * a.ldy + n] = acc[i][j][q];
-            }
-        }
-}
-
-template <int BM, int BN, bool TAIL>
-__global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    prefill_tile<BM, BN, TAIL>(a, tm, tn, lds);
-}
-
-// ---------------------------------------------------------------------------
-// Grouped form (independent products sharing N, K and k, e.g. the experts of
-// a MoE layer): one launch covers the tiles of up to GROUP_MAX groups.  The
-// group descriptors travel by value in the kernel arguments, so the launch
-// needs no device-side table (and can be captured in a graph); workgroup w
-// belongs to the group whose tile range [tile_start[e], tile_start[e+1])
-// holds w.
-// ---------------------------------------------------------------------------
-constexpr int GROUP_MAX = 32;
-
-struct GroupDesc {
-    const uint8_t *Xq, *Xs;
-    const float *alpha_x;
-    const uint16_t *X_S;
-    const uint8_t *Wq, *Ws;
-    const float *alpha_w;
-    const uint16_t *W_S;
-    float *Y;
-    int64_t M;
-};
-
-struct GroupedArgs {
-    GroupDesc g[GROUP_MAX];
-    int tile_start[GROUP_MAX + 1];
-    int64_t N, K;
-    int k, tiles_n, G;
-};
-
-template <int BM, int BN, bool TAIL>
-__global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int w = blockIdx.x;
-    int e = 0;
-    while (e + 1 < ga.G && w >= ga.tile_start[e + 1]) e++;
-    const int local = w - ga.tile_start[e];
-    const GroupDesc &d = ga.g[e];
-    const GemmArgs a{d.Xq, d.Xs, d.alpha_x, d.X_S, d.Wq, d.Ws, d.alpha_w, d.W_S,
-                     d.M, ga.N, ga.K, ga.k, d.Y, ga.N};
-    prefill_tile<BM, BN, TAIL>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
-}
-
 // ===========================================================================
-// LDS-decode prefill path: each workgroup decodes every NVFP4 element of its
-// 256x256 tile exactly once per K step (64 channels) into a swizzled FP16 tile
-// in LDS (double buffered, 2 x 64 KB); eight waves (2 x 4, 128 x 64 each, two
-// per SIMD) read their MFMA fragments from it with ds_read_b128 and run
-// v_mfma_f32_32x32x16_f16.  While a wave multiplies stage kt it decodes its
-// share of stage kt+1 from registers (fetched one step earlier) into the other
-// buffer; the second wave on each SIMD keeps the matrix core busy while the
-// first decodes, waits for LDS or sits at a barrier.
-// Decode share per thread and step: 2 units of (row, 32-channel half) = 32
-// code bytes + 4 scale bytes -> 64 FP16 values.
+// LDS-decode prefill tile: each workgroup decodes every NVFP4 element of its
+// tile exactly once per K step (64 channels) into a swizzled FP16 tile in LDS
+// (double buffered).  The main form is 256 x 256 with eight waves (2 x 4,
+// 128 x 64 each, two per SIMD, 2 x 64 KB of LDS); grids too small for it use
+// 128 x 128 with four waves of 64 x 64 (two workgroups per CU).  Waves read
+// their MFMA fragments with ds_read_b128 and run v_mfma_f32_32x32x16_f16.
+// While a wave multiplies stage kt it decodes its share of stage kt+1 from
+// registers (fetched one step earlier) into the other buffer; the second wave
+// on each SIMD keeps the matrix core busy while the first decodes, waits for
+// LDS or sits at a barrier.
+// Decode share per thread and step (both forms): 2 units of (row, 32-channel
+// half) = 32 code bytes + 4 scale bytes -> 64 FP16 values.
 // ===========================================================================
 struct LdsCfg {
     static constexpr int BKL = 64;
@@ -327,56 +75,64 @@ __device__ __forceinline__ int f16_off(int r, int c)
 
 // Each thread decodes one 8-channel piece of each of its two units per
 // sub-step.
-struct LdsTile {
-    static constexpr int BM = 256, BN = 256, BKL = 64, WM = 128, WN = 64, FM = 4, FN = 2;
-    static constexpr int TILE = (BM + BN) * LdsCfg::ROWB;   // 64 KB per stage
+// Geometry of an LDS-decode tile: BM x BN outputs, WGM x WGN waves of
+// (BM/WGM) x (BN/WGN), K step BKL channels, BM + BN FP16 rows per stage.
+template <int BM_, int BN_, int WGM, int WGN>
+struct LdsGeo {
+    static constexpr int BM = BM_, BN = BN_, BKL = LdsCfg::BKL;
+    static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    static constexpr int NT = 64 * WGM * WGN;                  // threads
+    static constexpr int ROWS = BM + BN;
+    static constexpr int UNITS = ROWS * 2 / NT;                // decode units per thread
+    static constexpr int TILE = ROWS * LdsCfg::ROWB;           // bytes per stage
+    static_assert(UNITS * NT == ROWS * 2 && FM * 32 == WM && FN * 32 == WN, "tile geometry");
 };
-
-template <bool TAIL>
-__global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
+// One BM x BN output tile (tm, tn) with WGM x WGN waves (see LdsGeo).
+template <int BM, int BN, int WGM, int WGN, bool TAIL>
+__device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint8_t *lds)
 {
-    using C = LdsTile;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    using C = LdsGeo<BM, BN, WGM, WGN>;
+    constexpr int NT = C::NT, UNITS = C::UNITS;
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 5, rr = lane & 31;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int tiles_m = (int)((M + C::BM - 1) / C::BM), tiles_n = (int)((N + C::BN - 1) / C::BN);
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int64_t rowb = K / 2, rows = K / 16;
     const int nk = (int)(K / C::BKL);
 
-    // decode units of this thread: unit 0 = X row tid/2, unit 1 = W row tid/2,
-    // channel half tid%2.  Rows past the edge read row 0 (never stored).
-    const int half = tid & 1, r = tid >> 1;
-    int urow[2];
-    const uint8_t *ucode[2];
-    const uint8_t *uscale[2];
+    // decode units of this thread: unit i = LDS row (tid + NT*i)/2 (X rows
+    // first, then W rows), channel half tid%2.  Rows past the edge read row 0
+    // (never stored).
+    const int half = tid & 1;
+    int urow[UNITS];
+    const uint8_t *ucode[UNITS];
+    const uint8_t *uscale[UNITS];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const bool isx = i == 0;
+    for (int i = 0; i < UNITS; i++) {
+        const int row = (tid + NT * i) >> 1;
+        const bool isx = row < C::BM;
+        const int r = isx ? row : row - C::BM;
         const int64_t gr = (isx ? m0 : n0) + r;
         const int64_t rr0 = gr < (isx ? M : N) ? gr : 0;
-        urow[i] = (isx ? 0 : C::BM) + r;
+        urow[i] = row;
         ucode[i] = (isx ? a.Xq : a.Wq) + rr0 * rowb + half * 16;
         uscale[i] = (isx ? a.Xs : a.Ws) + rr0 * rows + half * 2;
     }
-    u32x4 pc[2];
-    unsigned ps[2];
+    u32x4 pc[UNITS];
+    unsigned ps[UNITS];
     auto gload = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < UNITS; i++) {
             pc[i] = *reinterpret_cast<const u32x4 *>(ucode[i] + (int64_t)kt * 32);
             ps[i] = *reinterpret_cast<const uint16_t *>(uscale[i] + (int64_t)kt * 4);
         }
     };
-    // piece d (8 channels) of both units into `tile`
+    // piece d (8 channels) of every unit into `tile`
     auto decode_piece = [&](uint8_t *tile, int d) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < UNITS; i++) {
             const f16x2 sc = e4m3_pair(d < 2 ? (ps[i] & 0xFFu) : ((ps[i] >> 8) & 0xFFu));
             *reinterpret_cast<f16x8 *>(tile + f16_off(urow[i], half * 4 + d)) = decode8(pc[i][d], sc);
         }
@@ -469,20 +225,21 @@ __global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
     };
     const bool staged = TAIL && k > 0 && k % 16 == 0;
     auto stage = [&](int kp, int kn) {
-        const int r0 = tid >> 3, cc = tid & 7;              // rows r0 + 64u, chunk cc
+        constexpr int RS = NT / 8, PU = C::ROWS * 8 / NT;   // rows r0 + RS*u, chunk cc
+        const int r0 = tid >> 3, cc = tid & 7;
         const uint16_t *xp = a.X_S + cc * 8, *wp = a.W_S + cc * 8;
         for (int ch = 0; ch * C::BKL < kn; ch++) {
             const int c = min(kp + ch * C::BKL + cc * 8, k - 8) - cc * 8;
-            u32x4 v[8];
+            u32x4 v[PU];
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                v[u] = *reinterpret_cast<const u32x4 *>(xp + min(m0 + r0 + 64 * u, M - 1) * k + c);
+            for (int u = 0; u < PU; u++) {
+                const int row = r0 + RS * u;
+                v[u] = row < C::BM ? *reinterpret_cast<const u32x4 *>(xp + min(m0 + row, M - 1) * k + c)
+                                   : *reinterpret_cast<const u32x4 *>(wp + min(n0 + row - C::BM, N - 1) * k + c);
+            }
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                v[4 + u] = *reinterpret_cast<const u32x4 *>(wp + min(n0 + r0 + 64 * u, N - 1) * k + c);
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-                *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + 64 * u, cc)) = v[u];
+            for (int u = 0; u < PU; u++)
+                *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + RS * u, cc)) = v[u];
         }
         lds_barrier();
     };
@@ -548,9 +305,73 @@ __global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
 }
 
 template <bool TAIL>
+__global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    lds_tile<256, 256, 2, 4, TAIL>(a, tm, tn, lds);
+}
+
+// 128 x 128 tiles, four waves of 64 x 64 (two workgroups per CU): for grids
+// too small for the 256 x 256 tile
+template <bool TAIL>
+__global__ __launch_bounds__(256) void prefill_lds128_kernel(GemmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tiles_m = (int)((a.M + 127) / 128), tiles_n = (int)((a.N + 127) / 128);
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    lds_tile<128, 128, 2, 2, TAIL>(a, tm, tn, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped form (independent products sharing N, K and k, e.g. the experts of
+// a MoE layer): one launch covers the tiles of up to GROUP_MAX groups.  The
+// group descriptors travel by value in the kernel arguments, so the launch
+// needs no device-side table (and can be captured in a graph); workgroup w
+// belongs to the group whose tile range [tile_start[e], tile_start[e+1])
+// holds w.
+// ---------------------------------------------------------------------------
+constexpr int GROUP_MAX = 32;
+
+struct GroupDesc {
+    const uint8_t *Xq, *Xs;
+    const float *alpha_x;
+    const uint16_t *X_S;
+    const uint8_t *Wq, *Ws;
+    const float *alpha_w;
+    const uint16_t *W_S;
+    float *Y;
+    int64_t M;
+};
+
+struct GroupedArgs {
+    GroupDesc g[GROUP_MAX];
+    int tile_start[GROUP_MAX + 1];
+    int64_t N, K;
+    int k, tiles_n, G;
+};
+
+template <int BM, int BN, bool TAIL>
+__global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int w = blockIdx.x;
+    int e = 0;
+    while (e + 1 < ga.G && w >= ga.tile_start[e + 1]) e++;
+    const int local = w - ga.tile_start[e];
+    const GroupDesc &d = ga.g[e];
+    const GemmArgs a{d.Xq, d.Xs, d.alpha_x, d.X_S, d.Wq, d.Ws, d.alpha_w, d.W_S,
+                     d.M, ga.N, ga.K, ga.k, d.Y, ga.N};
+    lds_tile<BM, BN, 2, 2, TAIL>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
+}
+
+template <bool TAIL>
 static hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
 {
-    using C = LdsTile;
+    using C = LdsGeo<256, 256, 2, 4>;
     const int64_t tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
     const size_t lds = 2 * C::TILE;
     static bool attr = false;       // raise the dynamic-LDS limit once per instantiation
@@ -560,46 +381,26 @@ static hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(512), lds, s, a);
+    hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, bool TAIL>
-static hipError_t launch_prefill(const GemmArgs &a, hipStream_t s)
+template <bool TAIL>
+static hipError_t launch_prefill_lds128(const GemmArgs &a, hipStream_t s)
 {
-    using C = Prefill<BM, BN>;
-    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    const size_t lds = 2 * C::STAGE;
-    static bool attr = false;       // raise the dynamic-LDS limit once per instantiation
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<BM, BN, TAIL>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL((prefill_kernel<BM, BN, TAIL>), dim3((unsigned)tiles), dim3(256), lds, s, a);
+    using C = LdsGeo<128, 128, 2, 2>;
+    const int64_t tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+    const size_t lds = 2 * C::TILE;
+    hipLaunchKernelGGL(prefill_lds128_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN>
-static hipError_t run_prefill(const GemmArgs &a, hipStream_t s)
-{
-    return a.k > 0 ? launch_prefill<BM, BN, true>(a, s) : launch_prefill<BM, BN, false>(a, s);
-}
 
 template <bool TAIL>
 static hipError_t launch_grouped_chunk(const GroupedArgs &ga, int tiles, hipStream_t s)
 {
     constexpr int BM = 128, BN = 128;
-    const size_t lds = 2 * Prefill<BM, BN>::STAGE;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&grouped_prefill_kernel<BM, BN, TAIL>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    const size_t lds = 2 * LdsGeo<BM, BN, 2, 2>::TILE;         // 64 KB: no attribute needed
     hipLaunchKernelGGL((grouped_prefill_kernel<BM, BN, TAIL>), dim3((unsigned)tiles), dim3(256), lds,
                        s, ga);
     return hipGetLastError();
@@ -1136,7 +937,7 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
         const int64_t t256x128 = ((a.M + 255) / 256) * ((a.N + 127) / 128);
         (void)t256x128;
         if (t256 >= 240) return a.k > 0 ? launch_prefill_lds<true>(a, s) : launch_prefill_lds<false>(a, s);
-        return run_prefill<128, 128>(a, s);
+        return a.k > 0 ? launch_prefill_lds128<true>(a, s) : launch_prefill_lds128<false>(a, s);
     }
     // weight-streaming decode path; configurations chosen from measured sweeps
     // on MI355X (Qwen3-8B projection shapes, M = 1, 8, 32, 64)
