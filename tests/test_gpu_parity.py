@@ -365,3 +365,26 @@ def test_sweep_sampled(M, case):
         assert np.array_equal(host(idx_d), o["idx"])
     assert scalar(ax) == np.float32(o["ax"]) and scalar(aw) == np.float32(o["aw"])
     assert_gemm_close(host(Y)[np.ix_(rows, cols)], o["Y"], f"sweep M={M} {case}")
+
+
+@pytest.mark.parametrize("k", [0, 64, 144, 200])
+def test_prefill_large_tile_ragged_sampled(k):
+    """Grids that take the 256x256 tile with ragged M and N, side widths that
+    need two staging passes (144) or the unstaged path (200, not a multiple
+    of 16); sampled rows and columns always include the ragged edges."""
+    M, N, K = 4037, 3931, 1024
+    g = np.random.default_rng(77 + k)
+    X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
+    W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
+    idx = np.sort(g.choice(K, size=k, replace=False)).astype(np.int32)
+    Xd, Wd, idxd = dev(X), dev(W), dev(idx)
+    axd, awd = S.compute_alpha(Xd, idxd), S.compute_alpha(Wd, idxd)
+    gx, gw = S.quantize_nvfp4(Xd, idxd, axd), S.quantize_nvfp4(Wd, idxd, awd)
+    Y = S.splice_gemm(gx[0], gx[1], axd, gx[2] if k else None, gw[0], gw[1], awd, gw[2] if k else None,
+                      path=S.PATH_PREFILL)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(M - 70, M), g.choice(M, 40, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(0, 4), np.arange(N - 70, N), g.choice(N, 40, replace=False)]))
+    o = oracle_pipeline(X, X, W, k, rows=rows, cols=cols, idx=idx)
+    assert scalar(axd) == np.float32(o["ax"]) and scalar(awd) == np.float32(o["aw"])
+    assert_gemm_close(host(Y)[np.ix_(rows, cols)], o["Y"], f"M={M} N={N} K={K} k={k}")
