@@ -374,13 +374,11 @@ static hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
     using C = LdsGeo<256, 256, 2, 4>;
     const int64_t tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
     const size_t lds = 2 * C::TILE;
-    static bool attr = false;       // raise the dynamic-LDS limit once per instantiation
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_lds_kernel<TAIL>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&prefill_lds_kernel<TAIL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
     return hipGetLastError();
 }
@@ -878,22 +876,16 @@ static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
     const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16;
     dim3 grid((unsigned)((a.N + 15) / 16));
     if (a.k > 0) {
-        static bool attr = false;
-        if (!attr) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
-            if (e != hipSuccess) return e;
-            attr = true;
-        }
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
+        if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, true>), grid, dim3(64 * NW), lds, s, a);
     } else {
-        static bool attr = false;
-        if (!attr) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
-            if (e != hipSuccess) return e;
-            attr = true;
-        }
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
+        if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, false>), grid, dim3(64 * NW), lds, s, a);
     }
     return hipGetLastError();
@@ -931,6 +923,7 @@ size_t gemm_ws_bytes(Path, int64_t, int64_t, int64_t)
 hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t s)
 {
     if (a.M == 0 || a.N == 0) return hipSuccess;
+    if (a.K == 0) p = Path::Prefill;    // the decode kernels assume at least one K chunk
     if (p == Path::Prefill) {
         // largest tile that still gives every CU a tile
         const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);

@@ -388,3 +388,19 @@ def test_prefill_large_tile_ragged_sampled(k):
     o = oracle_pipeline(X, X, W, k, rows=rows, cols=cols, idx=idx)
     assert scalar(axd) == np.float32(o["ax"]) and scalar(awd) == np.float32(o["aw"])
     assert_gemm_close(host(Y)[np.ix_(rows, cols)], o["Y"], f"M={M} N={N} K={K} k={k}")
+
+
+@pytest.mark.parametrize("M", [1, 64, 300])
+def test_gemm_empty_k_writes_zeros(M):
+    """K = 0 (no channels at all): every path writes Y = 0."""
+    N = 70
+    dev_ = torch.device("cuda")
+    e8 = torch.zeros(M, 0, dtype=torch.uint8, device=dev_)
+    w8 = torch.zeros(N, 0, dtype=torch.uint8, device=dev_)
+    one = torch.ones(1, device=dev_)
+    paths = [S.PATH_AUTO, S.PATH_PREFILL] + ([S.PATH_DECODE] if M <= S.DECODE_MAX_M else [])
+    for path in paths:
+        Y = torch.full((M, N), float("nan"), device=dev_)
+        S.nvfp4_gemm(e8, e8, one, w8, w8, one, path=path, out=Y)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, torch.zeros_like(Y)), f"path {path}"
