@@ -939,8 +939,9 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
     const int64_t colblocks = (a.N + 15) / 16;
     if (a.M <= 16) {
         if (a.M <= 4 && a.M * a.K * 2 <= XLDS_MAX && nchunk >= 2 && nchunk % 2 == 0) {   // 16-byte aligned scale pairs
-            if (nchunk <= 4 * 8) return run_decode_xlds<4, 8>(a, s);
-            if (nchunk <= 8 * 8) return run_decode_xlds<8, 8>(a, s);
+            if (nchunk <= 8 * 4) return run_decode_xlds<8, 4>(a, s);
+            if (nchunk <= 16 * 4) return run_decode_xlds<16, 4>(a, s);
+            if (nchunk <= 16 * 6) return run_decode_xlds<16, 6>(a, s);
             if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, s);
         }
         if (colblocks >= 512 && run_decode3_k<1, 3, 4, 8>(a, s, e)) return e;

@@ -90,7 +90,8 @@ def test_quantize_all_protected_and_strided_rows():
                                    (100, 256, 256),
                                    (20, 20480, 64),      # more than 16 channels per select thread
                                    (3, 65536, 100),      # largest K
-                                   (16, 16384, 4096)])   # large k
+                                   (16, 16384, 4096),    # large k
+                                   (0, 64, 8)])          # empty batch: zero moments, ties everywhere
 def test_stats_select_bit_exact(T, K, k):
     X = synth.activations(7, T % 7, T, K, 2, "student", n_out=min(64, K // 4))
     st_o = O.stats(X)
