@@ -405,3 +405,55 @@ def test_gemm_empty_k_writes_zeros(M):
         S.nvfp4_gemm(e8, e8, one, w8, w8, one, path=path, out=Y)
         torch.cuda.synchronize()
         assert torch.equal(Y, torch.zeros_like(Y)), f"path {path}"
+
+
+@pytest.mark.parametrize("M", [1, 8, 64, 200])
+def test_projection_in_hip_graph(M):
+    """Activation preparation + SpliceGEMM captured in a HIP graph: the calls
+    allocate nothing and record no memset, so every replay (with eager work in
+    between) reproduces the eager result bit for bit."""
+    K, N, k = 1024, 640, 32
+    g = np.random.default_rng(321 + M)
+    W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
+    Xw = synth.activations(5, 0, 256, K, 2, "student", n_out=16)
+    Wd, Xwd = dev(W), dev(Xw)
+    idx, ax, _ = S.select_channels(Xwd, k)
+    aw = S.compute_alpha(Wd, idx)
+    wq, ws, wS = S.quantize_nvfp4(Wd, idx, aw)
+    Xs_in = [dev(synth.activations(5, 0, M, K, 10 + i, "student", n_out=16)) for i in range(3)]
+    Xin = torch.empty_like(Xs_in[0])
+    xpack = (torch.empty(M, K // 2, dtype=torch.uint8, device="cuda"),
+             torch.empty(M, K // 16, dtype=torch.uint8, device="cuda"),
+             torch.empty(M, k, dtype=torch.int16, device="cuda"))
+    Y = torch.empty(M, N, device="cuda")
+
+    def projection():
+        S.quantize_nvfp4(Xin, idx, ax, out=xpack)
+        S.splice_gemm(xpack[0], xpack[1], ax, xpack[2], wq, ws, aw, wS, out=Y)
+
+    eager = []
+    for x in Xs_in:
+        Xin.copy_(x)
+        projection()
+        eager.append(Y.clone())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        projection()                       # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        projection()
+    for rep in range(2):
+        for i, x in enumerate(Xs_in):
+            Xin.copy_(x)                   # eager work between replays
+            Y.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y, eager[i]), f"replay {rep} input {i}"
+    # and the result is the oracle's
+    o = oracle_pipeline(Xw, host(Xs_in[0]).view(np.uint16), W, k)
+    assert np.array_equal(host(idx), o["idx"])
+    assert_gemm_close(host(eager[0]), o["Y"], f"M={M}")
