@@ -340,6 +340,41 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                      "timing": "HIP-graph replay of back-to-back calls over rotated weight copies; "
                                "includes each kernel's dispatch",
                      "shapes": dec}
+
+    # ---------------- decode projection with its activation preparation:
+    # quantize + GEMM (two launches) against the fused call (one launch)
+    fz = {}
+    for M in (1, S.FUSED_MAX_M):
+        t2 = tf = 0.0
+        for n in names:
+            p = P[n]
+            K, N = p["K"], p["N"]
+            Xh = synth.activations(synth.CFG_DECODE, synth.INPUT_STREAM[n], M, K, 3, "student")
+            X = torch.from_numpy(Xh.view(np.int16)).to(dev)
+            xq = S.quantize_nvfp4(X, p["idx"], p["ax"])
+            Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+            cp = packs[n]
+
+            def two(i):
+                w = cp[i % ncopy]
+                S.quantize_nvfp4(X, p["idx"], p["ax"], out=xq)
+                S.splice_gemm(xq[0], xq[1], p["ax"], xq[2], w[0], w[1], p["aw"], w[2], out=Y)
+
+            def fused(i):
+                w = cp[i % ncopy]
+                S.splice_gemm_decode_fused(X, p["idx"], p["ax"], w[0], w[1], p["aw"], w[2], out=Y)
+            a2 = graph_timed(torch, two, args.decode_iters)
+            af = graph_timed(torch, fused, args.decode_iters)
+            fz[f"{n}@M{M}"] = {"two_call_us": round(a2 * 1e3, 2), "fused_us": round(af * 1e3, 2)}
+            t2 += a2
+            tf += af
+        fz[f"M{M}"] = {"two_call_us": round(t2 * 1e3, 2), "fused_us": round(tf * 1e3, 2),
+                       "speedup": round(t2 / tf, 3)}
+        log(f"decode with preparation M={M}: {fz[f'M{M}']}")
+    out["decode_fused_prep"] = {
+        "timing": "HIP-graph replay over rotated weight copies; per projection, the activation "
+                  "preparation (quantize + gather) and the GEMM as two launches, or one fused launch",
+        "shapes": fz}
     del packs
 
     # ---------------- grouped MoE stand-in

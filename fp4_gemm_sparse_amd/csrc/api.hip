@@ -166,6 +166,31 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const
     return run_gemm(a, ws, ws_bytes, path, hs(stream));
 }
 
+int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
+                             const float *alpha_x, const uint8_t *Wq, const uint8_t *Ws,
+                             const float *alpha_w, const uint16_t *W_S, int64_t M, int64_t N,
+                             int64_t K, int32_t k, float *Y, int64_t ldy, splice_stream_t stream)
+{
+    if (M < 0 || N < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(K, k);
+    if (rc) return rc;
+    if (M > SPLICE_FUSED_MAX_M) return SPLICE_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return SPLICE_OK;
+    if (!Y || !alpha_x || !alpha_w || ldy < N) return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(Y, 4) || !aligned(alpha_x, 4) || !aligned(alpha_w, 4)) return SPLICE_ERR_INVALID_ARG;
+    if (K > 0) {
+        if (!X || !Wq || !Ws || ldx < K || (k > 0 && (!idx || !W_S))) return SPLICE_ERR_INVALID_ARG;
+        if (!fused_decode_ok(M, K)) return SPLICE_ERR_UNSUPPORTED;
+        if (!aligned(X, 16) || ldx % 8 != 0) return SPLICE_ERR_UNSUPPORTED;
+        if (!aligned(Wq, 16) || !aligned(Ws, 8) || (k > 0 && !aligned(idx, 4)))
+            return SPLICE_ERR_INVALID_ARG;
+        if (k > 0 && !aligned(W_S, (k % 8 == 0) ? 16 : 2)) return SPLICE_ERR_INVALID_ARG;
+    }
+    GemmArgs a{nullptr, nullptr, alpha_x, nullptr, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy,
+               X, ldx, idx};
+    return hip_status(launch_gemm_fused(a, hs(stream)));
+}
+
 size_t splice_grouped_workspace_size(const splice_group *, int32_t, int64_t, int64_t, int32_t)
 {
     return 0;

@@ -34,6 +34,11 @@ struct GemmArgs {
     int32_t k;
     float *Y;
     int64_t ldy;
+    // activation-prep fused decode only: bf16 X [M, K] with row stride ldx and
+    // the protected channels idx[0..k); Xq, Xs and X_S are then unused
+    const uint16_t *X;
+    int64_t ldx;
+    const int32_t *idx;
 };
 enum class Path { Decode, Prefill };
 size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K);
@@ -41,5 +46,9 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t ws_bytes, hip
 // independent products sharing N, K and k (groups[i].N/K/k equal), one launch
 // per 32 groups; groups with M == 0 are skipped
 hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s);
+// decode GEMM that quantizes X itself (GemmArgs.X/ldx/idx, alpha_x); shapes
+// for which fused_decode_ok holds
+bool fused_decode_ok(int64_t M, int64_t K);
+hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t s);
 
 }  // namespace splice

@@ -25,6 +25,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "splice.h")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DECODE_MAX_M = 64
+FUSED_MAX_M = 4
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -57,6 +58,8 @@ _SIGS = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
                                   _sz, ctypes.c_int, _vp]),
     "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "splice_gemm_decode_fused": (ctypes.c_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                                _i64, _i32, _vp, _i64, _vp]),
     "splice_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32, _vp, _sz,
                                            _vp]),
     "splice_grouped_workspace_size": (_sz, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32]),
@@ -217,6 +220,22 @@ def nvfp4_gemm(Xq, Xs, alpha_x, Wq, Ws, alpha_w, path=PATH_AUTO, out=None, ws=No
     _check("nvfp4_gemm",
            lib().nvfp4_gemm(_p(Xq), _p(Xs), _p(alpha_x), _p(Wq), _p(Ws), _p(alpha_w), M, N, K, _p(Y),
                             Y.stride(0), _p(ws), 0 if ws is None else ws.numel(), path, _stream()))
+    return Y
+
+
+def splice_gemm_decode_fused(X, idx, alpha_x, Wq, Ws, alpha_w, W_S, out=None):
+    """Decode SpliceGEMM that quantizes the bf16 activations X [M, K] itself
+    (M <= FUSED_MAX_M); idx int32 [k] or None.  Same Y as quantize_nvfp4 then
+    splice_gemm."""
+    _bf16(X)
+    M, K = X.shape
+    N = Wq.shape[0]
+    k = 0 if idx is None else idx.numel()
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=X.device)
+    _check("splice_gemm_decode_fused",
+           lib().splice_gemm_decode_fused(_p(X), X.stride(0), _p(idx) if k else None, _p(alpha_x),
+                                          _p(Wq), _p(Ws), _p(alpha_w), _p(W_S) if k else None,
+                                          M, N, K, k, _p(Y), Y.stride(0), _stream()))
     return Y
 
 

@@ -151,6 +151,31 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x,
                int64_t M, int64_t N, int64_t K, float *Y, int64_t ldy,
                void *ws, size_t ws_bytes, int path, splice_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * SpliceGEMM for decode with the activation preparation done inside the GEMM
+ * (Sec. 5.1 data preparation and dual-path execution; the preparation is
+ * part of the projection's cost in Sec. 6.3): the kernel reads the bf16
+ * activations, masks the protected channels, quantizes the residual to NVFP4
+ * with alpha_x and gathers X_S itself, then computes the splice_gemm product.
+ * Y is bit-identical to splice_quantize_nvfp4(X, idx, alpha_x) followed by
+ * splice_gemm on the decode path, one launch instead of two, and no
+ * Xq/Xs/X_S buffers.
+ *   X       bf16 [M, K] in (DEVICE), row stride ldx (multiple of 8, 16-byte
+ *           aligned rows)
+ *   idx     int32 [k] in (DEVICE): the protected channels, distinct, in
+ *           [0, K) (as splice_select_channels writes them); NULL when k == 0
+ *   alpha_x float [1] in (DEVICE), > 0 and finite: the frozen activation scale
+ *   Wq, Ws, alpha_w, W_S, Y, ldy: as for splice_gemm.
+ * Shapes: M <= SPLICE_FUSED_MAX_M; K a multiple of 256 with 256 <= K <= 16384
+ * (the FP16 copy of X, up to 128 KB, stays in LDS), or K == 0 (Y = 0).
+ * Other shapes return SPLICE_ERR_UNSUPPORTED: use the two-call form.
+ * No workspace; nothing is allocated; safe inside stream capture. */
+#define SPLICE_FUSED_MAX_M 4
+int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
+                             const float *alpha_x, const uint8_t *Wq, const uint8_t *Ws,
+                             const float *alpha_w, const uint16_t *W_S, int64_t M, int64_t N,
+                             int64_t K, int32_t k, float *Y, int64_t ldy, splice_stream_t stream);
+
 /* Workspace bytes splice_gemm / nvfp4_gemm need for this shape (k is
  * ignored by the current kernels but part of the contract). */
 size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
@@ -160,9 +185,9 @@ size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
  * an MoE layer, each with its own S, alphas and token count M; the paper's
  * Nemotron3 Up/Down projections, Sec. 6.3).  groups is a HOST array; each
  * entry's pointers are device pointers laid out as for splice_gemm, with
- * ldy = N.  Groups with M == 0 are skipped.  Each group takes the path the
- * automatic dispatch would give it.
- * ws: splice_grouped_workspace_size(groups, G, N, K, k) bytes. */
+ * ldy = N.  Groups with M == 0 are skipped.  All groups run on the 128x128
+ * matrix-core tile of the prefill path, one launch per 32 groups.
+ * ws: splice_grouped_workspace_size(groups, G, N, K, k) bytes (currently 0). */
 typedef struct {
     const uint8_t *Xq, *Xs;
     const float *alpha_x;

@@ -124,3 +124,42 @@ def test_grouped_argument_errors(L):
     empty = (G * 1)()
     empty[0] = G(None, None, None, None, None, None, None, None, 0, None)    # M = 0 group
     assert L.splice_gemm_grouped(empty, 1, 64, 256, 8, None, 0, None) == splice.OK
+
+
+def fused(L, M=1, N=64, K=1024, k=8, **over):
+    args = dict(X=FAKE, ldx=K, idx=FAKE, ax=FAKE, Wq=FAKE, Ws=FAKE, aw=FAKE, WS=FAKE, Y=FAKE,
+                ldy=N)
+    args.update(over)
+    return L.splice_gemm_decode_fused(args["X"], args["ldx"], args["idx"], args["ax"], args["Wq"],
+                                      args["Ws"], args["aw"], args["WS"], M, N, K, k, args["Y"],
+                                      args["ldy"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), splice.ERR_INVALID_ARG),
+    (dict(K=100), splice.ERR_INVALID_ARG),                 # K % 16
+    (dict(k=2000), splice.ERR_INVALID_ARG),                # k > K
+    (dict(M=splice.FUSED_MAX_M + 1), splice.ERR_UNSUPPORTED),
+    (dict(K=384), splice.ERR_UNSUPPORTED),                 # odd number of 128-channel chunks
+    (dict(K=128), splice.ERR_UNSUPPORTED),
+    (dict(K=32768, k=8), splice.ERR_UNSUPPORTED),          # beyond 16 waves x 8 chunks
+    (dict(ldx=1028, K=1024), splice.ERR_UNSUPPORTED),      # ldx % 8
+    (dict(X=FAKE + 2), splice.ERR_UNSUPPORTED),            # X rows not 16-byte aligned
+    (dict(ldx=512), splice.ERR_INVALID_ARG),               # ldx < K
+    (dict(X=None), splice.ERR_INVALID_ARG),
+    (dict(idx=None), splice.ERR_INVALID_ARG),
+    (dict(WS=None), splice.ERR_INVALID_ARG),
+    (dict(ax=None), splice.ERR_INVALID_ARG),
+    (dict(Y=None), splice.ERR_INVALID_ARG),
+    (dict(ldy=10), splice.ERR_INVALID_ARG),
+    (dict(Wq=FAKE + 4), splice.ERR_INVALID_ARG),           # misaligned codes
+    (dict(idx=FAKE + 2), splice.ERR_INVALID_ARG),
+])
+def test_fused_decode_argument_errors(L, kw, code):
+    assert fused(L, **kw) == code
+
+
+def test_fused_decode_empty_is_ok(L):
+    assert fused(L, M=0) == splice.OK
+    assert fused(L, N=0) == splice.OK
+    assert fused(L, M=0, K=384) == splice.OK               # nothing to compute: no shape rule applies
