@@ -344,7 +344,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     # ---------------- decode projection with its activation preparation:
     # quantize + GEMM (two launches) against the fused call (one launch)
     fz = {}
-    for M in (1, S.FUSED_MAX_M):
+    for M in (1, 2, S.FUSED_MAX_M):
         t2 = tf = 0.0
         for n in names:
             p = P[n]

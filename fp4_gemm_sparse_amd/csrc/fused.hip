@@ -1,0 +1,298 @@
+// fused.hip -- decode SpliceGEMM with the activation preparation in its
+// prologue (FourSight, arXiv 2611.04887v1: Sec. 5.1 data preparation and
+// dual-path execution; the preparation belongs to the projection's cost as in
+// Sec. 6.3, Fig. 10).
+//
+// For M <= 4 token rows.  A workgroup owns 16*CB output channels and the
+// whole K; wave w multiplies K chunks (128 channels) w*CPW .. w*CPW+CPW-1.
+//  1. Every independent global load is issued first, the thread's half
+//     blocks of X and its idx entry ahead of the wave's weight codes and
+//     scales: loads complete in issue order, so the preparation can start
+//     while the weights are still on their way.
+//  2. The protected-channel mask is built in LDS from idx.
+//  3. Each 16-channel block of the M rows is masked, quantized by two lanes
+//     (eight elements each) with the scale, key and code functions of
+//     nvfp4.hpp that the quantize kernel uses, and decoded into an FP16 copy
+//     of X in LDS -- the bits the two-call form would decode from its packed
+//     codes.
+//  4. Each wave multiplies its chunks on v_mfma_f32_16x16x32_f16 (A from the
+//     LDS copy, B decoded from registers); partial sums meet in LDS in wave
+//     order, are scaled by alpha_x*alpha_w and completed with the BF16 side
+//     product of X_S (gathered from X through idx) and W_S.
+// With the same wave configuration as the two-call decode kernel for few
+// rows, the chunk split, the MFMA order and the reduction order are the same,
+// and Y is bit-identical to it.  Every workgroup repeats the preparation of the
+// few rows: that replaces a launch and the HBM round trip of Xq/Xs/X_S.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "nvfp4.hpp"
+
+namespace splice {
+
+namespace {
+
+constexpr int FBK = 128;                 // channels per K chunk
+constexpr int F_CODE_ROW = FBK / 2;      // code bytes per row per chunk
+constexpr int F_SCALE_ROW = FBK / 16;    // scale bytes per row per chunk
+constexpr int F_XMAX = 128 * 1024;       // bytes of FP16 activations kept in LDS
+constexpr int F_LDS = 160 * 1024;        // LDS of one CU
+
+// eight protected activations row[idx[i]], i < valid (zero beyond), as bf16x8
+__device__ __forceinline__ bf16x8 gather_side8(const uint16_t *row, const int32_t *ip, int valid,
+                                               int64_t K)
+{
+    unsigned v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const int64_t c = e < valid ? ip[e] : -1;
+        v[e] = (c >= 0 && c < K) ? row[c] : 0u;
+    }
+    const u32x4 w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+}  // namespace
+
+template <int NW, int CPW, int CB, int XPT, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
+{
+    // [M][K] FP16 activations, then [NW][CB][64] f32x4 partial sums (the
+    // protected-channel mask, and idx when k <= 64, use that space until the
+    // main loop).  XPT: half blocks of X per thread loaded up front.
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+    constexpr int NT = 64 * NW;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int g = lane >> 4, rr = lane & 15;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t rowb = K / 2, rows = K / 16, nb = K / 16;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * CB);
+    const int nchunk = (int)(K / FBK);
+    const int k = a.k;
+    const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
+
+    // 1. independent global loads: X and idx first, then the weights
+    // half blocks of X: item i = (row, block, half) with i = 2 * (m * nb + b) + h
+    const int64_t items = 2 * M * nb;
+    auto half_ptr = [&](int64_t it) {
+        const int64_t q = it >> 1, m = q / nb;
+        return a.X + m * a.ldx + (q - m * nb) * 16 + (it & 1) * 8;
+    };
+    u32x4 xv[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; j++) {
+        const int64_t it = tid + (int64_t)j * NT;
+        xv[j] = *reinterpret_cast<const u32x4 *>(half_ptr(it < items ? it : 0));
+    }
+    const int32_t my_idx = (TAIL && tid < k) ? a.idx[tid] : -1;
+    // W_S rows for k = 32 or 64 (wave j < CB finishes column block j):
+    // needed last, issued before the weights for the same reason
+    bf16x8 ta[2], tb[2];
+    const bool side_pre = TAIL && (k == 32 || k == 64);
+    if (side_pre && wave < CB) {
+        const int64_t n = n0 + wave * 16 + rr;
+        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int hh = (h * 32 < k) ? h : 0;
+            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);     // keep these loads ahead of the weight loads
+    const int c0 = wave * CPW;
+    u32x4 wc[CPW][CB];
+    unsigned ws[CPW][CB];
+#pragma unroll
+    for (int j = 0; j < CB; j++) {
+        const int64_t n = n0 + j * 16 + rr;
+        const int64_t nn = n < N ? n : 0;                      // edge rows: never stored
+        const uint8_t *pw = a.Wq + nn * rowb + g * 16;
+        const uint8_t *ps = a.Ws + nn * rows + 2 * g;
+#pragma unroll
+        for (int c = 0; c < CPW; c++) {
+            const int64_t ci = min(c0 + c, nchunk - 1);        // clamped; skipped at use
+            wc[c][j] = *reinterpret_cast<const u32x4 *>(pw + ci * F_CODE_ROW);
+            ws[c][j] = *reinterpret_cast<const uint16_t *>(ps + ci * F_SCALE_ROW);
+        }
+    }
+    // 2. protected-channel mask (and, for k <= 64, idx kept in LDS for the
+    // side gather, so that gather need not wait for an idx load issued
+    // behind the weights)
+    uint32_t *smask = reinterpret_cast<uint32_t *>(xl + red_off);
+    int32_t *sidx = reinterpret_cast<int32_t *>(xl + red_off + K / 8);     // after the K/32 mask words
+    if (TAIL) {
+        const int words = (int)((K + 31) / 32);
+        for (int i = tid; i < words; i += NT) smask[i] = 0;
+        if (side_pre && tid < k) sidx[tid] = my_idx;
+        __syncthreads();
+        if (my_idx >= 0 && my_idx < K) atomicOr(&smask[my_idx >> 5], 1u << (my_idx & 31));
+        for (int i = tid + NT; i < k; i += NT) {
+            const int c = a.idx[i];
+            if (c >= 0 && c < K) atomicOr(&smask[c >> 5], 1u << (c & 31));
+        }
+        __syncthreads();
+    }
+
+    // 3. quantize and decode the M rows into LDS, two lanes per block (items
+    // and NT are even, so both lanes of a block are in the same iteration)
+    {
+        const TensorScale ts = tensor_scale(*a.alpha_x);
+        auto prep = [&](const u32x4 v, int64_t it) {
+            unsigned w[4] = {v.x, v.y, v.z, v.w};
+            const int64_t q = it >> 1, b = q % nb;
+            if (TAIL) {
+                const unsigned mk = (block_mask16(smask, b) >> ((it & 1) * 8)) & 0xFFu;
+                if (mk) clear_protected_half(w, mk);
+            }
+            unsigned c;
+            const f16x2 sc = e4m3_pair(quantize_half_block(w, ts, c));
+            *reinterpret_cast<f16x8 *>(xl + (q * 16 + (it & 1) * 8) * 2) = decode8(c, sc);
+        };
+#pragma unroll
+        for (int j = 0; j < XPT; j++) {
+            const int64_t it = tid + (int64_t)j * NT;
+            if (it < items) prep(xv[j], it);
+        }
+        for (int64_t it = tid + (int64_t)XPT * NT; it < items; it += NT)
+            prep(*reinterpret_cast<const u32x4 *>(half_ptr(it)), it);
+    }
+    // X_S of the waves that finish a column block (k = 32 or 64), gathered
+    // from X; only needed after the main loop
+    if (side_pre && wave < CB) {
+        const int64_t mrow = rr;
+        const uint16_t *xr = a.X + (mrow < M ? mrow : 0) * a.ldx;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int hh = (h * 32 < k) ? h : 0;
+            ta[h] = gather_side8(xr, sidx + hh * 32 + g * 8, 8, K);
+        }
+    }
+    __syncthreads();
+
+    // 4. the wave's chunks
+    f32x4 acc[CB];
+#pragma unroll
+    for (int j = 0; j < CB; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool xrow = rr < M;
+    const uint8_t *xbase = xl + (int64_t)(xrow ? rr : 0) * K * 2 + g * 64;   // lane's 32 channels of a chunk
+#pragma unroll
+    for (int c = 0; c < CPW; c++) {
+        const int ci = c0 + c;
+        if (ci < nchunk) {
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                f16x8 af = *reinterpret_cast<const f16x8 *>(xbase + (int64_t)ci * FBK * 2 + s * 16);
+                if (!xrow) af = f16x8{};
+#pragma unroll
+                for (int j = 0; j < CB; j++) {
+                    const f16x8 bf = decode8(wc[c][j][s], e4m3_pair((ws[c][j] >> ((s >> 1) * 8)) & 0xFFu));
+                    acc[j] = mfma_f16(af, bf, acc[j]);
+                }
+            }
+        }
+    }
+
+    // 5. wave-order reduction, scale, side product, store
+    f32x4 *red = reinterpret_cast<f32x4 *>(xl + red_off);
+#pragma unroll
+    for (int j = 0; j < CB; j++) red[(wave * CB + j) * WAVE + lane] = acc[j];
+    __syncthreads();
+    if (wave < CB) {
+        const int j = wave;
+        f32x4 v = red[j * WAVE + lane];
+#pragma unroll
+        for (int w = 1; w < NW; w++) v += red[(w * CB + j) * WAVE + lane];
+        v *= (*a.alpha_x) * (*a.alpha_w);
+        const int64_t n = n0 + j * 16 + rr;
+        if (TAIL) {
+            if (side_pre) {
+                const bf16x8 z = {};
+                const bool okm = rr < M, okn = n < N;
+                v = mfma_bf16(okm ? ta[0] : z, okn ? tb[0] : z, v);
+                if (k == 64) v = mfma_bf16(okm ? ta[1] : z, okn ? tb[1] : z, v);
+            } else {
+                const bool al = (k % 8) == 0;
+                const int64_t mrow = rr;
+                const uint16_t *xr = a.X + (mrow < M ? mrow : 0) * a.ldx;
+                for (int kk = 0; kk < k; kk += 32) {
+                    const int cc = kk + g * 8;
+                    const int valid = max(0, min(8, k - cc));
+                    const bf16x8 af = gather_side8(xr, a.idx + cc, (mrow < M) ? valid : 0, K);
+                    const bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                    v = mfma_bf16(af, bf, v);
+                }
+            }
+        }
+        if (n < N)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int64_t m = g * 4 + q;
+                if (m < M) a.Y[m * a.ldy + n] = v[q];
+            }
+    }
+}
+
+template <int NW, int CPW, int CB, int XPT>
+static hipError_t run_fused_x(const GemmArgs &a, hipStream_t s)
+{
+    constexpr int red_bytes = NW * CB * WAVE * 16;
+    constexpr int lds_max = 4 * (NW * CPW * FBK) * 2 + red_bytes;    // largest M and K of the form
+    static_assert(lds_max <= F_LDS, "fused decode LDS budget");
+    const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + red_bytes;
+    const dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
+    if (a.k > 0) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&decode_fused_kernel<NW, CPW, CB, XPT, true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((decode_fused_kernel<NW, CPW, CB, XPT, true>), grid, dim3(64 * NW), lds, s, a);
+    } else {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&decode_fused_kernel<NW, CPW, CB, XPT, false>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((decode_fused_kernel<NW, CPW, CB, XPT, false>), grid, dim3(64 * NW), lds, s, a);
+    }
+    return hipGetLastError();
+}
+
+// half blocks of X per thread loaded ahead of the weights: all of them when
+// they are at most four, else the first four
+template <int NW, int CPW, int CB>
+static hipError_t run_fused(const GemmArgs &a, hipStream_t s)
+{
+    const int64_t items = a.M * a.K / 8;
+    if (items <= 64 * NW) return run_fused_x<NW, CPW, CB, 1>(a, s);
+    if (items <= 2 * 64 * NW) return run_fused_x<NW, CPW, CB, 2>(a, s);
+    return run_fused_x<NW, CPW, CB, 4>(a, s);
+}
+
+// The FP16 copy of the M rows must fit the LDS budget and K must be whole
+// 128-channel chunks, at most 16 waves x 8 chunks.
+bool fused_decode_ok(int64_t M, int64_t K)
+{
+    return M >= 1 && M <= 4 && K >= FBK && K % FBK == 0 && K <= 16 * 8 * FBK && M * K * 2 <= F_XMAX;
+}
+
+// Wave configurations from sweeps on MI355X (Qwen3-8B shapes, graph replay).
+// K <= 4096: one row takes the two-call kernel's eight waves of four chunks
+// (the two forms then agree bit for bit); more rows take sixteen waves of two
+// chunks, which spreads their larger preparation over twice the lanes, and
+// 48 columns per workgroup for wide N, so that fewer workgroups repeat it.
+// Larger K: the two-call kernel's configurations.
+hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t s)
+{
+    if (a.M == 0 || a.N == 0) return hipSuccess;
+    if (a.K == 0) return launch_gemm(Path::Prefill, a, nullptr, 0, s);   // Y = 0 (k <= K)
+    const int nchunk = (int)(a.K / FBK);
+    const int64_t colblocks = (a.N + 15) / 16;
+    if (nchunk <= 8 * 4) {
+        if (a.M == 1) return run_fused<8, 4, 1>(a, s);
+        return colblocks >= 512 ? run_fused<16, 2, 3>(a, s) : run_fused<16, 2, 1>(a, s);
+    }
+    if (nchunk <= 16 * 4) return run_fused<16, 4, 1>(a, s);
+    if (nchunk <= 16 * 6) return run_fused<16, 6, 1>(a, s);
+    return run_fused<16, 8, 1>(a, s);
+}
+
+}  // namespace splice

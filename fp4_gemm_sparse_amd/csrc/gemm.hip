@@ -16,7 +16,6 @@
 // only permutes the terms of each dot product; K steps are summed in order.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "nvfp4.hpp"
 
 namespace splice {
 
@@ -745,34 +744,10 @@ __global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
 // decodes the M real activation rows once into an FP16 LDS copy, and every
 // wave reads its A fragments from there instead of decoding 16 rows (most of
 // them padding) per chunk.  Weight handling is the single-round scheme above.
-//
-// FUSED: the workgroup also prepares the activations itself (FourSight,
-// Sec. 5.1 data preparation, moved into the GEMM prologue): it reads the bf16
-// rows of X, masks the protected channels, quantizes each 16-channel block
-// with the quantize kernel's own functions and decodes the result into the
-// same FP16 LDS copy; the side operand is gathered from X through idx.  The
-// numbers entering the matrix cores, and so Y, are bit-identical to
-// quantize-then-GEMM.  Every workgroup repeats the preparation of the few
-// rows, which replaces a launch and an HBM round trip of the codes.
 // ---------------------------------------------------------------------------
 constexpr int XLDS_MAX = 64 * 1024;        // bytes of FP16 activations kept in LDS
-constexpr int XFUSED_MAX = 128 * 1024;     // the same for the fused form (LDS is 160 KB per CU)
 
-// eight protected activations row[idx[i]], i < valid (zero beyond), as bf16x8
-__device__ __forceinline__ bf16x8 gather_side8(const uint16_t *row, const int32_t *ip, int valid,
-                                               int64_t K)
-{
-    unsigned v[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const int64_t c = e < valid ? ip[e] : -1;
-        v[e] = (c >= 0 && c < K) ? row[c] : 0u;
-    }
-    const u32x4 w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-template <int NW, int CPW, bool TAIL, bool FUSED>
+template <int NW, int CPW, bool TAIL>
 __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [M][K] f16, then reduction space
@@ -783,6 +758,32 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     const int64_t rowb = K / 2, rows = K / 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int nchunk = (int)(K / BK);
+
+    // the thread's first activation block (codes and scale) is loaded ahead
+    // of the weights: loads complete in issue order, so the decode into LDS
+    // below need not wait for the weight stream
+    const int64_t nbx = K / 16;
+    const int64_t it0 = tid < M * nbx ? tid : 0;
+    const u32x2 xc0 = *reinterpret_cast<const u32x2 *>(a.Xq + (it0 / nbx) * rowb + (it0 % nbx) * 8);
+    const unsigned xs0 = a.Xs[(it0 / nbx) * rows + it0 % nbx];
+    // side operands for k = 32 or 64 (wave 0 finishes the block): needed
+    // last, issued before the weights so that no wait for them is a wait
+    // for the weight stream
+    bf16x8 ta[2], tb[2];
+    const int k = a.k;
+    const bool side_pre = TAIL && (k == 32 || k == 64);
+    if (side_pre && wave == 0) {
+        const int64_t mrow = rr, n = n0 + rr;
+        const uint16_t *xa = a.X_S + (mrow < M ? mrow : 0) * k + g * 8;
+        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int hh = (h * 32 < k) ? h : 0;
+            ta[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + hh * 32));
+            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);     // keep these loads ahead of the weight loads
 
     // weights of this wave: chunks [c0, c0 + CPW) of each of its 16 rows,
     // so the waves of the workgroup sweep every row contiguously.  Scales come
@@ -806,54 +807,13 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
             wsv[c] = *reinterpret_cast<const u32x4 *>(ps + ci * SCALE_ROW);
         }
     }
-    bf16x8 ta[2], tb[2];
-    const int k = a.k;
-    const bool side_pre = TAIL && (k == 32 || k == 64);
-    if (side_pre && wave == 0) {
-        const int64_t mrow = rr, n = n0 + rr;
-        const uint16_t *xa = a.X_S + (mrow < M ? mrow : 0) * k + g * 8;
-        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int hh = (h * 32 < k) ? h : 0;
-            if (FUSED)
-                ta[h] = gather_side8(a.X + (mrow < M ? mrow : 0) * a.ldx, a.idx + hh * 32 + g * 8, 8, K);
-            else
-                ta[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + hh * 32));
-            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
-        }
-    }
-
-    const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
-    if (FUSED) {
-        // quantize the M activation rows (one 16-channel block per item) and
-        // decode them into LDS; the channel mask lives in the reduction space
-        // until the main loop
-        uint32_t *smask = reinterpret_cast<uint32_t *>(xl + red_off);
-        if (TAIL) build_mask(smask, K, a.idx, k);
-        const double alpha = (double)*a.alpha_x;
-        const double six_alpha = 6.0 * alpha;
+    // decode the M activation rows into LDS: one 16-channel block per item
+    {
         const int64_t nb = K / 16;
         for (int64_t it = tid; it < M * nb; it += 64 * NW) {
             const int64_t m = it / nb, b = it - m * nb;
-            Block16 x = load_block(a.X + m * a.ldx + b * 16);
-            if (TAIL) {
-                const unsigned mk = block_mask16(smask, b);
-                if (mk) clear_protected(x, mk);
-            }
-            u32x2 c;
-            const f16x2 sc = e4m3_pair(quantize_block(x, alpha, six_alpha, c));
-            f16x8 *dst = reinterpret_cast<f16x8 *>(xl + (m * K + b * 16) * 2);
-            dst[0] = decode8(c.x, sc);
-            dst[1] = decode8(c.y, sc);
-        }
-    } else {
-        // decode the M activation rows into LDS: one 16-channel block per item
-        const int64_t nb = K / 16;
-        for (int64_t it = tid; it < M * nb; it += 64 * NW) {
-            const int64_t m = it / nb, b = it - m * nb;
-            const u32x2 c = *reinterpret_cast<const u32x2 *>(a.Xq + m * rowb + b * 8);
-            const f16x2 sc = e4m3_pair(a.Xs[m * rows + b]);
+            const u32x2 c = (it == tid) ? xc0 : *reinterpret_cast<const u32x2 *>(a.Xq + m * rowb + b * 8);
+            const f16x2 sc = e4m3_pair((it == tid) ? xs0 : a.Xs[m * rows + b]);
             f16x8 *dst = reinterpret_cast<f16x8 *>(xl + (m * K + b * 16) * 2);
             dst[0] = decode8(c.x, sc);
             dst[1] = decode8(c.y, sc);
@@ -885,7 +845,7 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     }
 
     // wave-order reduction through LDS (reuses the space after the activations)
-    f32x4 *red = reinterpret_cast<f32x4 *>(xl + red_off);
+    f32x4 *red = reinterpret_cast<f32x4 *>(xl + ((M * K * 2 + 15) & ~(int64_t)15));
     red[wave * WAVE + lane] = acc;
     __syncthreads();
     if (wave == 0) {
@@ -906,9 +866,7 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
                 for (int kk = 0; kk < k; kk += 32) {
                     const int cc = kk + g * 8;
                     const int valid = max(0, min(8, k - cc));
-                    bf16x8 af = FUSED ? gather_side8(a.X + (mrow < M ? mrow : 0) * a.ldx, a.idx + cc,
-                                                     (mrow < M) ? valid : 0, K)
-                                      : load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
+                    bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
                     bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
                     v = mfma_bf16(af, bf, v);
                 }
@@ -923,24 +881,23 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     }
 }
 
-template <int NW, int CPW, bool FUSED>
+template <int NW, int CPW>
 static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
 {
-    constexpr int lds_max = (FUSED ? XFUSED_MAX : XLDS_MAX) + 16 * WAVE * 16;
     const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16;
     dim3 grid((unsigned)((a.N + 15) / 16));
     if (a.k > 0) {
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true, FUSED>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, true, FUSED>), grid, dim3(64 * NW), lds, s, a);
+        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, true>), grid, dim3(64 * NW), lds, s, a);
     } else {
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false, FUSED>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, false, FUSED>), grid, dim3(64 * NW), lds, s, a);
+        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, false>), grid, dim3(64 * NW), lds, s, a);
     }
     return hipGetLastError();
 }
@@ -993,10 +950,10 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
     const int64_t colblocks = (a.N + 15) / 16;
     if (a.M <= 16) {
         if (a.M <= 4 && a.M * a.K * 2 <= XLDS_MAX && nchunk >= 2 && nchunk % 2 == 0) {   // 16-byte aligned scale pairs
-            if (nchunk <= 8 * 4) return run_decode_xlds<8, 4, false>(a, s);
-            if (nchunk <= 16 * 4) return run_decode_xlds<16, 4, false>(a, s);
-            if (nchunk <= 16 * 6) return run_decode_xlds<16, 6, false>(a, s);
-            if (nchunk <= 16 * 8) return run_decode_xlds<16, 8, false>(a, s);
+            if (nchunk <= 8 * 4) return run_decode_xlds<8, 4>(a, s);
+            if (nchunk <= 16 * 4) return run_decode_xlds<16, 4>(a, s);
+            if (nchunk <= 16 * 6) return run_decode_xlds<16, 6>(a, s);
+            if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, s);
         }
         if (colblocks >= 512 && run_decode3_k<1, 3, 4, 8>(a, s, e)) return e;
         if (run_decode3_k<1, 1, 8, 16>(a, s, e)) return e;
@@ -1014,26 +971,6 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
         return run_decode2<4, 3, 8, 1>(a, s);
     }
     return run_decode2<4, 1, 8, 2>(a, s);
-}
-
-// Activation-prep fused decode: the FP16 copy of the M rows must fit the LDS
-// budget, K must hold an even number (>= 2) of 128-channel chunks (scale
-// bytes are read 16 at a time) and at most 16 waves x 8 chunks.
-bool fused_decode_ok(int64_t M, int64_t K)
-{
-    return M >= 1 && M <= 4 && K >= 2 * BK && K % (2 * BK) == 0 && K <= 16 * 8 * BK &&
-           M * K * 2 <= XFUSED_MAX;
-}
-
-hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t s)
-{
-    if (a.M == 0 || a.N == 0) return hipSuccess;
-    if (a.K == 0) return launch_gemm(Path::Prefill, a, nullptr, 0, s);   // Y = 0 (k <= K)
-    const int nchunk = (int)(a.K / BK);
-    if (nchunk <= 8 * 4) return run_decode_xlds<8, 4, true>(a, s);
-    if (nchunk <= 16 * 4) return run_decode_xlds<16, 4, true>(a, s);
-    if (nchunk <= 16 * 6) return run_decode_xlds<16, 6, true>(a, s);
-    return run_decode_xlds<16, 8, true>(a, s);
 }
 
 }  // namespace splice

@@ -91,7 +91,9 @@ __device__ __forceinline__ unsigned block_amax_bits(const Block16 &x)
 //    an element is then the number of keys below its magnitude pattern,
 //    found for two elements at once by a three-step binary search on packed
 //    16-bit lanes (keys are non-decreasing, patterns and keys < 2^15, so the
-//    sign bit of key - pattern says pattern > key).
+//    sign bit of key - pattern says pattern > key).  The keys come from the
+//    exact fp64 products, or, when alpha >= 2^-80, from fp32 products with
+//    their fma residual, which yields the same keys with fewer instructions.
 // ===========================================================================
 
 // Round v >= 0 to E4M3FN, nearest, ties to even mantissa, saturating at 448.
@@ -132,6 +134,20 @@ __device__ __forceinline__ unsigned key_pair(double t, bool tie_up)
     return (kb >> 16) | (kb & 0xFFFF0000u);
 }
 
+// The same key for t = ms * alpha in fp32 arithmetic: ms = m_i * s is exact
+// (at most 3 + 4 significant bits), hi = fl(ms * alpha) is the nearest float
+// to t, i.e. the fp32 value key_pair starts from, and lo = fma(ms, alpha, -hi)
+// is exactly t - hi as long as nothing underflows, so its sign says whether
+// hi lies above, on or below t.  Valid when alpha >= 2^-80 (t >= 2^-91).
+__device__ __forceinline__ unsigned key_pair_f32(float ms, float alpha, bool tie_up)
+{
+#pragma clang fp contract(off)
+    const float hi = ms * alpha;
+    const float lo = __builtin_fmaf(ms, alpha, -hi);
+    const unsigned kb = __float_as_uint(hi) - ((tie_up ? lo <= 0.0f : lo < 0.0f) ? 1u : 0u);
+    return (kb >> 16) | (kb & 0xFFFF0000u);
+}
+
 // 0xFFFF in each half where the pattern half of p2 is above the key half of
 // k2: packed 16-bit subtract, then an arithmetic shift of each half by 15.
 // (Written as two instructions: left to the compiler, the shift is turned
@@ -154,36 +170,115 @@ __device__ __forceinline__ unsigned pack_nibbles(unsigned a, unsigned b, unsigne
     return ((x | (x >> 12)) & 0xFFFFu) | (((y | (y >> 12)) & 0xFFFFu) << 16);
 }
 
-// Codes (16 nibbles, element 2i in the low nibble of byte i) and E4M3 scale
-// byte of one block whose protected lanes are already +0.
-__device__ __forceinline__ unsigned quantize_block(const Block16 &x, double alpha, double six_alpha,
-                                                   u32x2 &codes)
+// The tensor scale in the forms the block functions use.  fast: alpha is
+// large enough for the fp32 keys (a property of the whole tensor, so every
+// lane takes the same branch).
+struct TensorScale {
+    double alpha, six_alpha;
+    float alpha_f;
+    bool fast;
+};
+
+__device__ __forceinline__ TensorScale tensor_scale(float alpha)
 {
 #pragma clang fp contract(off)
-    const unsigned sc = e4m3_rne_sat((double)bf16_bits_to_f32(block_amax_bits(x)) / six_alpha);
-    unsigned k0 = 0x7FFF7FFFu, k1 = k0, k2 = k0, k3 = k0, k4 = k0, k5 = k0, k6 = k0;
+    return TensorScale{(double)alpha, 6.0 * (double)alpha, alpha, alpha >= 0x1p-80f};
+}
+
+// E4M3 scale byte of a block from its amax pattern (protected lanes at +0).
+__device__ __forceinline__ unsigned block_scale(unsigned amax_bits, const TensorScale &ts)
+{
+#pragma clang fp contract(off)
+    return e4m3_rne_sat((double)bf16_bits_to_f32(amax_bits) / ts.six_alpha);
+}
+
+// Keys of the seven E2M1 midpoints times s*alpha (key_pair above).  When the
+// scale byte is 0 every element codes to 0: all keys at the top.
+struct Keys { unsigned k[7]; };
+
+__device__ __forceinline__ Keys block_keys(unsigned sc, const TensorScale &ts)
+{
+#pragma clang fp contract(off)
+    Keys r;
+#pragma unroll
+    for (int i = 0; i < 7; i++) r.k[i] = 0x7FFF7FFFu;
     if (sc != 0) {
-        const double phys = e4m3_value(sc) * alpha;                   // exact
-        k0 = key_pair(0.25 * phys, false);
-        k1 = key_pair(0.75 * phys, true);
-        k2 = key_pair(1.25 * phys, false);
-        k3 = key_pair(1.75 * phys, true);
-        k4 = key_pair(2.5 * phys, false);
-        k5 = key_pair(3.5 * phys, true);
-        k6 = key_pair(5.0 * phys, false);
+        if (ts.fast) {
+            const float s = (float)e4m3_value(sc);                   // exact
+            r.k[0] = key_pair_f32(0.25f * s, ts.alpha_f, false);
+            r.k[1] = key_pair_f32(0.75f * s, ts.alpha_f, true);
+            r.k[2] = key_pair_f32(1.25f * s, ts.alpha_f, false);
+            r.k[3] = key_pair_f32(1.75f * s, ts.alpha_f, true);
+            r.k[4] = key_pair_f32(2.5f * s, ts.alpha_f, false);
+            r.k[5] = key_pair_f32(3.5f * s, ts.alpha_f, true);
+            r.k[6] = key_pair_f32(5.0f * s, ts.alpha_f, false);
+        } else {
+            const double phys = e4m3_value(sc) * ts.alpha;           // exact
+            r.k[0] = key_pair(0.25 * phys, false);
+            r.k[1] = key_pair(0.75 * phys, true);
+            r.k[2] = key_pair(1.25 * phys, false);
+            r.k[3] = key_pair(1.75 * phys, true);
+            r.k[4] = key_pair(2.5 * phys, false);
+            r.k[5] = key_pair(3.5 * phys, true);
+            r.k[6] = key_pair(5.0 * phys, false);
+        }
     }
+    return r;
+}
+
+// Codes of the two elements of one word (bits 3:0 and 19:16): the number of
+// keys below each magnitude pattern, found by a three-step binary search over
+// the sorted keys, and the sign bit.
+__device__ __forceinline__ unsigned code_word(unsigned w, const Keys &ks)
+{
+    const unsigned p2 = w & 0x7FFF7FFFu;
+    const unsigned a4 = pk_above(p2, ks.k[3]);
+    const unsigned a2 = pk_above(p2, pick(a4, ks.k[5], ks.k[1]));
+    const unsigned a1 = pk_above(p2, pick(a4, pick(a2, ks.k[6], ks.k[4]), pick(a2, ks.k[2], ks.k[0])));
+    return (a4 & 0x00040004u) | (a2 & 0x00020002u) | (a1 & 0x00010001u) | ((w >> 12) & 0x00080008u);
+}
+
+// Codes (16 nibbles, element 2i in the low nibble of byte i) and E4M3 scale
+// byte of one block whose protected lanes are already +0.
+__device__ __forceinline__ unsigned quantize_block(const Block16 &x, const TensorScale &ts, u32x2 &codes)
+{
+    const unsigned sc = block_scale(block_amax_bits(x), ts);
+    const Keys ks = block_keys(sc, ts);
     unsigned nib[8];
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
-        const unsigned p2 = x.w[t] & 0x7FFF7FFFu;
-        const unsigned a4 = pk_above(p2, k3);
-        const unsigned a2 = pk_above(p2, pick(a4, k5, k1));
-        const unsigned a1 = pk_above(p2, pick(a4, pick(a2, k6, k4), pick(a2, k2, k0)));
-        nib[t] = (a4 & 0x00040004u) | (a2 & 0x00020002u) | (a1 & 0x00010001u) |
-                 ((x.w[t] >> 12) & 0x00080008u);
-    }
+    for (int t = 0; t < 8; t++) nib[t] = code_word(x.w[t], ks);
     codes = u32x2{pack_nibbles(nib[0], nib[1], nib[2], nib[3]), pack_nibbles(nib[4], nib[5], nib[6], nib[7])};
     return sc;
+}
+
+// Half a block per lane: the lane holds elements 8h .. 8h+7 as four words
+// (protected lanes already +0) and lane ^ 1 holds the other half; both lanes
+// must call this together.  Returns the block's scale byte and the lane's
+// eight codes; the decisions are those of quantize_block.
+__device__ __forceinline__ unsigned quantize_half_block(const unsigned (&w)[4], const TensorScale &ts,
+                                                        unsigned &codes)
+{
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[t] & 0x7FFF7FFFu));
+    unsigned am = max((unsigned)m.x, (unsigned)m.y);
+    am = max(am, (unsigned)__shfl_xor((int)am, 1));
+    const unsigned sc = block_scale(am, ts);
+    const Keys ks = block_keys(sc, ts);
+    codes = pack_nibbles(code_word(w[0], ks), code_word(w[1], ks), code_word(w[2], ks), code_word(w[3], ks));
+    return sc;
+}
+
+// Sets the protected elements (bit e of m, 8 elements) of four words to +0.
+__device__ __forceinline__ void clear_protected_half(unsigned (&w)[4], unsigned m)
+{
+    const unsigned spread = (m & 0x55u) | ((m & 0xAAu) << 15);
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const unsigned b = (spread >> (2 * t)) & 0x00010001u;
+        w[t] &= ~((b << 16) - b);
+    }
 }
 
 }  // namespace splice

@@ -453,8 +453,7 @@ __global__ __launch_bounds__(ROW_THREADS) void quantize_kernel(
 {
     __shared__ uint32_t smask[MAX_K / 32];
     if (PROT) build_mask(smask, K, idx, k);
-    const double alpha = (double)*alpha_p;
-    const double six_alpha = 6.0 * alpha;
+    const TensorScale ts = tensor_scale(*alpha_p);
     const int nb = (int)(K / NVFP4_BLOCK);
     for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
         const uint16_t *row = A + r * lda;
@@ -467,7 +466,7 @@ __global__ __launch_bounds__(ROW_THREADS) void quantize_kernel(
                 if (m) clear_protected(x, m);
             }
             u32x2 cw;
-            const unsigned sc = quantize_block(x, alpha, six_alpha, cw);
+            const unsigned sc = quantize_block(x, ts, cw);
             *reinterpret_cast<u32x2 *>(crow + b * 8) = cw;
             srow[b] = (uint8_t)sc;
         }

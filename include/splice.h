@@ -157,17 +157,20 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x,
  * part of the projection's cost in Sec. 6.3): the kernel reads the bf16
  * activations, masks the protected channels, quantizes the residual to NVFP4
  * with alpha_x and gathers X_S itself, then computes the splice_gemm product.
- * Y is bit-identical to splice_quantize_nvfp4(X, idx, alpha_x) followed by
- * splice_gemm on the decode path, one launch instead of two, and no
- * Xq/Xs/X_S buffers.
+ * The same operand bits reach the matrix cores as in the two-call form
+ * (splice_quantize_nvfp4(X, idx, alpha_x), then splice_gemm on the decode
+ * path): one launch instead of two and no Xq/Xs/X_S buffers.  Y is
+ * bit-identical to the two-call form where both use the same chunk split and
+ * summation order (K/128 even, M*K <= 32768, and M == 1 when K <= 4096), and
+ * within the GEMM tolerance otherwise.
  *   X       bf16 [M, K] in (DEVICE), row stride ldx (multiple of 8, 16-byte
  *           aligned rows)
  *   idx     int32 [k] in (DEVICE): the protected channels, distinct, in
  *           [0, K) (as splice_select_channels writes them); NULL when k == 0
  *   alpha_x float [1] in (DEVICE), > 0 and finite: the frozen activation scale
  *   Wq, Ws, alpha_w, W_S, Y, ldy: as for splice_gemm.
- * Shapes: M <= SPLICE_FUSED_MAX_M; K a multiple of 256 with 256 <= K <= 16384
- * (the FP16 copy of X, up to 128 KB, stays in LDS), or K == 0 (Y = 0).
+ * Shapes: M <= SPLICE_FUSED_MAX_M; K a multiple of 128 with K <= 16384 (the
+ * FP16 copy of X, up to 128 KB, stays in LDS), or K == 0 (Y = 0).
  * Other shapes return SPLICE_ERR_UNSUPPORTED: use the two-call form.
  * No workspace; nothing is allocated; safe inside stream capture. */
 #define SPLICE_FUSED_MAX_M 4

@@ -140,8 +140,7 @@ def fused(L, M=1, N=64, K=1024, k=8, **over):
     (dict(K=100), splice.ERR_INVALID_ARG),                 # K % 16
     (dict(k=2000), splice.ERR_INVALID_ARG),                # k > K
     (dict(M=splice.FUSED_MAX_M + 1), splice.ERR_UNSUPPORTED),
-    (dict(K=384), splice.ERR_UNSUPPORTED),                 # odd number of 128-channel chunks
-    (dict(K=128), splice.ERR_UNSUPPORTED),
+    (dict(K=400), splice.ERR_UNSUPPORTED),                 # not whole 128-channel chunks
     (dict(K=32768, k=8), splice.ERR_UNSUPPORTED),          # beyond 16 waves x 8 chunks
     (dict(ldx=1028, K=1024), splice.ERR_UNSUPPORTED),      # ldx % 8
     (dict(X=FAKE + 2), splice.ERR_UNSUPPORTED),            # X rows not 16-byte aligned
@@ -162,4 +161,4 @@ def test_fused_decode_argument_errors(L, kw, code):
 def test_fused_decode_empty_is_ok(L):
     assert fused(L, M=0) == splice.OK
     assert fused(L, N=0) == splice.OK
-    assert fused(L, M=0, K=384) == splice.OK               # nothing to compute: no shape rule applies
+    assert fused(L, M=0, K=400) == splice.OK               # nothing to compute: no shape rule applies

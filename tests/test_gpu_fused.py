@@ -4,8 +4,9 @@
 Against the oracle: the tolerance in gpu_util, with the oracle quantizing the
 bf16 activations itself.  Against the two-call form (splice_quantize_nvfp4,
 then splice_gemm on the decode path): bit-identical wherever the two-call form
-runs the same activations-in-LDS kernel (M*K*2 <= 64 KB), since the same FP16
-operands then enter the same matrix-core sequence; elsewhere the two forms sum
+runs its activations-in-LDS kernel with the fused call's wave configuration
+(same_kernel below), since the same FP16 operands then enter the same
+matrix-core sequence and the same summation order; elsewhere the two forms sum
 the K chunks in different orders and agree to the tolerance.
 """
 import numpy as np
@@ -20,6 +21,14 @@ from gpu_util import assert_gemm_close, dev, host, scalar
 pytestmark = pytest.mark.gpu
 
 XLDS_BYTES = 64 * 1024     # FP16 activations the two-call decode keeps in LDS
+
+
+def same_kernel(M, K):
+    """The two-call decode runs the kernel the fused call mirrors, with the
+    same waves: an even chunk count and X in its LDS budget; K <= 4096 only
+    for one row (more rows take sixteen waves in the fused form)."""
+    nchunk = K // 128
+    return M * K * 2 <= XLDS_BYTES and nchunk % 2 == 0 and (nchunk > 32 or M == 1)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,19 +67,22 @@ def check_case(X, W, idx, what, ldx_pad=0):
     Y2 = two_call(Xd, idxd, axd, wq, ws, awd, wS, k)
     torch.cuda.synchronize()
     assert_gemm_close(host(Yf), Yo, what)
-    if M * K * 2 <= XLDS_BYTES:
+    if same_kernel(M, K):
         assert torch.equal(Yf, Y2), f"{what}: fused and two-call results differ"
     else:
         assert_gemm_close(host(Yf), host(Y2).astype(np.float64), what + " vs two-call")
 
 
 # (M, N, K, k): several 16-column blocks and a ragged tail in N, every wave
-# count of the dispatch (K up to 32, 64, 96, 128 chunks), the side-operand
+# count of the dispatch (K up to 32, 64, 96, 128 chunks; odd chunk counts),
+# 48-column workgroups for wide N (N >= 8192 with K <= 4096), the side-operand
 # forms (k = 0; 32 and 64 preloaded; ragged, unaligned and all-protected)
 CASES = [(1, 16, 256, 0), (1, 100, 1024, 5), (2, 48, 512, 64), (3, 130, 1024, 32),
          (4, 1000, 1024, 64), (1, 272, 4096, 64), (4, 80, 4096, 100), (2, 70, 8192, 33),
          (1, 50, 12288, 64), (4, 40, 12288, 64), (3, 24, 16384, 16), (1, 33, 16384, 128),
-         (2, 64, 256, 256), (4, 17, 768, 7)]
+         (2, 64, 256, 256), (4, 17, 768, 7), (1, 40, 128, 16), (3, 60, 384, 64),
+         (2, 90, 1152, 0), (1, 8200, 1024, 64), (2, 8195, 512, 5), (4, 8240, 4096, 32),
+         (1, 8192, 640, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,k", CASES)
@@ -94,6 +106,18 @@ def test_fused_decode_special_values_and_row_stride():
     W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
     idx = np.sort(g.choice(K, size=k, replace=False)).astype(np.int32)
     check_case(X, W, idx, "special rows, ldx = K + 40", ldx_pad=40)
+
+
+def test_fused_decode_tiny_tensor():
+    """A tensor so small that alpha < 2^-80: the quantizer's fp64 threshold
+    arithmetic (the fp32 form needs alpha >= 2^-80)."""
+    g = np.random.default_rng(80)
+    M, N, K, k = 3, 96, 512, 16
+    X = synth.to_bf16(g.standard_normal((M, K)) * 1e-30)
+    W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
+    idx = np.sort(g.choice(K, size=k, replace=False)).astype(np.int32)
+    assert O.compute_alpha(X, idx) < 2.0 ** -80
+    check_case(X, W, idx, "tiny tensor")
 
 
 def test_fused_decode_output_stride_and_empty_k():
@@ -144,7 +168,7 @@ def test_fused_decode_full_size_sampled(name, M):
     wq_o, ws_o, wS_o = O.quantize_nvfp4(p["W"][cols], oidx, oaw)
     Yo = O.splice_gemm(xq, xs, oax, xS, wq_o, ws_o, oaw, wS_o)
     assert_gemm_close(host(Yf)[:, cols], Yo, f"{name} M={M}")
-    if M * K * 2 <= XLDS_BYTES:
+    if same_kernel(M, K):
         assert torch.equal(Yf, Y2), f"{name} M={M}: fused and two-call results differ"
     else:
         assert_gemm_close(host(Yf), host(Y2).astype(np.float64), f"{name} M={M} vs two-call")

@@ -59,7 +59,11 @@ def test_alpha_and_quantize_bit_exact(R, K, k):
     Ad, idxd = dev(A), dev(idx)
     a_g = S.compute_alpha(Ad, idxd)
     assert scalar(a_g) == np.float32(a_o)
-    for alpha in (a_o, np.float32(1.0), np.float32(2.0 ** -20), np.float32(0.37)):
+    # alphas on both sides of 2^-80, where the quantizer switches between its
+    # fp32 and fp64 threshold arithmetic, down to 2^-100, and a large one
+    for alpha in (a_o, np.float32(1.0), np.float32(2.0 ** -20), np.float32(0.37),
+                  np.float32(2.0 ** -79), np.float32(2.0 ** -80), np.float32(2.0 ** -80 * 0.75),
+                  np.float32(2.0 ** -100), np.float32(1e4)):
         c_o, s_o, side_o = O.quantize_nvfp4(A, idx, alpha)
         c_g, s_g, side_g = S.quantize_nvfp4(Ad, idxd, dev(np.array([alpha], np.float32)))
         torch.cuda.synchronize()
@@ -405,6 +409,14 @@ def test_gemm_empty_k_writes_zeros(M):
         S.nvfp4_gemm(e8, e8, one, w8, w8, one, path=path, out=Y)
         torch.cuda.synchronize()
         assert torch.equal(Y, torch.zeros_like(Y)), f"path {path}"
+    # the grouped form as well (two groups of M rows)
+    Ys = [torch.full((M, N), float("nan"), device=dev_) for _ in range(2)]
+    groups = [dict(Xq=e8, Xs=e8, alpha_x=one, X_S=None, Wq=w8, Ws=w8, alpha_w=one, W_S=None, Y=y)
+              for y in Ys]
+    S.splice_gemm_grouped(groups, N, 0, 0)
+    torch.cuda.synchronize()
+    for y in Ys:
+        assert torch.equal(y, torch.zeros_like(y)), "grouped"
 
 
 @pytest.mark.parametrize("M", [1, 8, 64, 200])
