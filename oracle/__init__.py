@@ -59,6 +59,7 @@ def lib():
                                                 _f32p, _f64p]),
             "oracle_stats": (ctypes.c_int, [_u16p, _i64, _i64, _i64, _i64p, _f64p, _f64p, _f32p]),
             "oracle_select_topk": (ctypes.c_int, [_f64p, _i64, _i32, _i32p]),
+            "oracle_second_moments": (ctypes.c_int, [_f64p, _f64p, _i64, _i64, _f64p]),
             "oracle_select_channels": (ctypes.c_int, [_u16p, _i64, _i64, _i64, _i32, _i64p,
                                                       _f64p, _f64p, _f32p, _i32p, _f32p]),
             "oracle_num_threads": (ctypes.c_int, []),
@@ -247,11 +248,36 @@ def select_topk(m2, k):
     return idx[:k].copy()
 
 
-def select_channels(X, k):
+VARIANCE, SECOND_MOMENT = "variance", "second_moment"
+
+
+def second_moments(st):
+    """E[x^2] per channel from running moments: m2/n + mean^2."""
+    out = np.zeros(st.K, np.float64)
+    mean = _c(st.mean, np.float64)
+    m2 = _c(st.m2, np.float64)
+    _check(lib().oracle_second_moments(_p(mean, _f64p), _p(m2, _f64p), st.count, st.K,
+                                       _p(out, _f64p)), "second_moments")
+    return out
+
+
+def select_from_stats(st, k, criterion=VARIANCE):
+    """Top-k channels of running moments by variance (M2) or by second
+    moment, and the frozen activation scale."""
+    if criterion == VARIANCE:
+        idx = select_topk(st.m2, k)
+    elif criterion == SECOND_MOMENT:
+        idx = select_topk(second_moments(st), k)
+    else:
+        raise ValueError(criterion)
+    return idx, alpha_from_absmax(st.absmax, idx)
+
+
+def select_channels(X, k, criterion=VARIANCE):
     """Calibration on a warm-up batch: returns (idx, alpha_x, Stats)."""
     st = stats(X)
-    idx = select_topk(st.m2, k)
-    return idx, alpha_from_absmax(st.absmax, idx), st
+    idx, ax = select_from_stats(st, k, criterion)
+    return idx, ax, st
 
 
 def num_threads():

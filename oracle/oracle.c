@@ -16,6 +16,8 @@
  *   - Y = alpha_X alpha_W * deq(Q(X_R)) deq(Q(W_R))^T + X_S W_S^T (Sec. 4.2 Eq. 5,
  *                                                                  App. 9.3.1 Eq. 7-8)
  *   - top-s variance channel selection                            (Sec. 4.2)
+ *   - top-s second-moment selection, the minimiser of the relaxed
+ *     error bound                                    (App., Prop. 2, Cor. 1)
  *   - running channel moments accumulated from token rows         (Sec. 5.2)
  *
  * Conventions the pages leave open and that this oracle fixes (each one is
@@ -36,6 +38,9 @@
  *     update of Chan, Golub & LeVeque (1983) folding tiles left to right.
  *   - selection ranks by M2 (n is the same for every channel), larger first,
  *     ties to the lower channel index; the result is returned ascending.
+ *   - the second moment of a channel is formed from the running moments as
+ *     m2/n + mean*mean (variance plus squared mean, three roundings), 0 when
+ *     no row has been seen; it is ranked the same way.
  *
  * Every fp64 expression is written so that each operator is one IEEE
  * rounding; the file is compiled with -ffp-contract=off.
@@ -423,6 +428,25 @@ int oracle_select_topk(const double *m2, int64_t K, int32_t k, int32_t *idx)
     memcpy(idx, order, sizeof(int32_t) * (size_t)k);
     qsort(idx, (size_t)k, sizeof(int32_t), int_cmp);
     free(order);
+    return 0;
+}
+
+/* Second moments m_j = E[x_j^2] of K channels from running moments over n
+ * rows: the population variance m2_j / n plus the squared mean (the relaxed
+ * bound of Prop. 2 is minimised by the largest m_j; Cor. 1 says when the
+ * largest variances give the same set).  0 for every channel when n == 0. */
+int oracle_second_moments(const double *mean, const double *m2, int64_t n, int64_t K, double *out)
+{
+    if (n < 0 || K < 0) return -1;
+    for (int64_t j = 0; j < K; j++) {
+        if (n == 0) {
+            out[j] = 0.0;
+            continue;
+        }
+        double v = m2[j] / (double)n;
+        double mu2 = mean[j] * mean[j];
+        out[j] = v + mu2;
+    }
     return 0;
 }
 

@@ -291,3 +291,96 @@ def test_select_recovers_planted_outliers(oracle_lib):
     xr = synth.bf16_to_f32(d["X_warm"]).copy()
     xr[:, idx] = 0
     assert alpha_x == np.float32(np.abs(xr).max()) / np.float32(2688)
+
+
+# ------------------------------------------------------------------ second-moment selection
+def test_second_moments_exact_rational(oracle_lib):
+    """m_j = E[x_j^2] formed from the running moments equals the exact mean of
+    squares of the bf16 values (the m_j of Prop. 2), over several 64-row tiles
+    and two folded batches."""
+    o = oracle_lib
+    g = np.random.default_rng(21)
+    a = synth.to_bf16(g.standard_normal((150, 5)) * 2 + np.array([0, 3, -1, 0.5, 10]))
+    b = synth.to_bf16(g.standard_normal((70, 5)) + 1)
+    st = o.stats(a).update(b)
+    m = o.second_moments(st)
+    xf = np.concatenate([synth.bf16_to_f32(a), synth.bf16_to_f32(b)])
+    for j in range(5):
+        exact = sum(Fraction(float(v)) ** 2 for v in xf[:, j]) / xf.shape[0]
+        assert m[j] == pytest.approx(float(exact), rel=1e-12)
+
+
+def test_second_moments_without_rows(oracle_lib):
+    o = oracle_lib
+    assert not o.second_moments(o.Stats(7)).any()
+
+
+def _separated_channels(g, T, K, means):
+    """Channels whose standard deviations are spread 1 .. 1 + 0.5 (K - 1) in
+    a random order, with the given means."""
+    sd = 1.0 + 0.5 * g.permutation(K)
+    return synth.to_bf16(g.standard_normal((T, K)) * sd + means)
+
+
+def test_second_moment_selection_brute_force(oracle_lib):
+    """The second-moment top-k equals sorting the exact means of squares
+    (ties to the lower index), on channels far from ties."""
+    o = oracle_lib
+    g = np.random.default_rng(22)
+    T, K = 300, 40
+    x = _separated_channels(g, T, K, g.uniform(-3, 3, K))
+    st = o.stats(x)
+    xf = synth.bf16_to_f32(x)
+    exact = [sum(Fraction(float(v)) ** 2 for v in xf[:, j]) / T for j in range(K)]
+    order = sorted(range(K), key=lambda j: (-exact[j], j))
+    for k in (1, 5, 17, 39, 40):
+        if k < K:                                  # the case is meaningful: a real gap at the boundary
+            assert exact[order[k - 1]] - exact[order[k]] > 1e-6 * exact[order[k - 1]]
+        idx, _ = o.select_from_stats(st, k, o.SECOND_MOMENT)
+        assert idx.tolist() == sorted(order[:k])
+
+
+def test_corollary1_gap_condition(oracle_lib):
+    """Cor. 1: when the largest squared mean is below the variance gap
+    v_(s) - v_(s+1), the top-s variance set is the top-s second-moment set;
+    with zero means the two rankings coincide for every s."""
+    o = oracle_lib
+    g = np.random.default_rng(23)
+    T, K, s = 400, 32, 8
+    x = _separated_channels(g, T, K, 0.02 * g.standard_normal(K))
+    st = o.stats(x)
+    v = np.sort(st.m2 / st.count)[::-1]
+    assert np.max(st.mean ** 2) < v[s - 1] - v[s]          # the hypothesis holds here
+    iv, _ = o.select_from_stats(st, s, o.VARIANCE)
+    im, _ = o.select_from_stats(st, s, o.SECOND_MOMENT)
+    assert np.array_equal(iv, im)
+    # exactly zero means: rows x and -x in pairs, so the second moment is the variance
+    half = _separated_channels(g, T // 2, K, 0.0)
+    sym = np.empty((T, K), np.uint16)
+    sym[0::2] = half
+    sym[1::2] = half ^ np.uint16(0x8000)
+    st0 = o.stats(sym)
+    xf = synth.bf16_to_f32(sym)
+    for k in (1, 8, 31):
+        want = sorted(sorted(range(K), key=lambda j: (-float(np.sum(xf[:, j].astype(np.float64) ** 2)), j))[:k])
+        assert o.select_from_stats(st0, k, o.VARIANCE)[0].tolist() == want
+        assert o.select_from_stats(st0, k, o.SECOND_MOMENT)[0].tolist() == want
+
+
+def test_second_moment_differs_when_the_gap_condition_fails(oracle_lib):
+    """A channel with a large mean and almost no spread has the largest
+    second moment and the smallest variance: the two criteria disagree, as
+    Cor. 1 allows once the squared mean exceeds the variance gap."""
+    o = oracle_lib
+    g = np.random.default_rng(24)
+    T, K = 256, 16
+    xr = g.standard_normal((T, K))
+    xr[:, 5] = 8.0 + 0.01 * g.standard_normal(T)
+    st = o.stats(synth.to_bf16(xr))
+    iv, _ = o.select_from_stats(st, 1, o.VARIANCE)
+    im, ax_m = o.select_from_stats(st, 1, o.SECOND_MOMENT)
+    assert im.tolist() == [5] and iv.tolist() != [5]
+    assert int(np.argmin(st.m2)) == 5
+    # the frozen scale follows the selected set: channel 5 no longer counts
+    assert ax_m == o.alpha_from_absmax(st.absmax, np.array([5], np.int32))
+    assert ax_m < o.alpha_from_absmax(st.absmax, iv)
