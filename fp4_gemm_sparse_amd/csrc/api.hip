@@ -103,10 +103,49 @@ int splice_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx,
         return SPLICE_ERR_INVALID_ARG;
     hipError_t e = launch_stats(X, T, K, ldx, *count, mean, m2, absmax, hs(stream));
     if (e != hipSuccess) return SPLICE_ERR_HIP;
-    e = launch_select(m2, absmax, K, k, idx, alpha_x, hs(stream));
+    e = launch_select(m2, nullptr, *count + T, absmax, K, k, idx, alpha_x, hs(stream));
     if (e != hipSuccess) return SPLICE_ERR_HIP;
     *count += T;
     return SPLICE_OK;
+}
+
+int splice_channel_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int64_t *count,
+                         double *mean, double *m2, float *absmax, splice_stream_t stream)
+{
+    if (T < 0 || !count || *count < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(K, 0);
+    if (rc) return rc;
+    if (K == 0) {
+        *count += T;
+        return SPLICE_OK;
+    }
+    if (!mean || !m2 || !absmax || (T > 0 && !X)) return SPLICE_ERR_INVALID_ARG;
+    if (T > 0 && ldx < K) return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(X, 2) || !aligned(mean, 8) || !aligned(m2, 8) || !aligned(absmax, 4))
+        return SPLICE_ERR_INVALID_ARG;
+    hipError_t e = launch_stats(X, T, K, ldx, *count, mean, m2, absmax, hs(stream));
+    if (e != hipSuccess) return SPLICE_ERR_HIP;
+    *count += T;
+    return SPLICE_OK;
+}
+
+int splice_select_topk(const double *mean, const double *m2, const float *absmax, int64_t count,
+                       int64_t K, int32_t k, int criterion, int32_t *idx, float *alpha_x,
+                       splice_stream_t stream)
+{
+    if (count < 0) return SPLICE_ERR_INVALID_ARG;
+    int rc = check_k(K, k);
+    if (rc) return rc;
+    if (criterion != SPLICE_SELECT_VARIANCE && criterion != SPLICE_SELECT_SECOND_MOMENT)
+        return SPLICE_ERR_INVALID_ARG;
+    if (K == 0) return SPLICE_OK;
+    const bool sm = criterion == SPLICE_SELECT_SECOND_MOMENT;
+    if (!m2 || !absmax || (k > 0 && !idx) || (sm && !mean)) return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(m2, 8) || !aligned(mean, 8) || !aligned(absmax, 4) || !aligned(idx, 4) ||
+        !aligned(alpha_x, 4))
+        return SPLICE_ERR_INVALID_ARG;
+    return hip_status(launch_select(m2, sm ? mean : nullptr, count, absmax, K, k, idx, alpha_x,
+                                    hs(stream)));
 }
 
 size_t splice_alpha_workspace_size(void) { return alpha_ws_bytes(); }

@@ -9,8 +9,9 @@ namespace splice {
 // channel statistics + top-k (+ frozen activation scale)
 hipError_t launch_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int64_t count_prev,
                         double *mean, double *m2, float *absmax, hipStream_t s);
-hipError_t launch_select(const double *m2, const float *absmax, int64_t K, int32_t k,
-                         int32_t *idx, float *alpha_x, hipStream_t s);
+// mean == nullptr: rank by M2 (variance); else by m2/count + mean^2
+hipError_t launch_select(const double *m2, const double *mean, int64_t count, const float *absmax,
+                         int64_t K, int32_t k, int32_t *idx, float *alpha_x, hipStream_t s);
 
 // masked amax -> alpha
 size_t alpha_ws_bytes();

@@ -127,12 +127,15 @@ hipError_t launch_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, in
 }
 
 // ===========================================================================
-// Top-k selection: the k channels with the largest M2, ties to the lower
-// index, written in ascending channel order; plus the frozen activation scale
-// (largest absmax over the channels left unprotected) / 2688.
+// Top-k selection: the k channels with the largest M2 (variance), or with
+// the largest second moment m2/n + mean^2 (the minimiser of the relaxed error
+// bound, FourSight App. Prop. 2 / Cor. 1), ties to the lower index, written in
+// ascending channel order; plus the frozen activation scale (largest absmax
+// over the channels left unprotected) / 2688.
 // One workgroup: an 8-pass radix select over a total-order key of the fp64
-// M2 finds the k-th largest key and how many of the keys equal to it are
-// taken (the lowest-indexed ones); two scans then compact the selection.
+// ranking value finds the k-th largest key and how many of the keys equal to
+// it are taken (the lowest-indexed ones); two scans then compact the
+// selection.
 // ===========================================================================
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / WAVE;
@@ -190,21 +193,36 @@ __device__ __forceinline__ void hist_add(unsigned *hist, unsigned d, bool active
     if (active) atomicAdd(&hist[d], 1u);
 }
 
+// Ranking value of channel j: M2, or with mean != nullptr the second moment
+// m2/n + mean^2 (one IEEE rounding per operation; 0 before any row).
+struct RankValue {
+    const double *m2, *mean;
+    double n;
+    __device__ __forceinline__ double operator()(int64_t j) const
+    {
+        if (!mean) return m2[j];
+        if (n == 0.0) return 0.0;
+        const double v = m2[j] / n;
+        const double mu2 = mean[j] * mean[j];
+        return v + mu2;
+    }
+};
+
 // The order keys of a thread's channels c0 .. c1-1: held in registers when
-// PER > 0 (at most PER per thread), re-read from m2 otherwise.
+// PER > 0 (at most PER per thread), recomputed otherwise.
 template <int PER>
 struct KeySource {
     uint64_t reg[PER > 0 ? PER : 1];
-    const double *m2;
+    RankValue val;
     int64_t c0, c1;
-    __device__ __forceinline__ void init(const double *m, int64_t a, int64_t b)
+    __device__ __forceinline__ void init(const RankValue &v, int64_t a, int64_t b)
     {
-        m2 = m;
+        val = v;
         c0 = a;
         c1 = b;
         if (PER > 0) {
 #pragma unroll
-            for (int i = 0; i < (PER > 0 ? PER : 1); i++) reg[i] = (c0 + i < c1) ? order_key(m2[c0 + i]) : 0;
+            for (int i = 0; i < (PER > 0 ? PER : 1); i++) reg[i] = (c0 + i < c1) ? order_key(val(c0 + i)) : 0;
         }
     }
     __device__ __forceinline__ uint64_t operator()(int i) const
@@ -215,12 +233,12 @@ struct KeySource {
             for (int q = 0; q < (PER > 0 ? PER : 1); q++) v = (q == i) ? reg[q] : v;
             return v;
         }
-        return order_key(m2[c0 + i]);
+        return order_key(val(c0 + i));
     }
 };
 
 template <int PER>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__restrict__ m2,
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
                                                              const float *__restrict__ absmax,
                                                              int64_t K, int32_t k, int32_t *idx,
                                                              float *alpha_x)
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__res
     const int64_t c0 = min(K, (int64_t)tid * per), c1 = min(K, c0 + per);
     const int n = (int)(c1 - c0);
     KeySource<PER> keys;
-    keys.init(m2, c0, c1);
+    keys.init(rv, c0, c1);
 
     uint64_t thr = 0;       // key of the k-th largest channel
     int64_t need = 0;       // how many channels with key == thr are taken
@@ -331,18 +349,19 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const double *__res
     }
 }
 
-hipError_t launch_select(const double *m2, const float *absmax, int64_t K, int32_t k, int32_t *idx,
-                         float *alpha_x, hipStream_t s)
+hipError_t launch_select(const double *m2, const double *mean, int64_t count, const float *absmax,
+                         int64_t K, int32_t k, int32_t *idx, float *alpha_x, hipStream_t s)
 {
+    const RankValue rv{m2, mean, (double)count};
     const int64_t per = (K + SEL_THREADS - 1) / SEL_THREADS;
     if (per <= 4)
-        hipLaunchKernelGGL(select_kernel<4>, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k,
+        hipLaunchKernelGGL(select_kernel<4>, dim3(1), dim3(SEL_THREADS), 0, s, rv, absmax, K, k,
                            idx, alpha_x);
     else if (per <= 16)
-        hipLaunchKernelGGL(select_kernel<16>, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k,
+        hipLaunchKernelGGL(select_kernel<16>, dim3(1), dim3(SEL_THREADS), 0, s, rv, absmax, K, k,
                            idx, alpha_x);
     else
-        hipLaunchKernelGGL(select_kernel<0>, dim3(1), dim3(SEL_THREADS), 0, s, m2, absmax, K, k,
+        hipLaunchKernelGGL(select_kernel<0>, dim3(1), dim3(SEL_THREADS), 0, s, rv, absmax, K, k,
                            idx, alpha_x);
     return hipGetLastError();
 }

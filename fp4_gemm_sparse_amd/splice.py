@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "splice.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+SELECT_VARIANCE, SELECT_SECOND_MOMENT = 0, 1
 DECODE_MAX_M = 64
 FUSED_MAX_M = 4
 
@@ -49,6 +50,10 @@ _SIGS = {
     "splice_select_channels": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, ctypes.POINTER(_i64),
                                               _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "splice_select_workspace_size": (_sz, [_i64]),
+    "splice_channel_stats": (ctypes.c_int, [_vp, _i64, _i64, _i64, ctypes.POINTER(_i64), _vp, _vp,
+                                            _vp, _vp]),
+    "splice_select_topk": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, ctypes.c_int, _vp, _vp,
+                                          _vp]),
     "splice_compute_alpha": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
     "splice_alpha_workspace_size": (_sz, []),
     "splice_quantize_nvfp4": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp,
@@ -158,6 +163,39 @@ def select_channels(X, k, stats: ChannelStats | None = None, ldx=None, T=None, o
                                         _stream()))
     stats.count = cnt.value
     return idx, alpha, stats
+
+
+def channel_stats(X, stats: ChannelStats | None = None, ldx=None, T=None):
+    """Fold the rows of X (bf16 [T, K], row stride ldx) into running moments."""
+    X = _bf16(X)
+    K = X.shape[-1]
+    if ldx is None:
+        ldx = X.stride(0) if X.dim() == 2 else K
+    if T is None:
+        T = X.shape[0]
+    if stats is None:
+        stats = ChannelStats.empty(K, X.device)
+    cnt = _i64(stats.count)
+    _check("splice_channel_stats",
+           lib().splice_channel_stats(_p(X), T, K, ldx, ctypes.byref(cnt), _p(stats.mean),
+                                      _p(stats.m2), _p(stats.absmax), _stream()))
+    stats.count = cnt.value
+    return stats
+
+
+def select_topk(stats: ChannelStats, k, criterion=SELECT_VARIANCE, out=None):
+    """Top-k channels of running moments by variance or second moment.
+    Returns (idx int32 [k] ascending, alpha_x float32 [1])."""
+    K = stats.m2.numel()
+    if out is None:
+        idx = torch.empty(k, dtype=torch.int32, device=stats.m2.device)
+        alpha = torch.empty(1, dtype=torch.float32, device=stats.m2.device)
+    else:
+        idx, alpha = out
+    _check("splice_select_topk",
+           lib().splice_select_topk(_p(stats.mean), _p(stats.m2), _p(stats.absmax), stats.count, K,
+                                    k, criterion, _p(idx), _p(alpha), _stream()))
+    return idx, alpha
 
 
 def compute_alpha(A, idx=None, out=None, ws=None):

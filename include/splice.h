@@ -104,6 +104,33 @@ int splice_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx,
 size_t splice_select_workspace_size(int64_t K);
 
 /* ---------------------------------------------------------------------------
+ * The two halves of splice_select_channels, for callers that fold token rows
+ * into the running moments as they pass (Sec. 5.2: a forward hook subsamples
+ * rows into running channel moments; the protected set is reselected once
+ * per optimizer step from what the previous step gathered).
+ *
+ * splice_channel_stats: folds the T rows of X into mean/m2/absmax exactly as
+ * splice_select_channels does (same arguments, same arithmetic, same count
+ * rules), without selecting.
+ *
+ * splice_select_topk: the k channels ranked by `criterion` from running
+ * moments over `count` rows (count is a HOST value), ties to the lower index,
+ * written to idx[0..k) ascending, and alpha_x (may be NULL) as for
+ * splice_select_channels.
+ *   SPLICE_SELECT_VARIANCE: the largest M2 (the paper's selection, Sec. 4.2);
+ *     mean may be NULL.
+ *   SPLICE_SELECT_SECOND_MOMENT: the largest m2/count + mean^2 = E[x^2] per
+ *     channel (fp64, one rounding per operation; 0 when count == 0), the set
+ *     that minimises the relaxed error bound (App. Prop. 2); Cor. 1 gives the
+ *     condition on the means under which both criteria pick the same set. */
+enum { SPLICE_SELECT_VARIANCE = 0, SPLICE_SELECT_SECOND_MOMENT = 1 };
+int splice_channel_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int64_t *count,
+                         double *mean, double *m2, float *absmax, splice_stream_t stream);
+int splice_select_topk(const double *mean, const double *m2, const float *absmax, int64_t count,
+                       int64_t K, int32_t k, int criterion, int32_t *idx, float *alpha_x,
+                       splice_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * alpha = fp32(max |A| over the unprotected columns / 2688), 1 if that is 0
  * (Sec. 2.1 FP32 tensor scale; App. 9.3.1 Eq. 9).  A: bf16 [R, K], stride
  * lda.  alpha: float [1] out.  ws: splice_alpha_workspace_size() bytes. */

@@ -162,3 +162,35 @@ def test_fused_decode_empty_is_ok(L):
     assert fused(L, M=0) == splice.OK
     assert fused(L, N=0) == splice.OK
     assert fused(L, M=0, K=400) == splice.OK               # nothing to compute: no shape rule applies
+
+
+def test_channel_stats_argument_errors(L):
+    f = L.splice_channel_stats
+    cnt = ctypes.c_int64(0)
+    assert f(FAKE, -1, 64, 64, ctypes.byref(cnt), FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 64, None, FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG      # count
+    assert f(FAKE, 4, 60, 64, ctypes.byref(cnt), FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 32, ctypes.byref(cnt), FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 64, ctypes.byref(cnt), None, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 64, ctypes.byref(cnt), FAKE + 4, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(FAKE, 4, 131072, 131072, ctypes.byref(cnt), FAKE, FAKE, FAKE, None) == splice.ERR_UNSUPPORTED
+    bad = ctypes.c_int64(-1)
+    assert f(FAKE, 4, 64, 64, ctypes.byref(bad), FAKE, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert cnt.value == 0                                   # nothing folded on an error
+    assert f(None, 5, 0, 0, ctypes.byref(cnt), None, None, None, None) == splice.OK
+    assert cnt.value == 5                                   # K = 0: rows counted, nothing else
+
+
+def test_select_topk_argument_errors(L):
+    f = L.splice_select_topk
+    V, SM = splice.SELECT_VARIANCE, splice.SELECT_SECOND_MOMENT
+    assert f(FAKE, FAKE, FAKE, -1, 64, 8, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # count
+    assert f(FAKE, FAKE, FAKE, 10, 64, 65, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG  # k > K
+    assert f(FAKE, FAKE, FAKE, 10, 60, 8, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # K % 16
+    assert f(FAKE, FAKE, FAKE, 10, 64, 8, 2, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # criterion
+    assert f(None, FAKE, FAKE, 10, 64, 8, SM, FAKE, FAKE, None) == splice.ERR_INVALID_ARG  # mean
+    assert f(FAKE, None, FAKE, 10, 64, 8, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # m2
+    assert f(FAKE, FAKE, None, 10, 64, 8, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG   # absmax
+    assert f(FAKE, FAKE, FAKE, 10, 64, 8, V, None, FAKE, None) == splice.ERR_INVALID_ARG   # idx
+    assert f(FAKE, FAKE + 4, FAKE, 10, 64, 8, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(None, None, None, 10, 0, 0, SM, None, None, None) == splice.OK                # K = 0

@@ -141,6 +141,76 @@ def test_select_row_stride_subsamples():
     assert np.array_equal(host(idx_g), idx_o)
 
 
+
+def _offset_activations(T, K, seed):
+    """Activations whose channels also carry means of several sizes, so that
+    the variance and second-moment rankings differ."""
+    g = np.random.default_rng(seed)
+    x = synth.bf16_to_f32(synth.activations(7, seed % 7, T, K, 2, "student", n_out=min(64, K // 4)))
+    mu = np.where(g.random(K) < 0.05, g.uniform(-12, 12, K), g.uniform(-0.5, 0.5, K))
+    return synth.to_bf16(x.astype(np.float64) + mu)
+
+
+@pytest.mark.parametrize("T,K,k", [(64, 1024, 64), (512, 4096, 64), (300, 12288, 128), (33, 256, 17),
+                                   (1, 64, 8), (40, 20480, 64), (0, 128, 5)])
+def test_select_topk_both_criteria_bit_exact(T, K, k):
+    """Statistics folded with splice_channel_stats, then selection by variance
+    and by second moment, against the oracle; the variance form equals the
+    combined splice_select_channels bit for bit."""
+    X = _offset_activations(T, K, T + K + k)
+    st_o = O.stats(X)
+    st_g = S.channel_stats(dev(X)) if T else S.ChannelStats.empty(K)
+    assert st_g.count == T
+    assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
+    assert np.array_equal(host(st_g.mean).view(np.uint64), st_o.mean.view(np.uint64))
+    for crit, ocrit in ((S.SELECT_VARIANCE, O.VARIANCE), (S.SELECT_SECOND_MOMENT, O.SECOND_MOMENT)):
+        idx_o, ax_o = O.select_from_stats(st_o, k, ocrit)
+        idx_g, ax_g = S.select_topk(st_g, k, crit)
+        assert np.array_equal(host(idx_g), idx_o), crit
+        assert scalar(ax_g) == np.float32(ax_o), crit
+    if T:
+        idx_c, ax_c, _ = S.select_channels(dev(X), k)
+        idx_v, ax_v = S.select_topk(st_g, k, S.SELECT_VARIANCE)
+        assert torch.equal(idx_c, idx_v) and torch.equal(ax_c, ax_v)
+
+
+def test_second_moment_selection_differs_and_follows_the_oracle():
+    """On the offset activations, beyond the 64 planted high-variance
+    channels (which lead both rankings), the two criteria pick different
+    channels; each set matches the oracle."""
+    X = _offset_activations(512, 4096, 5)
+    st_o = O.stats(X)
+    st_g = S.channel_stats(dev(X))
+    iv, _ = S.select_topk(st_g, 128, S.SELECT_VARIANCE)
+    im, _ = S.select_topk(st_g, 128, S.SELECT_SECOND_MOMENT)
+    assert len(set(host(iv).tolist()) ^ set(host(im).tolist())) > 64
+    assert np.array_equal(host(iv), O.select_from_stats(st_o, 128, O.VARIANCE)[0])
+    assert np.array_equal(host(im), O.select_from_stats(st_o, 128, O.SECOND_MOMENT)[0])
+
+
+def test_running_subsampled_stats_across_steps():
+    """Three batches folded in turn, each through a row stride that keeps
+    every other token row (the forward hook's subsampling), then reselection
+    by both criteria: bit-identical moments and selections to the oracle's
+    running fold over the same rows."""
+    K, k = 2048, 64
+    st_o = O.Stats(K)
+    st_g = S.ChannelStats.empty(K)
+    for step, T in enumerate((256, 130, 64)):
+        X = _offset_activations(T, K, 40 + step)
+        st_o.update(X[::2])
+        st_g = S.channel_stats(dev(X), st_g, ldx=2 * K, T=(T + 1) // 2)
+        assert st_g.count == st_o.count
+        assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
+        assert np.array_equal(host(st_g.mean).view(np.uint64), st_o.mean.view(np.uint64))
+        assert np.array_equal(host(st_g.absmax), st_o.absmax)
+        for crit, ocrit in ((S.SELECT_VARIANCE, O.VARIANCE), (S.SELECT_SECOND_MOMENT, O.SECOND_MOMENT)):
+            idx_o, ax_o = O.select_from_stats(st_o, k, ocrit)
+            idx_g, ax_g = S.select_topk(st_g, k, crit)
+            assert np.array_equal(host(idx_g), idx_o), (step, crit)
+            assert scalar(ax_g) == np.float32(ax_o), (step, crit)
+
+
 # ------------------------------------------------------------------ GEMM
 def oracle_pipeline(X_warm, X, W, k, rows=None, cols=None, idx=None):
     """The oracle's own calibration, packs and product (optionally on a row /
