@@ -63,6 +63,9 @@ def lib():
             "oracle_select_channels": (ctypes.c_int, [_u16p, _i64, _i64, _i64, _i32, _i64p,
                                                       _f64p, _f64p, _f32p, _i32p, _f32p]),
             "oracle_num_threads": (ctypes.c_int, []),
+            "oracle_tim_filter": (ctypes.c_int, [_f32p, _i64, _i64, _i32p, ctypes.c_float, _i64,
+                                                 _i64, _i64, _u8p, _i32p, _i32p, _f32p, _i64,
+                                                 _i64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -278,6 +281,33 @@ def select_channels(X, k, criterion=VARIANCE):
     st = stats(X)
     idx, ax = select_from_stats(st, k, criterion)
     return idx, ax, st
+
+
+def tim_filter(logp, lengths, log_tau, k1_num=1, k1_den=100, k2=5, adv=None):
+    """TIM-aware sequence filter over per-token log-probabilities logp
+    float32 [B, L] (tokens t >= lengths[i] are padding).  Returns
+    (keep u8 [B], G1 int32 [B], G2 int32 [B], masked copy of adv or None);
+    adv is float32 [B] or [B, C]."""
+    logp = _c(logp, np.float32)
+    B, L = logp.shape
+    lengths = _c(lengths, np.int32)
+    keep = np.zeros(max(B, 1), np.uint8)
+    g1 = np.zeros(max(B, 1), np.int32)
+    g2 = np.zeros(max(B, 1), np.int32)
+    out = None
+    cols = 0
+    if adv is not None:
+        out = np.array(adv, np.float32, copy=True).reshape(B, -1)
+        cols = out.shape[1]
+    lp = logp if logp.size else np.zeros(1, np.float32)
+    ln = lengths if lengths.size else np.zeros(1, np.int32)
+    ob = out if (out is not None and out.size) else np.zeros(1, np.float32)
+    _check(lib().oracle_tim_filter(_p(lp, _f32p), B, L, _p(ln, _i32p), np.float32(log_tau), k1_num,
+                                   k1_den, k2, _p(keep, _u8p), _p(g1, _i32p), _p(g2, _i32p),
+                                   _p(ob, _f32p), cols, cols), "tim_filter")
+    if out is not None:
+        out = out.reshape(np.shape(adv))
+    return keep[:B].copy(), g1[:B].copy(), g2[:B].copy(), out
 
 
 def num_threads():

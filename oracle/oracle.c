@@ -18,6 +18,8 @@
  *   - top-s variance channel selection                            (Sec. 4.2)
  *   - top-s second-moment selection, the minimiser of the relaxed
  *     error bound                                    (App., Prop. 2, Cor. 1)
+ *   - TIM-aware sequence filtering: tail tokens, the cumulative gate G1,
+ *     the consecutive gate G2 and the masked advantages (Sec. 4.1, Eq. 3-4)
  *   - running channel moments accumulated from token rows         (Sec. 5.2)
  *
  * Conventions the pages leave open and that this oracle fixes (each one is
@@ -462,6 +464,49 @@ int oracle_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx,
     if (rc) return rc;
     if (alpha_x) rc = oracle_alpha_from_absmax(absmax, K, idx, k, alpha_x);
     return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* TIM-aware sequence filtering (Sec. 4.1, Eq. 3-4; settings Sec. 6.1) */
+/* ------------------------------------------------------------------ */
+
+/* For each of B sequences: token t < len[i] is a tail token when its
+ * training-policy log-probability logp[i*ldl + t] <= log_tau (pi_train <= tau
+ * in the log domain; tokens at or past len[i] are padding).
+ *   G1 = number of tail tokens, G2 = longest run of consecutive tail tokens;
+ *   the sequence is kept (f_i = 1) when G1 < K1 and G2 < K2 with
+ *   K1 = (k1_num / k1_den) * len[i], compared exactly as
+ *   G1 * k1_den < k1_num * len[i];
+ *   adv[i*lda + c] for c < adv_cols is multiplied by f_i: a dropped
+ *   sequence's advantages become +0, a kept one's are untouched (Eq. 4).
+ * keep, g1, g2 and adv may each be NULL. */
+int oracle_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *len,
+                      float log_tau, int64_t k1_num, int64_t k1_den, int64_t k2,
+                      uint8_t *keep, int32_t *g1, int32_t *g2,
+                      float *adv, int64_t adv_cols, int64_t lda)
+{
+    if (B < 0 || k1_num < 0 || k1_den <= 0 || k2 < 0 || adv_cols < 0) return -1;
+    for (int64_t i = 0; i < B; i++) {
+        const int64_t n = len[i];
+        if (n < 0 || n > ldl) return -1;
+        int64_t count = 0, run = 0, longest = 0;
+        for (int64_t t = 0; t < n; t++) {
+            if (logp[i * ldl + t] <= log_tau) {
+                count++;
+                run++;
+                if (run > longest) longest = run;
+            } else {
+                run = 0;
+            }
+        }
+        const int kept = (count * k1_den < k1_num * n) && (longest < k2);
+        if (keep) keep[i] = (uint8_t)kept;
+        if (g1) g1[i] = (int32_t)count;
+        if (g2) g2[i] = (int32_t)longest;
+        if (adv && !kept)
+            for (int64_t c = 0; c < adv_cols; c++) adv[i * lda + c] = 0.0f;
+    }
+    return 0;
 }
 
 int oracle_num_threads(void)
