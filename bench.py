@@ -419,6 +419,27 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             S.compute_alpha(p["W"], p["idx"], out=p["aw"])
             S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
     out["reselect_layer_ms"] = round(timed(torch, stream, cold, 5), 4)
+
+    # ---------------- TIM-aware sequence filter over a rollout batch
+    lp, lens = synth.rollout_logprobs()
+    lpd = torch.from_numpy(lp).to(dev)
+    lensd = torch.from_numpy(lens).to(dev)
+    adv0 = torch.randn(len(lens), device=dev)
+    adv = adv0.clone()
+    log_tau = float(np.log(np.float32(1e-4)))
+    res = [torch.empty(len(lens), dtype=torch.uint8, device=dev),
+           torch.empty(len(lens), dtype=torch.int32, device=dev),
+           torch.empty(len(lens), dtype=torch.int32, device=dev)]
+    us = graph_timed(torch, lambda i: S.tim_filter(lpd, lensd, log_tau, adv=adv, out=res), 50) * 1e3
+    kept = int(res[0].sum().item())
+    B = len(lens)
+    byts = 4.0 * float(lens.sum()) + 4 * B + B + 8 * B + 4 * (B - kept)
+    out["tim_filter"] = {"sequences": B, "tokens": int(lens.sum()), "us": round(us, 2),
+                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                         "frac_hbm": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "kept": kept,
+                         "timing": "HIP-graph replay, one launch per call, logp read once"}
+    log("tim filter", out["tim_filter"])
     return out
 
 

@@ -230,6 +230,26 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
     return hip_status(launch_gemm_fused(a, hs(stream)));
 }
 
+int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *len, float log_tau,
+                      int64_t k1_num, int64_t k1_den, int64_t k2, uint8_t *keep, int32_t *g1,
+                      int32_t *g2, float *adv, int64_t adv_cols, int64_t lda,
+                      splice_stream_t stream)
+{
+    constexpr int64_t I31 = 2147483647;
+    if (B < 0 || ldl < 0 || k1_num < 0 || k1_den <= 0 || k2 < 0 || adv_cols < 0)
+        return SPLICE_ERR_INVALID_ARG;
+    if (B > I31 || ldl > I31 || k1_num > I31 || k1_den > I31) return SPLICE_ERR_UNSUPPORTED;
+    if (B == 0) return SPLICE_OK;
+    if (!len || (ldl > 0 && !logp) || (adv_cols > 0 && (!adv || lda < adv_cols)))
+        return SPLICE_ERR_INVALID_ARG;
+    if (!aligned(logp, 4) || !aligned(len, 4) || !aligned(g1, 4) || !aligned(g2, 4) ||
+        !aligned(adv, 4))
+        return SPLICE_ERR_INVALID_ARG;
+    TimArgs a{logp, B, ldl, len, log_tau, k1_num, k1_den, k2, keep, g1, g2,
+              adv_cols > 0 ? adv : nullptr, adv_cols, lda};
+    return hip_status(launch_tim_filter(a, hs(stream)));
+}
+
 size_t splice_grouped_workspace_size(const splice_group *, int32_t, int64_t, int64_t, int32_t)
 {
     return 0;

@@ -52,4 +52,18 @@ hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s);
 bool fused_decode_ok(int64_t M, int64_t K);
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t s);
 
+// TIM-aware sequence filter (tim.hip)
+struct TimArgs {
+    const float *logp;
+    int64_t B, ldl;
+    const int32_t *len;
+    float log_tau;
+    int64_t k1_num, k1_den, k2;
+    uint8_t *keep;
+    int32_t *g1, *g2;
+    float *adv;
+    int64_t adv_cols, lda;
+};
+hipError_t launch_tim_filter(const TimArgs &a, hipStream_t s);
+
 }  // namespace splice

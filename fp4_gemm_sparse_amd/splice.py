@@ -63,6 +63,8 @@ _SIGS = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
                                   _sz, ctypes.c_int, _vp]),
     "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "splice_tim_filter": (ctypes.c_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _i64, _i64, _i64, _vp,
+                                         _vp, _vp, _vp, _i64, _i64, _vp]),
     "splice_gemm_decode_fused": (ctypes.c_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                                 _i64, _i32, _vp, _i64, _vp]),
     "splice_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32, _vp, _sz,
@@ -275,6 +277,29 @@ def splice_gemm_decode_fused(X, idx, alpha_x, Wq, Ws, alpha_w, W_S, out=None):
                                           _p(Wq), _p(Ws), _p(alpha_w), _p(W_S) if k else None,
                                           M, N, K, k, _p(Y), Y.stride(0), _stream()))
     return Y
+
+
+def tim_filter(logp, lengths, log_tau, k1=(1, 100), k2=5, adv=None, out=None):
+    """TIM-aware sequence filter.  logp float32 [B, L] (row stride may exceed L),
+    lengths int32 [B]; adv float32 [B] or [B, C], masked in place.  Returns
+    (keep uint8 [B], G1 int32 [B], G2 int32 [B])."""
+    assert logp.dtype == torch.float32 and lengths.dtype == torch.int32
+    B = logp.shape[0]
+    if out is None:
+        keep = torch.empty(B, dtype=torch.uint8, device=logp.device)
+        g1 = torch.empty(B, dtype=torch.int32, device=logp.device)
+        g2 = torch.empty(B, dtype=torch.int32, device=logp.device)
+    else:
+        keep, g1, g2 = out
+    cols, lda = 0, 0
+    if adv is not None:
+        assert adv.dtype == torch.float32 and adv.shape[0] == B
+        cols = 1 if adv.dim() == 1 else adv.shape[1]
+        lda = adv.stride(0) if adv.dim() == 2 else 1
+    _check("splice_tim_filter",
+           lib().splice_tim_filter(_p(logp), B, logp.stride(0), _p(lengths), float(log_tau), k1[0], k1[1],
+                                   k2, _p(keep), _p(g1), _p(g2), _p(adv), cols, lda, _stream()))
+    return keep, g1, g2
 
 
 def splice_gemm_grouped(groups, N, K, k, ws=None):

@@ -157,3 +157,36 @@ def moe_counts(total: int = 4096, experts: int = 32, cap: int = 512, s: float = 
         excess -= take
     assert int(c.sum()) == total and c.max() <= cap
     return c
+
+
+CFG_TIM = 5
+TIM_BATCH, TIM_MAX_LEN = 512, 8192        # sequences per step, response limit (8k, Sec. 6.1)
+
+
+def rollout_logprobs(B: int = TIM_BATCH, L: int = TIM_MAX_LEN, seed: int = 0, tau: float = 1e-4):
+    """Per-token training-policy log-probabilities of a rollout batch, float32
+    [B, L], and response lengths int32 [B] (tokens past a length are padding).
+
+    Lengths are uniform in [1, L] with a few at the edges (1, 255, 256, 257, L).
+    Ordinary tokens have probabilities uniform in [1e-3, 1]; each sequence has
+    its own rate of sporadic tail tokens (probabilities in [1e-8, tau]):
+    most a low rate (1e-3), one in ten a high one (3e-2, widespread drift),
+    one in twenty a run of 3-20 consecutive tail tokens (a degenerate
+    stretch), and a few tokens sit exactly at log(tau)."""
+    g = np.random.Generator(np.random.PCG64(1000 * CFG_TIM + seed))
+    lens = g.integers(1, L + 1, B).astype(np.int32)
+    edge = [1, 255, 256, 257, L]
+    lens[: min(B, len(edge))] = edge[: min(B, len(edge))]
+    lp = np.log(g.uniform(1e-3, 1.0, (B, L))).astype(np.float32)
+    rate = np.where(g.random(B) < 0.1, 3e-2, 1e-3)
+    tail = g.random((B, L)) < rate[:, None]
+    runs = g.random(B) < 0.05
+    for i in np.nonzero(runs)[0]:
+        n = int(lens[i])
+        r = int(g.integers(3, 21))
+        s = int(g.integers(0, max(1, n - r + 1)))
+        tail[i, s: s + r] = True
+    lp[tail] = np.log(g.uniform(1e-8, tau, int(tail.sum()))).astype(np.float32)
+    at = g.random((B, L)) < 1e-4
+    lp[at] = np.float32(np.log(np.float32(tau)))
+    return lp, lens

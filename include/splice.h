@@ -234,6 +234,30 @@ int splice_gemm_grouped(const splice_group *groups, int32_t G, int64_t N, int64_
 size_t splice_grouped_workspace_size(const splice_group *groups, int32_t G, int64_t N,
                                      int64_t K, int32_t k);
 
+/* ---------------------------------------------------------------------------
+ * TIM-aware sequence filtering (Sec. 4.1 dual-gate mechanism, Eq. 3-4; the
+ * paper's settings, Sec. 6.1: tau = 1e-4, K1 = 0.01 x response length,
+ * K2 = 5).  For each of B sequences:
+ *   logp   float [B, ldl] (DEVICE): training-policy log-probabilities of the
+ *          sampled tokens; tokens t >= len[i] are padding and never read.
+ *   len    int32 [B] (DEVICE): response lengths; values outside [0, ldl] are
+ *          clamped to it.
+ *   A token is a tail token when logp <= log_tau (pi_train <= tau).
+ *   G1 = tail tokens, G2 = longest run of consecutive tail tokens; the
+ *   sequence is kept when G1 * k1_den < k1_num * len (K1 = k1_num/k1_den x
+ *   len, exact) and G2 < k2.  An empty response has G1 = 0 = K1 and is
+ *   therefore dropped, as Eq. 3 reads.
+ *   keep uint8 [B], g1 / g2 int32 [B] out (DEVICE, each may be NULL).
+ *   adv    float [B, adv_cols] in/out (DEVICE, row stride lda >= adv_cols, may
+ *          be NULL when adv_cols == 0): the rows of dropped sequences are set
+ *          to +0, the rest are untouched (Eq. 4; the caller keeps the loss
+ *          denominator G).
+ * B, ldl, k1_num and k1_den up to 2^31 - 1.  No workspace. */
+int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *len, float log_tau,
+                      int64_t k1_num, int64_t k1_den, int64_t k2, uint8_t *keep, int32_t *g1,
+                      int32_t *g2, float *adv, int64_t adv_cols, int64_t lda,
+                      splice_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

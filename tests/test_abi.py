@@ -194,3 +194,28 @@ def test_select_topk_argument_errors(L):
     assert f(FAKE, FAKE, FAKE, 10, 64, 8, V, None, FAKE, None) == splice.ERR_INVALID_ARG   # idx
     assert f(FAKE, FAKE + 4, FAKE, 10, 64, 8, V, FAKE, FAKE, None) == splice.ERR_INVALID_ARG
     assert f(None, None, None, 10, 0, 0, SM, None, None, None) == splice.OK                # K = 0
+
+
+def test_tim_filter_argument_errors(L):
+    f = L.splice_tim_filter
+    ok = (FAKE, 4, 64, FAKE, -9.0, 1, 100, 5, FAKE, FAKE, FAKE, FAKE, 1, 1, None)
+
+    def call(**over):
+        a = list(ok)
+        names = ["logp", "B", "ldl", "len", "tau", "k1n", "k1d", "k2", "keep", "g1", "g2", "adv",
+                 "cols", "lda", "s"]
+        for k, v in over.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(B=-1) == splice.ERR_INVALID_ARG
+    assert call(k1d=0) == splice.ERR_INVALID_ARG
+    assert call(k1n=-1) == splice.ERR_INVALID_ARG
+    assert call(k2=-1) == splice.ERR_INVALID_ARG
+    assert call(len=None) == splice.ERR_INVALID_ARG
+    assert call(logp=None) == splice.ERR_INVALID_ARG
+    assert call(adv=None) == splice.ERR_INVALID_ARG          # cols > 0 without adv
+    assert call(cols=8, lda=4) == splice.ERR_INVALID_ARG     # lda < cols
+    assert call(g1=FAKE + 2) == splice.ERR_INVALID_ARG
+    assert call(B=1 << 31) == splice.ERR_UNSUPPORTED
+    assert call(B=0) == splice.OK                            # nothing to do
