@@ -60,6 +60,8 @@ def parse():
                          "(the run that rocprofv3 --pmc passes profile)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"),
                     help="write the profiles/ summaries from rocprofv3 result databases")
+    ap.add_argument("--summarize-extras", metavar="TRACE_DB",
+                    help="write the profiles/ kernel-time summary of a full run (all extras)")
     return ap.parse_args()
 
 
@@ -80,6 +82,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.summarize_extras:
+        summarize_extras(args.summarize_extras)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -631,6 +636,31 @@ def summarize(trace_db, fetch_db, write_db):
            f"- algorithmic_bytes_per_launch: {float(np.mean(alg)):.0f}",
            f"- kernel_source_sha: {kernel_source_hash()}", ""]
     path = TRAFFIC_FILE
+    open(path, "w").write("\n".join(out) + "\n")
+    print("wrote", path)
+
+
+def summarize_extras(trace_db):
+    """Kernel times of a full bench run, per kernel and grid size (so the
+    decode, fused-decode, grouped, TIM-filter and preparation launches of each
+    shape appear on their own rows)."""
+    rows = _db_rows(trace_db, "select name, grid_x / workgroup_x, workgroup_x, count(*), avg(duration), "
+                              "sum(duration), min(duration), max(duration) from kernels "
+                              "group by name, grid_x, workgroup_x order by name, sum(duration) desc")
+    out = ["# Kernel times: full bench run, Qwen3-8B layer shapes (prefill, decode, fused decode, "
+           "grouped MoE, sweep, TIM filter)", "",
+           "Command (repo root, MI355X):", "",
+           "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof_extras -o run -- "
+           "python3 bench.py --steps 1 --warmup 1 --no-cpu",
+           "    python3 bench.py --summarize-extras gpurun_out/prof_extras/run_results.db", "",
+           "One row per kernel and launch shape (workgroups x threads per workgroup). Decode shapes "
+           "run under HIP-graph replay; durations are per dispatch.", "",
+           "| kernel | workgroups | threads | calls | avg us | total ms | min us | max us |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, wg, th, n, avg, tot, mn, mx in rows:
+        out.append(f"| `{name[:80]}` | {wg} | {th} | {n} | {avg / 1e3:.2f} | {tot / 1e6:.3f} | "
+                   f"{mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    path = os.path.join(ROOT, "profiles", "bench_extras_kernels_qwen3_8b.md")
     open(path, "w").write("\n".join(out) + "\n")
     print("wrote", path)
 
