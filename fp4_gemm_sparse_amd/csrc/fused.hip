@@ -85,17 +85,21 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
         xv[j] = *reinterpret_cast<const u32x4 *>(half_ptr(it < items ? it : 0));
     }
     const int32_t my_idx = (TAIL && tid < k) ? a.idx[tid] : -1;
-    // W_S rows for k = 32 or 64 (wave j < CB finishes column block j):
-    // needed last, issued before the weights for the same reason
-    bf16x8 ta[2], tb[2];
+    // W_S tile for k = 32 or 64 (CB*16 rows x k): SWD dwords per thread,
+    // spread over every thread so that all waves issue the same loads (the
+    // compiler can then wait for the weights chunk by chunk); it reaches the
+    // waves that finish the column blocks through LDS.  Needed last, issued
+    // before the weights for the same reason as X.
     const bool side_pre = TAIL && (k == 32 || k == 64);
-    if (side_pre && wave < CB) {
-        const int64_t n = n0 + wave * 16 + rr;
-        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
+    const int kd = k / 2;                                   // dwords per side row
+    constexpr int SWD = (CB * 16 * 32 + NT - 1) / NT;
+    unsigned swv[SWD];
+    if (side_pre) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int hh = (h * 32 < k) ? h : 0;
-            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
+        for (int u = 0; u < SWD; u++) {
+            const int e = tid + u * NT;
+            const int64_t n = n0 + min(e / kd, CB * 16 - 1);
+            swv[u] = *reinterpret_cast<const unsigned *>(a.W_S + (n < N ? n : 0) * k + (e % kd) * 2);
         }
     }
     __builtin_amdgcn_sched_barrier(0);     // keep these loads ahead of the weight loads
@@ -156,16 +160,21 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
         for (int64_t it = tid + (int64_t)XPT * NT; it < items; it += NT)
             prep(*reinterpret_cast<const u32x4 *>(half_ptr(it)), it);
     }
-    // X_S of the waves that finish a column block (k = 32 or 64), gathered
-    // from X; only needed after the main loop
-    if (side_pre && wave < CB) {
-        const int64_t mrow = rr;
-        const uint16_t *xr = a.X + (mrow < M ? mrow : 0) * a.ldx;
+    // the side tiles' LDS home, after the reduction space: W_S [CB*16][kd]
+    // dwords, then X_S [M][k] bf16
+    uint32_t *sbuf = reinterpret_cast<uint32_t *>(xl + red_off + NW * CB * WAVE * 16);
+    uint16_t *sxb = reinterpret_cast<uint16_t *>(sbuf + CB * 16 * kd);
+    unsigned short xsv = 0;
+    if (side_pre) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int hh = (h * 32 < k) ? h : 0;
-            ta[h] = gather_side8(xr, sidx + hh * 32 + g * 8, 8, K);
-        }
+        for (int u = 0; u < SWD; u++)
+            if (tid + u * NT < CB * 16 * kd) sbuf[tid + u * NT] = swv[u];
+        // one element of X_S per thread, gathered from X through idx: issued
+        // behind the weights but by every wave alike, and kept in a register
+        // until the main loop is done
+        const int e = min(tid, (int)M * k - 1);
+        const int64_t c = sidx[e % k];
+        xsv = a.X[(e / k) * a.ldx + (c >= 0 && c < K ? c : 0)];
     }
     __syncthreads();
 
@@ -196,31 +205,44 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
     f32x4 *red = reinterpret_cast<f32x4 *>(xl + red_off);
 #pragma unroll
     for (int j = 0; j < CB; j++) red[(wave * CB + j) * WAVE + lane] = acc[j];
+    if (side_pre && tid < M * k) sxb[tid] = xsv;
     __syncthreads();
     if (wave < CB) {
         const int j = wave;
         f32x4 v = red[j * WAVE + lane];
 #pragma unroll
         for (int w = 1; w < NW; w++) v += red[(w * CB + j) * WAVE + lane];
-        v *= (*a.alpha_x) * (*a.alpha_w);
+        const float alpha = (*a.alpha_x) * (*a.alpha_w);
         const int64_t n = n0 + j * 16 + rr;
-        if (TAIL) {
-            if (side_pre) {
-                const bf16x8 z = {};
-                const bool okm = rr < M, okn = n < N;
-                v = mfma_bf16(okm ? ta[0] : z, okn ? tb[0] : z, v);
-                if (k == 64) v = mfma_bf16(okm ? ta[1] : z, okn ? tb[1] : z, v);
-            } else {
-                const bool al = (k % 8) == 0;
-                const int64_t mrow = rr;
-                const uint16_t *xr = a.X + (mrow < M ? mrow : 0) * a.ldx;
-                for (int kk = 0; kk < k; kk += 32) {
-                    const int cc = kk + g * 8;
-                    const int valid = max(0, min(8, k - cc));
-                    const bf16x8 af = gather_side8(xr, a.idx + cc, (mrow < M) ? valid : 0, K);
-                    const bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
-                    v = mfma_bf16(af, bf, v);
-                }
+        if (side_pre) {
+            // the side product from zero, then Y = fma(alpha, acc, side): the
+            // two-call kernel's arithmetic.  Lane (g, rr): row rr, channels
+            // 32h + 8g .. +8
+            const bf16x8 z = {};
+            const bool okm = rr < M, okn = n < N;
+            const uint32_t *wrow = sbuf + (j * 16 + rr) * kd;
+            const uint16_t *xrow = sxb + (okm ? rr : 0) * k;
+            f32x4 side = {0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < k / 32; h++) {
+                const bf16x8 ta = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xrow + 32 * h + 8 * g));
+                const bf16x8 tb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wrow + 16 * h + 4 * g));
+                side = mfma_bf16(okm ? ta : z, okn ? tb : z, side);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++) v[q] = __builtin_fmaf(alpha, v[q], side[q]);
+        } else {
+            v *= alpha;
+        }
+        if (TAIL && !side_pre) {          // other k: gathered and direct loads, masked
+            const bool al = (k % 8) == 0;
+            const int64_t mrow = rr;
+            const uint16_t *xr = a.X + (mrow < M ? mrow : 0) * a.ldx;
+            for (int kk = 0; kk < k; kk += 32) {
+                const int cc = kk + g * 8;
+                const int valid = max(0, min(8, k - cc));
+                const bf16x8 af = gather_side8(xr, a.idx + cc, (mrow < M) ? valid : 0, K);
+                const bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                v = mfma_bf16(af, bf, v);
             }
         }
         if (n < N)
@@ -236,9 +258,10 @@ template <int NW, int CPW, int CB, int XPT>
 static hipError_t run_fused_x(const GemmArgs &a, hipStream_t s)
 {
     constexpr int red_bytes = NW * CB * WAVE * 16;
-    constexpr int lds_max = 4 * (NW * CPW * FBK) * 2 + red_bytes;    // largest M and K of the form
+    constexpr int side_bytes = (CB * 16 + 4) * 128;                  // W_S and X_S tiles, k <= 64
+    constexpr int lds_max = 4 * (NW * CPW * FBK) * 2 + red_bytes + side_bytes;   // largest M and K
     static_assert(lds_max <= F_LDS, "fused decode LDS budget");
-    const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + red_bytes;
+    const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + red_bytes + (a.k > 0 ? side_bytes : 0);
     const dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
     if (a.k > 0) {
         static const hipError_t attr = hipFuncSetAttribute(

@@ -766,22 +766,21 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     const int64_t it0 = tid < M * nbx ? tid : 0;
     const u32x2 xc0 = *reinterpret_cast<const u32x2 *>(a.Xq + (it0 / nbx) * rowb + (it0 % nbx) * 8);
     const unsigned xs0 = a.Xs[(it0 / nbx) * rows + it0 % nbx];
-    // side operands for k = 32 or 64 (wave 0 finishes the block): needed
-    // last, issued before the weights so that no wait for them is a wait
-    // for the weight stream
-    bf16x8 ta[2], tb[2];
+    // side operands for k = 32 or 64: one dword of the W_S tile (16 rows x k)
+    // and one of X_S (M rows x k) per thread, so that every wave issues the
+    // same loads (the compiler can then count each wave's outstanding loads
+    // exactly and wait for the weights chunk by chunk); they reach wave 0,
+    // which finishes the block, through LDS.  Needed last, issued before the
+    // weights so that no wait for them is a wait for the weight stream.
     const int k = a.k;
     const bool side_pre = TAIL && (k == 32 || k == 64);
-    if (side_pre && wave == 0) {
-        const int64_t mrow = rr, n = n0 + rr;
-        const uint16_t *xa = a.X_S + (mrow < M ? mrow : 0) * k + g * 8;
-        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int hh = (h * 32 < k) ? h : 0;
-            ta[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + hh * 32));
-            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
-        }
+    const int kd = k / 2;                               // dwords per side row
+    unsigned sw = 0, sx = 0;
+    if (side_pre) {
+        const int64_t wr = min(tid / kd, 15), xr = min((int64_t)(tid / kd), M - 1);
+        const int64_t n = n0 + wr;
+        sw = *reinterpret_cast<const unsigned *>(a.W_S + (n < N ? n : 0) * k + (tid % kd) * 2);
+        sx = *reinterpret_cast<const unsigned *>(a.X_S + xr * k + (tid % kd) * 2);
     }
     __builtin_amdgcn_sched_barrier(0);     // keep these loads ahead of the weight loads
 
@@ -796,15 +795,15 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
         const int64_t nn = n < N ? n : 0;
         const uint8_t *pw = a.Wq + nn * rowb + g * 16;
         const uint8_t *ps = a.Ws + nn * rows;
+        // in the order of use: each scale pair just ahead of its two chunks
 #pragma unroll
         for (int c = 0; c < CPW; c++) {
+            if (c % 2 == 0) {
+                const int64_t cs = min(c0 + c, nchunk - 2);
+                wsv[c / 2] = *reinterpret_cast<const u32x4 *>(ps + cs * SCALE_ROW);
+            }
             const int64_t ci = min(c0 + c, nchunk - 1);
             wc[c] = *reinterpret_cast<const u32x4 *>(pw + ci * CODE_ROW);
-        }
-#pragma unroll
-        for (int c = 0; c < CPW / 2; c++) {
-            const int64_t ci = min(c0 + 2 * c, nchunk - 2);
-            wsv[c] = *reinterpret_cast<const u32x4 *>(ps + ci * SCALE_ROW);
         }
     }
     // decode the M activation rows into LDS: one 16-channel block per item
@@ -819,7 +818,30 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
             dst[1] = decode8(c.y, sc);
         }
     }
+    // side tiles after the reduction space: W_S [16][kd] dwords, then X_S [M][kd]
+    const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
+    uint32_t *sbuf = reinterpret_cast<uint32_t *>(xl + red_off + NW * WAVE * 16);
+    if (side_pre) {
+        if (tid < 16 * kd) sbuf[tid] = sw;
+        if (tid < M * kd) sbuf[16 * kd + tid] = sx;
+    }
     __syncthreads();
+
+    // the BF16 side product of the block (k = 32 or 64), by wave 0 before
+    // its chunks, while the weights are still arriving; lane (g, rr) holds
+    // row rr, channels 32h + 8g .. +8
+    f32x4 side = {0.f, 0.f, 0.f, 0.f};
+    if (side_pre && wave == 0) {
+        const bf16x8 z = {};
+        const bool okm = rr < M, okn = n0 + rr < N;
+        const uint32_t *wrow = sbuf + rr * kd;
+        const uint32_t *xrow = sbuf + 16 * kd + (okm ? rr : 0) * kd;
+        for (int h = 0; h < k / 32; h++) {
+            const bf16x8 ta = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xrow + 16 * h + 4 * g));
+            const bf16x8 tb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wrow + 16 * h + 4 * g));
+            side = mfma_bf16(okm ? ta : z, okn ? tb : z, side);
+        }
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const bool xrow = rr < M;
@@ -845,31 +867,30 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     }
 
     // wave-order reduction through LDS (reuses the space after the activations)
-    f32x4 *red = reinterpret_cast<f32x4 *>(xl + ((M * K * 2 + 15) & ~(int64_t)15));
+    f32x4 *red = reinterpret_cast<f32x4 *>(xl + red_off);
     red[wave * WAVE + lane] = acc;
     __syncthreads();
     if (wave == 0) {
         f32x4 v = red[lane];
 #pragma unroll
         for (int w = 1; w < NW; w++) v += red[w * WAVE + lane];
-        v *= (*a.alpha_x) * (*a.alpha_w);
+        const float alpha = (*a.alpha_x) * (*a.alpha_w);
         const int64_t n = n0 + rr;
-        if (TAIL) {
-            if (side_pre) {
-                const bf16x8 z = {};
-                const bool okm = rr < M, okn = n < N;
-                v = mfma_bf16(okm ? ta[0] : z, okn ? tb[0] : z, v);
-                if (k == 64) v = mfma_bf16(okm ? ta[1] : z, okn ? tb[1] : z, v);
-            } else {
-                const bool al = (k % 8) == 0;
-                const int64_t mrow = rr;
-                for (int kk = 0; kk < k; kk += 32) {
-                    const int cc = kk + g * 8;
-                    const int valid = max(0, min(8, k - cc));
-                    bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
-                    bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
-                    v = mfma_bf16(af, bf, v);
-                }
+        if (side_pre) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) v[q] = __builtin_fmaf(alpha, v[q], side[q]);
+        } else {
+            v *= alpha;
+        }
+        if (TAIL && !side_pre) {          // other k: direct loads, masked
+            const bool al = (k % 8) == 0;
+            const int64_t mrow = rr;
+            for (int kk = 0; kk < k; kk += 32) {
+                const int cc = kk + g * 8;
+                const int valid = max(0, min(8, k - cc));
+                bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
+                bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                v = mfma_bf16(af, bf, v);
             }
         }
         if (n < N)
@@ -884,18 +905,20 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
 template <int NW, int CPW>
 static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
 {
-    const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16;
+    // activations, reduction space, side tiles (k <= 64: (16 + M) rows of 128 bytes)
+    const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16 +
+                       (a.k > 0 ? (size_t)(16 + a.M) * 128 : 0);
     dim3 grid((unsigned)((a.N + 15) / 16));
     if (a.k > 0) {
         static const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
+            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16 + 20 * 128);
         if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, true>), grid, dim3(64 * NW), lds, s, a);
     } else {
         static const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16);
+            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16 + 20 * 128);
         if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, false>), grid, dim3(64 * NW), lds, s, a);
     }
