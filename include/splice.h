@@ -70,7 +70,8 @@ typedef enum {
 enum { SPLICE_PATH_AUTO = 0, SPLICE_PATH_DECODE = 1, SPLICE_PATH_PREFILL = 2 };
 
 /* Largest M the automatic dispatch sends to the decode (weight-streaming)
- * path.  The paper switches at 32 tokens (Sec. 5.1); this build uses 64. */
+ * path.  The paper switches at 32 tokens (Sec. 5.1); the decode kernels here
+ * take up to 64 rows. */
 #define SPLICE_DECODE_MAX_M 64
 
 /* Human-readable name of a status code (static string). */
