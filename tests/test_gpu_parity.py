@@ -411,6 +411,33 @@ def test_grouped_many_ragged_groups(k):
             assert_gemm_close(host(groups[e]["Y"]), refs[e], f"group {e} M={int(Ms[e])}")
 
 
+def test_grouped_many_small_groups():
+    """36 groups of 1..64 rows (more than one launch's worth of groups, each a
+    single padded row tile), a ragged N and a side width that is not a
+    multiple of 8, each group against the oracle."""
+    K, N, G, k = 512, 100, 36, 12
+    g = np.random.default_rng(31)
+    Ms = np.concatenate([g.integers(1, 33, 33), g.integers(33, 65, 3)])
+    groups, refs = [], []
+    for e in range(G):
+        Me = int(Ms[e])
+        Xw = synth.activations(9, e % 4, 128, K, 5 + 10 * e, "student", n_out=8)
+        X = synth.activations(9, e % 4, Me, K, 6 + 10 * e, "student", n_out=8)
+        W = synth.weights(9, 90 + e, N, K)
+        Xwd, Xd, Wd = dev(Xw), dev(X), dev(W)
+        idx, ax, _ = S.select_channels(Xwd, k)
+        aw = S.compute_alpha(Wd, idx)
+        gx, gw = S.quantize_nvfp4(Xd, idx, ax), S.quantize_nvfp4(Wd, idx, aw)
+        Y = torch.full((Me, N), float("nan"), device="cuda")
+        groups.append(dict(Xq=gx[0], Xs=gx[1], alpha_x=ax, X_S=gx[2], Wq=gw[0], Ws=gw[1], alpha_w=aw,
+                           W_S=gw[2], Y=Y))
+        refs.append(oracle_pipeline(Xw, X, W, k)["Y"])
+    S.splice_gemm_grouped(groups, N, K, k)
+    torch.cuda.synchronize()
+    for e in range(G):
+        assert_gemm_close(host(groups[e]["Y"]), refs[e], f"group {e} M={int(Ms[e])}")
+
+
 @pytest.mark.parametrize("M", synth.SWEEP_MS)
 @pytest.mark.parametrize("case", ["k0", "top64", "top128", "top256", "rand64"])
 def test_sweep_sampled(M, case):
