@@ -245,7 +245,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
 {
     __shared__ unsigned hist[256];
     __shared__ uint64_t s_prefix;
-    __shared__ int64_t s_need;
+    __shared__ int64_t s_need, s_bin;
     __shared__ int64_t s_wtot[2 * SEL_WAVES];
     __shared__ float s_max[SEL_WAVES];
     const int tid = threadIdx.x, lane = tid % WAVE;
@@ -255,11 +255,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
     KeySource<PER> keys;
     keys.init(rv, c0, c1);
 
-    uint64_t thr = 0;       // key of the k-th largest channel
-    int64_t need = 0;       // how many channels with key == thr are taken
+    uint64_t thr = 0;       // key bits (under pmask) of the k-th largest channel
+    uint64_t pmask = 0;     // the key bits decided so far
+    int64_t need = 0;       // how many channels whose key matches thr under pmask are taken
     if (k > 0) {
-        uint64_t prefix = 0, pmask = 0;
+        uint64_t prefix = 0;
         int64_t remaining = k;
+        // radix passes from the top byte down; they stop early once the bin
+        // that holds the k-th key holds exactly the keys still needed (all
+        // of them are then taken, whatever their lower bits)
         for (int shift = 56; shift >= 0; shift -= 8) {
             if (tid < 256) hist[tid] = 0;
             __syncthreads();
@@ -290,6 +294,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
                     if (before < remaining && before + (int64_t)h[q] >= remaining) {
                         s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << shift);
                         s_need = remaining - before;
+                        s_bin = (int64_t)h[q];
                     }
                     before += h[q];
                 }
@@ -297,8 +302,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
             __syncthreads();
             prefix = s_prefix;
             remaining = s_need;
+            const bool whole_bin = s_bin == remaining;
             pmask |= (uint64_t)255 << shift;
             __syncthreads();
+            if (whole_bin) break;                      // uniform: read from LDS by every thread
         }
         thr = prefix;
         need = remaining;
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
 
     int64_t my_eq = 0;
     if (k > 0)
-        for (int i = 0; i < n; i++) my_eq += (keys(i) == thr);
+        for (int i = 0; i < n; i++) my_eq += ((keys(i) & pmask) == thr);
     const int64_t eq_before = block_exclusive_scan(my_eq, s_wtot);
 
     int64_t my_sel = 0;
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
         int64_t e = eq_before;
         if (k > 0)
             for (int i = 0; i < n; i++) {
-                const uint64_t key = keys(i);
+                const uint64_t key = keys(i) & pmask;
                 const bool eq = key == thr;
                 my_sel += (key > thr) || (eq && e < need);
                 e += eq;
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(RankValue rv,
         for (int i = 0; i < n; i++) {
             bool sel = false;
             if (k > 0) {
-                const uint64_t key = keys(i);
+                const uint64_t key = keys(i) & pmask;
                 const bool eq = key == thr;
                 sel = (key > thr) || (eq && e < need);
                 e += eq;
