@@ -20,14 +20,15 @@ namespace splice {
 // Channel statistics: Welford over 64-row tiles, tiles folded left to right
 // with the pairwise update of Chan, Golub & LeVeque, then merged into the
 // running moments.  One workgroup owns 64 channels (one per lane).  Its eight
-// waves each take one tile of a round of eight: a wave issues the loads of 16
-// rows before it starts their (serial) Welford steps, parks the tile moments
+// waves each take one tile of a round of eight: a wave issues the loads of
+// all 64 rows of its tile (one round trip) before it starts their (serial)
+// Welford steps, parks the tile moments
 // in LDS, and wave 0 folds the round in tile order, so the result does not
 // depend on scheduling.
 // ===========================================================================
 constexpr int ST_TILE = 64;
 constexpr int ST_WAVES = 8;    // tiles per fold round, one per wave
-constexpr int ST_BATCH = 16;   // rows loaded ahead of their Welford steps
+constexpr int ST_BATCH = 64;   // rows loaded ahead of their Welford steps (a whole tile)
 
 struct Moments { double n, mean, m2; };
 
