@@ -199,6 +199,20 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                 "traffic": traffic}
+    # the FP16 matrix-core rate this GPU sustains (independent back-to-back
+    # 32x32x16 MFMAs, two waves per SIMD), as context for the published peak
+    wgs = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(wgs * 4, dtype=torch.float32, device=dev)
+    S.probe_mfma_f16(64, wgs, sink)
+    pi = 4096
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    S.probe_mfma_f16(pi, wgs, sink)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    mfma_measured = wgs * 4 * 4 * pi * 32 * 32 * 16 * 2 / (p0.elapsed_time(p1) * 1e-3) / 1e12
+    log(f"measured FP16 MFMA rate {mfma_measured:.0f} TFLOP/s; prefill GEMM at "
+        f"{achieved / mfma_measured:.3f} of it")
 
     result = {
         "metric": "SpliceGEMM prefill TFLOP/s & decode HBM GB/s; % overhead vs plain NVFP4 GEMM",
@@ -211,6 +225,10 @@ def main():
                    "step": "per distinct layer input (q/k/v share one, gate/up share one): stats+select "
                            "and activation prep; per projection: weight alpha+pre-split and SpliceGEMM"},
         "roofline": roofline,
+        "mfma_f16_measured": {"tflops": round(mfma_measured, 1),
+                              "gemm_frac": round(achieved / mfma_measured, 4),
+                              "probe": "4 independent v_mfma_f32_32x32x16_f16 chains per wave, "
+                                       "two waves per SIMD, register operands"},
     }
 
     if not args.no_extra:

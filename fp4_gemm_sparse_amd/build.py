@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsplice.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "fused.hip", "tim.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "fused.hip", "tim.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

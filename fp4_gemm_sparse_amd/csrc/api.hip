@@ -250,6 +250,13 @@ int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *
     return hip_status(launch_tim_filter(a, hs(stream)));
 }
 
+int splice_probe_mfma_f16(int64_t iters, int64_t workgroups, float *sink, splice_stream_t stream)
+{
+    if (iters < 0 || workgroups <= 0 || workgroups > 65536 || !sink || !aligned(sink, 4))
+        return SPLICE_ERR_INVALID_ARG;
+    return hip_status(launch_mfma_rate(iters, workgroups, sink, hs(stream)));
+}
+
 size_t splice_grouped_workspace_size(const splice_group *, int32_t, int64_t, int64_t, int32_t)
 {
     return 0;

@@ -66,4 +66,7 @@ struct TimArgs {
 };
 hipError_t launch_tim_filter(const TimArgs &a, hipStream_t s);
 
+// measurement aid: `workgroups` x 4 waves, each 4 * iters 32x32x16 FP16 MFMAs
+hipError_t launch_mfma_rate(int64_t iters, int64_t workgroups, float *sink, hipStream_t s);
+
 }  // namespace splice

@@ -63,6 +63,7 @@ _SIGS = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
                                   _sz, ctypes.c_int, _vp]),
     "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "splice_probe_mfma_f16": (ctypes.c_int, [_i64, _i64, _vp, _vp]),
     "splice_tim_filter": (ctypes.c_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _i64, _i64, _i64, _vp,
                                          _vp, _vp, _vp, _i64, _i64, _vp]),
     "splice_gemm_decode_fused": (ctypes.c_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
@@ -300,6 +301,12 @@ def tim_filter(logp, lengths, log_tau, k1=(1, 100), k2=5, adv=None, out=None):
            lib().splice_tim_filter(_p(logp), B, logp.stride(0), _p(lengths), float(log_tau), k1[0], k1[1],
                                    k2, _p(keep), _p(g1), _p(g2), _p(adv), cols, lda, _stream()))
     return keep, g1, g2
+
+
+def probe_mfma_f16(iters, workgroups, sink):
+    """Measurement aid: 4 * iters 32x32x16 FP16 MFMAs per wave, 4 waves per
+    workgroup (sink float32 [workgroups * 4])."""
+    _check("splice_probe_mfma_f16", lib().splice_probe_mfma_f16(iters, workgroups, _p(sink), _stream()))
 
 
 def splice_gemm_grouped(groups, N, K, k, ws=None):

@@ -259,6 +259,15 @@ int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *
                       int32_t *g2, float *adv, int64_t adv_cols, int64_t lda,
                       splice_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid, not part of the SpliceGEMM path: `workgroups` workgroups
+ * of 4 waves each issue 4 * iters independent v_mfma_f32_32x32x16_f16 (the
+ * prefill tile's instruction) on register operands, 32*32*16*2 flops each;
+ * timing the call gives the FP16 matrix-core rate the GPU sustains at its
+ * clock under that load.  sink: float [workgroups * 4] out (DEVICE).
+ * 2 * (number of CUs) workgroups put two waves on every SIMD. */
+int splice_probe_mfma_f16(int64_t iters, int64_t workgroups, float *sink, splice_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
