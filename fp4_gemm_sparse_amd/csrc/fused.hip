@@ -5,10 +5,10 @@
 //
 // For M <= 4 token rows.  A workgroup owns 16*CB output channels and the
 // whole K; wave w multiplies K chunks (128 channels) w*CPW .. w*CPW+CPW-1.
-//  1. Every independent global load is issued first, the thread's half
-//     blocks of X and its idx entry ahead of the wave's weight codes and
-//     scales: loads complete in issue order, so the preparation can start
-//     while the weights are still on their way.
+//  1. Every independent global load is issued first: the thread's half
+//     blocks of X, its idx entry and its share of the W_S tile ahead of the
+//     wave's weight codes and scales.  Loads complete in issue order, so the
+//     preparation can start while the weights are still on their way.
 //  2. The protected-channel mask is built in LDS from idx.
 //  3. Each 16-channel block of the M rows is masked, quantized by two lanes
 //     (eight elements each) with the scale, key and code functions of
@@ -17,8 +17,10 @@
 //     codes.
 //  4. Each wave multiplies its chunks on v_mfma_f32_16x16x32_f16 (A from the
 //     LDS copy, B decoded from registers); partial sums meet in LDS in wave
-//     order, are scaled by alpha_x*alpha_w and completed with the BF16 side
-//     product of X_S (gathered from X through idx) and W_S.
+//     order.  The waves that finish a column block add the BF16 side product
+//     of X_S (gathered from X through idx) and W_S, both brought in by every
+//     thread alike and passed on through LDS: Y = fma(alpha_x*alpha_w, acc,
+//     side), as in the two-call kernel.
 // With the same wave configuration as the two-call decode kernel for few
 // rows, the chunk split, the MFMA order and the reduction order are the same,
 // and Y is bit-identical to it.  Every workgroup repeats the preparation of the
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
 {
     // [M][K] FP16 activations, then [NW][CB][64] f32x4 partial sums (the
     // protected-channel mask, and idx when k <= 64, use that space until the
-    // main loop).  XPT: half blocks of X per thread loaded up front.
+    // main loop), then the W_S and X_S tiles.  XPT: half blocks of X per
+    // thread loaded up front.
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     constexpr int NT = 64 * NW;
     const int tid = threadIdx.x, lane = tid % WAVE;

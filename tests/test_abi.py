@@ -219,3 +219,11 @@ def test_tim_filter_argument_errors(L):
     assert call(g1=FAKE + 2) == splice.ERR_INVALID_ARG
     assert call(B=1 << 31) == splice.ERR_UNSUPPORTED
     assert call(B=0) == splice.OK                            # nothing to do
+
+
+def test_probe_argument_errors(L):
+    f = L.splice_probe_mfma_f16
+    assert f(-1, 8, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(16, 0, FAKE, None) == splice.ERR_INVALID_ARG
+    assert f(16, 8, None, None) == splice.ERR_INVALID_ARG
+    assert f(16, 8, FAKE + 2, None) == splice.ERR_INVALID_ARG
