@@ -967,7 +967,7 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
         return a.k > 0 ? launch_prefill_lds128<true>(a, s) : launch_prefill_lds128<false>(a, s);
     }
     // weight-streaming decode path; configurations chosen from measured sweeps
-    // on MI355X (Qwen3-8B projection shapes, M = 1, 8, 32, 64)
+    // on MI355X (Qwen3-8B projection shapes, M = 1, 4, 8, 16, 32, 64)
     hipError_t e = hipSuccess;
     const int nchunk = (int)(a.K / BK);
     const int64_t colblocks = (a.N + 15) / 16;
@@ -978,21 +978,23 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
             if (nchunk <= 16 * 6) return run_decode_xlds<16, 6>(a, s);
             if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, s);
         }
-        if (colblocks >= 512 && run_decode3_k<1, 3, 4, 8>(a, s, e)) return e;
-        if (run_decode3_k<1, 1, 8, 16>(a, s, e)) return e;
-        return run_decode2<1, 1, 8, 2>(a, s);
+        // wide N: 48 columns per workgroup, streaming one chunk at a time
+        // (N = 12288: 6-9% faster than the single-round form at M = 8-16);
+        // K up to 4096: single round, eight waves of four chunks; longer K:
+        // streaming, 16 columns per workgroup (K = 12288: 25% faster than the
+        // single round at M = 4-16, whose sixteen waves hold six chunks each)
+        if (colblocks >= 512) return run_decode2<1, 3, 8, 1>(a, s);
+        if (nchunk <= 32) return run_decode3<1, 1, 8, 4>(a, s);
+        return run_decode2<1, 1, 8, 1>(a, s);
     }
-    // M in 17..64: wide N takes the single-round form with 48 columns per
-    // workgroup (one workgroup per CU at N = 12288); otherwise the looping
-    // form with 16 columns per workgroup and 8 waves over K
+    // M in 17..64: wide N at M <= 32 takes the single-round form with 48
+    // columns per workgroup (one workgroup per CU at N = 12288); otherwise
+    // the streaming form over 8 waves
     if (a.M <= 32) {
         if (colblocks >= 512 && run_decode3_k<2, 3, 4, 8>(a, s, e)) return e;
-        return run_decode2<2, 1, 8, 2>(a, s);
+        return run_decode2<2, 1, 8, 1>(a, s);
     }
-    if (colblocks >= 512) {
-        if (run_decode3_k<4, 3, 4, 8>(a, s, e)) return e;
-        return run_decode2<4, 3, 8, 1>(a, s);
-    }
+    if (colblocks >= 512) return run_decode2<4, 3, 8, 1>(a, s);
     return run_decode2<4, 1, 8, 2>(a, s);
 }
 
