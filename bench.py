@@ -274,7 +274,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     dev = torch.device("cuda:0")
     out = {}
     # ---------------- prefill overhead vs the plain NVFP4 GEMM on identical bf16 inputs
-    nv_ms, sp_ms, nv_full_ms, sp_full_ms = {}, {}, {}, {}
+    nv_ms, sp_ms, nv_full_ms, sp_full_ms, lib_ms = {}, {}, {}, {}, {}
     empty = torch.zeros(0, dtype=torch.int32, device=dev)
     for n in names:
         p = P[n]
@@ -300,6 +300,13 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             S.quantize_nvfp4(p["X"], p["idx"], p["ax"], out=p["xpack"]),
             S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])), 10)
         del xq0, wq0, Y0
+        # context: the vendor library's dense 16-bit GEMM on the same shapes
+        x16 = p["X"].view(torch.bfloat16).to(torch.float16)
+        w16 = p["W"].view(torch.bfloat16).to(torch.float16)
+        for _ in range(3):
+            torch.matmul(x16, w16.t())
+        lib_ms[n] = timed(torch, stream, lambda i: torch.matmul(x16, w16.t()), 10)
+        del x16, w16
     tot_sp, tot_nv = sum(sp_ms.values()), sum(nv_ms.values())
     out["prefill"] = {
         "timing": "each GEMM back to back on resident inputs (HIP events); gemm_ms_in_step are the "
@@ -312,6 +319,12 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         "gemm_ms": {n: round(v, 4) for n, v in sp_ms.items()},
         "gemm_ms_in_step": {n: round(v, 4) for n, v in gemm_ms.items()},
         "nvfp4_ms": {n: round(v, 4) for n, v in nv_ms.items()},
+        "library_fp16_dense": {
+            "note": "context only: torch.matmul FP16 x FP16 -> FP16 (hipBLASLt) on the same shapes; "
+                    "16-bit operands read as they are, no decode, half the output bytes",
+            "tflops": round(sum(flops.values()) / (sum(lib_ms.values()) * 1e-3) / 1e12, 2),
+            "ms": {n: round(v, 4) for n, v in lib_ms.items()},
+        },
     }
     log("prefill", out["prefill"])
 

@@ -260,7 +260,9 @@ SHAPES = [(1, 16, 128, 0), (1, 100, 1024, 5), (8, 48, 256, 64), (16, 1000, 1024,
           (17, 64, 512, 31), (32, 1024, 1024, 1), (33, 80, 256, 64), (63, 130, 384, 64),
           (64, 1024, 2048, 256), (65, 96, 256, 64), (128, 128, 1024, 0), (130, 1040, 1024, 64),
           (200, 300, 640, 100), (257, 257, 128, 128),
-          (5, 40, 17408, 16), (40, 24, 8192, 64), (3, 48, 384, 64), (16, 272, 256, 32)]
+          (5, 40, 17408, 16), (40, 24, 8192, 64), (3, 48, 384, 64), (16, 272, 256, 32),
+          # wide N with a ragged last 48-column block on the streaming decode forms
+          (2, 8200, 384, 64), (8, 8200, 256, 64), (12, 8200, 4608, 16), (40, 8200, 384, 32)]
 
 
 @pytest.mark.parametrize("M,N,K,k", SHAPES)
