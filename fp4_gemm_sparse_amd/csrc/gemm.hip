@@ -532,6 +532,27 @@ __global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
 
     int c = wave;
     if (c < nchunk) load(c, wc0, ws0, xc0, xs0);
+    // W_S fragments (k = 32 or 64) of the tile this wave finishes, issued by
+    // every wave alike right behind its first batch: the waits for later
+    // batches, younger loads, include them, and by then they have arrived.
+    // (Loaded in the epilogue, their HBM latency would add to the call's
+    // tail.)  X_S, a few KB that every workgroup reads, comes from L2 in the
+    // epilogue.  Only where each wave finishes at most one tile, in one
+    // round: two would hold 8 more registers than the widest form can spare.
+    constexpr int TPW = (C::T + NW - 1) / NW;
+    const int k = a.k;
+    const bool side_pre = TAIL && TPW == 1 && C::RED_TILES == C::T && (k == 32 || k == 64);
+    bf16x8 tb[2];
+    if (side_pre) {
+        const int t = min(wave, C::T - 1);
+        const int64_t n = n0 + (t % CB) * 16 + rr;
+        const uint16_t *wb = a.W_S + (n < N ? n : 0) * k + g * 8;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int hh = (h * 32 < k) ? h : 0;              // k = 32: second half re-reads the first
+            tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
+        }
+    }
     while (c < nchunk) {
         const int c1 = c + BB * NW;
         if (c1 < nchunk) load(c1, wc1, ws1, xc1, xs1);
@@ -559,10 +580,19 @@ __global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
             for (int w = 1; w < NW; w++) v += red[w][t][lane];
             v *= alpha;
             const int64_t n = n0 + j * 16 + rr;
-            if (TAIL) {
-                const int k = a.k;
+            const int64_t mrow = i * 16 + rr;
+            if (side_pre) {                // one round, one tile per wave: t == wave
+                const bf16x8 z = {};
+                const bool okm = mrow < M, okn = n < N;
+                const uint16_t *xa = a.X_S + (okm ? mrow : 0) * k + g * 8;
+                const bf16x8 ta0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa));
+                v = mfma_bf16(okm ? ta0 : z, okn ? tb[0] : z, v);
+                if (k == 64) {
+                    const bf16x8 ta1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + 32));
+                    v = mfma_bf16(okm ? ta1 : z, okn ? tb[1] : z, v);
+                }
+            } else if (TAIL) {
                 const bool al = (k % 8) == 0;
-                const int64_t mrow = i * 16 + rr;
                 for (int kk = 0; kk < k; kk += 32) {
                     const int cc = kk + g * 8;
                     const int valid = max(0, min(8, k - cc));
@@ -747,7 +777,9 @@ __global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
 // ---------------------------------------------------------------------------
 constexpr int XLDS_MAX = 64 * 1024;        // bytes of FP16 activations kept in LDS
 
-template <int NW, int CPW, bool TAIL>
+// SIDE: 0 for k = 0; 1 for k = 32 or 64 (side tiles staged through LDS);
+// 2 for any other k (side operands loaded in the epilogue).
+template <int NW, int CPW, int SIDE>
 __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [M][K] f16, then reduction space
@@ -766,22 +798,6 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     const int64_t it0 = tid < M * nbx ? tid : 0;
     const u32x2 xc0 = *reinterpret_cast<const u32x2 *>(a.Xq + (it0 / nbx) * rowb + (it0 % nbx) * 8);
     const unsigned xs0 = a.Xs[(it0 / nbx) * rows + it0 % nbx];
-    // side operands for k = 32 or 64: one dword of the W_S tile (16 rows x k)
-    // and one of X_S (M rows x k) per thread, so that every wave issues the
-    // same loads (the compiler can then count each wave's outstanding loads
-    // exactly and wait for the weights chunk by chunk); they reach wave 0,
-    // which finishes the block, through LDS.  Needed last, issued before the
-    // weights so that no wait for them is a wait for the weight stream.
-    const int k = a.k;
-    const bool side_pre = TAIL && (k == 32 || k == 64);
-    const int kd = k / 2;                               // dwords per side row
-    unsigned sw = 0, sx = 0;
-    if (side_pre) {
-        const int64_t wr = min(tid / kd, 15), xr = min((int64_t)(tid / kd), M - 1);
-        const int64_t n = n0 + wr;
-        sw = *reinterpret_cast<const unsigned *>(a.W_S + (n < N ? n : 0) * k + (tid % kd) * 2);
-        sx = *reinterpret_cast<const unsigned *>(a.X_S + xr * k + (tid % kd) * 2);
-    }
     __builtin_amdgcn_sched_barrier(0);     // keep these loads ahead of the weight loads
 
     // weights of this wave: chunks [c0, c0 + CPW) of each of its 16 rows,
@@ -806,6 +822,22 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
             wc[c] = *reinterpret_cast<const u32x4 *>(pw + ci * CODE_ROW);
         }
     }
+    // side operands for k = 32 or 64: one dword of the W_S tile (16 rows x k)
+    // and one of X_S (M rows x k) per thread, so that every wave issues the
+    // same loads (the compiler can then count each wave's outstanding loads
+    // exactly and wait for the weights chunk by chunk); they reach wave 0,
+    // which finishes the block, through LDS.  Issued after the weights: W_S
+    // comes from HBM, and a wait for it ahead of the main loop (loads
+    // complete in issue order) would hold the MFMAs back by its latency.
+    const int k = a.k;
+    const int kd = k / 2;                               // dwords per side row
+    unsigned sw = 0, sx = 0;
+    if (SIDE == 1) {
+        const int64_t wr = min(tid / kd, 15), xr = min((int64_t)(tid / kd), M - 1);
+        const int64_t n = n0 + wr;
+        sw = *reinterpret_cast<const unsigned *>(a.W_S + (n < N ? n : 0) * k + (tid % kd) * 2);
+        sx = *reinterpret_cast<const unsigned *>(a.X_S + xr * k + (tid % kd) * 2);
+    }
     // decode the M activation rows into LDS: one 16-channel block per item
     {
         const int64_t nb = K / 16;
@@ -818,30 +850,8 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
             dst[1] = decode8(c.y, sc);
         }
     }
-    // side tiles after the reduction space: W_S [16][kd] dwords, then X_S [M][kd]
     const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
-    uint32_t *sbuf = reinterpret_cast<uint32_t *>(xl + red_off + NW * WAVE * 16);
-    if (side_pre) {
-        if (tid < 16 * kd) sbuf[tid] = sw;
-        if (tid < M * kd) sbuf[16 * kd + tid] = sx;
-    }
     __syncthreads();
-
-    // the BF16 side product of the block (k = 32 or 64), by wave 0 before
-    // its chunks, while the weights are still arriving; lane (g, rr) holds
-    // row rr, channels 32h + 8g .. +8
-    f32x4 side = {0.f, 0.f, 0.f, 0.f};
-    if (side_pre && wave == 0) {
-        const bf16x8 z = {};
-        const bool okm = rr < M, okn = n0 + rr < N;
-        const uint32_t *wrow = sbuf + rr * kd;
-        const uint32_t *xrow = sbuf + 16 * kd + (okm ? rr : 0) * kd;
-        for (int h = 0; h < k / 32; h++) {
-            const bf16x8 ta = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xrow + 16 * h + 4 * g));
-            const bf16x8 tb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wrow + 16 * h + 4 * g));
-            side = mfma_bf16(okm ? ta : z, okn ? tb : z, side);
-        }
-    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const bool xrow = rr < M;
@@ -866,23 +876,44 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
         }
     }
 
-    // wave-order reduction through LDS (reuses the space after the activations)
+    // wave-order reduction through LDS (reuses the space after the
+    // activations); the side tiles go after it: W_S [16][kd] dwords, then
+    // X_S [M][kd]
     f32x4 *red = reinterpret_cast<f32x4 *>(xl + red_off);
+    uint32_t *sbuf = reinterpret_cast<uint32_t *>(xl + red_off + NW * WAVE * 16);
     red[wave * WAVE + lane] = acc;
+    if (SIDE == 1) {
+        if (tid < 16 * kd) sbuf[tid] = sw;
+        if (tid < M * kd) sbuf[16 * kd + tid] = sx;
+    }
     __syncthreads();
     if (wave == 0) {
+        // the BF16 side product of the block (k = 32 or 64); lane (g, rr)
+        // holds row rr, channels 32h + 8g .. +8
+        f32x4 side = {0.f, 0.f, 0.f, 0.f};
+        if (SIDE == 1) {
+            const bf16x8 z = {};
+            const bool okm = rr < M, okn = n0 + rr < N;
+            const uint32_t *wrow = sbuf + rr * kd;
+            const uint32_t *xrow = sbuf + 16 * kd + (okm ? rr : 0) * kd;
+            for (int h = 0; h < k / 32; h++) {
+                const bf16x8 ta = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xrow + 16 * h + 4 * g));
+                const bf16x8 tb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wrow + 16 * h + 4 * g));
+                side = mfma_bf16(okm ? ta : z, okn ? tb : z, side);
+            }
+        }
         f32x4 v = red[lane];
 #pragma unroll
         for (int w = 1; w < NW; w++) v += red[w * WAVE + lane];
         const float alpha = (*a.alpha_x) * (*a.alpha_w);
         const int64_t n = n0 + rr;
-        if (side_pre) {
+        if (SIDE == 1) {
 #pragma unroll
             for (int q = 0; q < 4; q++) v[q] = __builtin_fmaf(alpha, v[q], side[q]);
         } else {
             v *= alpha;
         }
-        if (TAIL && !side_pre) {          // other k: direct loads, masked
+        if (SIDE == 2) {                  // other k: direct loads, masked
             const bool al = (k % 8) == 0;
             const int64_t mrow = rr;
             for (int kk = 0; kk < k; kk += 32) {
@@ -902,6 +933,17 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     }
 }
 
+template <int NW, int CPW, int SIDE>
+static hipError_t launch_xlds(const GemmArgs &a, dim3 grid, size_t lds, hipStream_t s)
+{
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, SIDE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16 + 20 * 128);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, SIDE>), grid, dim3(64 * NW), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int NW, int CPW>
 static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
 {
@@ -909,20 +951,9 @@ static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
     const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16 +
                        (a.k > 0 ? (size_t)(16 + a.M) * 128 : 0);
     dim3 grid((unsigned)((a.N + 15) / 16));
-    if (a.k > 0) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16 + 20 * 128);
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, true>), grid, dim3(64 * NW), lds, s, a);
-    } else {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, false>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16 + 20 * 128);
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, false>), grid, dim3(64 * NW), lds, s, a);
-    }
-    return hipGetLastError();
+    if (a.k == 32 || a.k == 64) return launch_xlds<NW, CPW, 1>(a, grid, lds, s);
+    if (a.k > 0) return launch_xlds<NW, CPW, 2>(a, grid, lds, s);
+    return launch_xlds<NW, CPW, 0>(a, grid, lds, s);
 }
 
 template <int MB, int CB, int NW, int CPW>

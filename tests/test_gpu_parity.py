@@ -262,7 +262,9 @@ SHAPES = [(1, 16, 128, 0), (1, 100, 1024, 5), (8, 48, 256, 64), (16, 1000, 1024,
           (200, 300, 640, 100), (257, 257, 128, 128),
           (5, 40, 17408, 16), (40, 24, 8192, 64), (3, 48, 384, 64), (16, 272, 256, 32),
           # wide N with a ragged last 48-column block on the streaming decode forms
-          (2, 8200, 384, 64), (8, 8200, 256, 64), (12, 8200, 4608, 16), (40, 8200, 384, 32)]
+          (2, 8200, 384, 64), (8, 8200, 256, 64), (12, 8200, 4608, 16), (40, 8200, 384, 32),
+          # k = 32 on the streaming forms whose W_S fragments are loaded up front
+          (8, 1000, 8192, 32), (20, 500, 4608, 32), (50, 200, 1024, 32)]
 
 
 @pytest.mark.parametrize("M,N,K,k", SHAPES)
