@@ -225,7 +225,18 @@ def oracle_pipeline(X_warm, X, W, k, rows=None, cols=None, idx=None):
     xq, xs, xS = O.quantize_nvfp4(Xs_, idx, ax)
     wq, ws, wS = O.quantize_nvfp4(Ws_, idx, aw)
     Y = O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
-    return dict(idx=idx, ax=ax, aw=aw, Y=Y, xq=xq, xs=xs, wq=wq, ws=ws)
+    return dict(idx=idx, ax=ax, aw=aw, Y=Y, xq=xq, xs=xs, wq=wq, ws=ws, xS=xS, wS=wS)
+
+
+def product_magnitudes(o, i, j):
+    """Sum over the reduction of |x * w| for output (i, j) of an
+    oracle_pipeline result: the dequantized FP4 products and the BF16 side
+    products, in output units."""
+    dx = O.dequantize(o["xq"][i:i + 1], o["xs"][i:i + 1], o["ax"])[0]
+    dw = O.dequantize(o["wq"][j:j + 1], o["ws"][j:j + 1], o["aw"])[0]
+    sx = np.array([O.bf16_to_double(b) for b in o["xS"][i]])
+    sw = np.array([O.bf16_to_double(b) for b in o["wS"][j]])
+    return float(np.abs(dx * dw).sum() + np.abs(sx * sw).sum())
 
 
 def gpu_pipeline(X_warm, X, W, k, path=S.PATH_AUTO):
@@ -354,6 +365,26 @@ def test_prefill_full_size_sampled(name):
     assert np.array_equal(host(gw[0]), o["wq"]) and np.array_equal(host(gw[1]), o["ws"])
     assert_gemm_close(host(Y)[rows], o["Y"], f"prefill {name}")
     assert torch.isfinite(Yn).all()
+
+
+@pytest.mark.parametrize("name", ["q", "o"])
+def test_prefill_full_size_every_row(name):
+    """q and o of the prefill workload (M = 8192, K = N = 4096), every output
+    element against the oracle's own calibration and packs."""
+    M = 8192
+    p = synth.projection(synth.CFG_PREFILL, name, M)
+    o = oracle_pipeline(p["X_warm"], p["X"], p["W"], 64)
+    Xw, Xd, Wd = dev(p["X_warm"]), dev(p["X"]), dev(p["W"])
+    idx, ax, _ = S.select_channels(Xw, 64)
+    aw = S.compute_alpha(Wd, idx)
+    gx, gw = S.quantize_nvfp4(Xd, idx, ax), S.quantize_nvfp4(Wd, idx, aw)
+    Y = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
+    assert np.array_equal(host(gx[0]), o["xq"]) and np.array_equal(host(gx[1]), o["xs"])
+    assert np.array_equal(host(gw[0]), o["wq"]) and np.array_equal(host(gw[1]), o["ws"])
+    # 33.5 M outputs of 4096-term dot products: allow the scaled floor for at
+    # most 8 elements whose products cancel
+    assert_gemm_close(host(Y), o["Y"], f"prefill {name}, all rows",
+                      terms=lambda i, j: product_magnitudes(o, i, j), max_scaled=8)
 
 
 def test_grouped_moe_sampled():
