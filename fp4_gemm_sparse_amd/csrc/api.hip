@@ -205,6 +205,28 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const
     return run_gemm(a, ws, ws_bytes, path, hs(stream));
 }
 
+int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
+                      int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs, int32_t nseg,
+                      int path, splice_stream_t stream)
+{
+    static_assert(SPLICE_SEG_MAX == SEG_MAX, "segment limit");
+    if (nseg < 1 || nseg > SPLICE_SEG_MAX || !segs) return SPLICE_ERR_INVALID_ARG;
+    GemmSeg seg[SEG_MAX];
+    int64_t total = 0;
+    for (int32_t i = 0; i < nseg; i++) {
+        const splice_weight_seg &w = segs[i];
+        GemmArgs a{Xq, Xs, alpha_x, X_S, w.Wq, w.Ws, w.alpha_w, w.W_S, M, w.N, K, k, w.Y, w.ldy};
+        int rc = check_gemm(a, path);
+        if (rc) return rc;
+        seg[i] = GemmSeg{w.Wq, w.Ws, w.alpha_w, w.W_S, w.Y, w.ldy, w.N};
+        total += w.N;
+    }
+    if (total > (int64_t)1 << 30) return SPLICE_ERR_UNSUPPORTED;   // launch units fit an int
+    if (M == 0 || total == 0) return SPLICE_OK;
+    GemmArgs base{Xq, Xs, alpha_x, X_S, nullptr, nullptr, nullptr, nullptr, M, total, K, k, nullptr, 0};
+    return hip_status(launch_gemm_seg(choose_path(M, path), base, seg, nseg, hs(stream)));
+}
+
 int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
                              const float *alpha_x, const uint8_t *Wq, const uint8_t *Ws,
                              const float *alpha_w, const uint16_t *W_S, int64_t M, int64_t N,

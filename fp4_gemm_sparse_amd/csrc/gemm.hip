@@ -45,6 +45,55 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
 }
 
 // ===========================================================================
+// Column segments: products that share the activation operands (X, its
+// packs and X_S) but each have their own weights, tensor scale and output --
+// the q, k and v projections of one layer input, say -- computed by one
+// launch.  The launch units of a kernel (tile columns, column blocks) are
+// numbered across the segments in order and never straddle two, so each unit
+// runs exactly the code of a call on its own segment.
+// ===========================================================================
+struct SegTable {
+    GemmArgs a;                          // shared operands, M, K, k
+    GemmSeg seg[SEG_MAX];
+    int start[SEG_MAX + 1];              // first unit of each segment; start[nseg] = all units
+    int nseg;
+};
+
+static SegTable make_seg_table(const GemmArgs &a, const SegSpec &sp, int64_t unit)
+{
+    SegTable t;
+    t.a = a;
+    t.nseg = sp.nseg;
+    t.start[0] = 0;
+    for (int i = 0; i < SEG_MAX; i++) {
+        t.seg[i] = i < sp.nseg ? sp.seg[i] : sp.seg[0];
+        if (i < sp.nseg) t.start[i + 1] = t.start[i] + (int)((sp.seg[i].N + unit - 1) / unit);
+    }
+    for (int i = sp.nseg + 1; i <= SEG_MAX; i++) t.start[i] = t.start[sp.nseg];
+    return t;
+}
+
+// the arguments of unit u's segment, and u's index inside it
+__device__ __forceinline__ GemmArgs seg_args(const SegTable &t, int u, int &local)
+{
+    int sg = 0;
+#pragma unroll
+    for (int i = 1; i < SEG_MAX; i++)
+        if (i < t.nseg && u >= t.start[i]) sg = i;
+    local = u - t.start[sg];
+    GemmArgs r = t.a;
+    const GemmSeg &w = t.seg[sg];
+    r.Wq = w.Wq;
+    r.Ws = w.Ws;
+    r.alpha_w = w.alpha_w;
+    r.W_S = w.W_S;
+    r.Y = w.Y;
+    r.ldy = w.ldy;
+    r.N = w.N;
+    return r;
+}
+
+// ===========================================================================
 // LDS-decode prefill tile: each workgroup decodes every NVFP4 element of its
 // tile exactly once per K step (64 channels) into a swizzled FP16 tile in LDS
 // (double buffered).  The main form is 256 x 256 with eight waves (2 x 4,
@@ -326,6 +375,18 @@ __global__ __launch_bounds__(256) void prefill_lds128_kernel(GemmArgs a)
     lds_tile<128, 128, 2, 2, TAIL>(a, tm, tn, lds);
 }
 
+// the same tiles over column segments: tile columns numbered across them
+template <int BT, int WGN, bool TAIL>
+__global__ __launch_bounds__(64 * 2 * WGN) void prefill_seg_kernel(SegTable t)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tiles_m = (int)((t.a.M + BT - 1) / BT);
+    int tm, tn, local;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, t.start[t.nseg], tm, tn);
+    const GemmArgs a = seg_args(t, tn, local);
+    lds_tile<BT, BT, 2, WGN, TAIL>(a, tm, local, lds);
+}
+
 // ---------------------------------------------------------------------------
 // Grouped form (independent products sharing N, K and k, e.g. the experts of
 // a MoE layer): one launch covers the tiles of up to GROUP_MAX groups.  The
@@ -369,27 +430,45 @@ __global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
 }
 
 template <bool TAIL>
-static hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
+static hipError_t launch_prefill_lds(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     using C = LdsGeo<256, 256, 2, 4>;
-    const int64_t tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
     const size_t lds = 2 * C::TILE;
     // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&prefill_lds_kernel<TAIL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static const hipError_t attr_seg = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&prefill_seg_kernel<256, 4, TAIL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
+    if (attr_seg != hipSuccess) return attr_seg;
+    const int64_t tiles_m = (a.M + C::BM - 1) / C::BM;
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, C::BN);
+        hipLaunchKernelGGL((prefill_seg_kernel<256, 4, TAIL>), dim3((unsigned)(tiles_m * t.start[t.nseg])),
+                           dim3(C::NT), lds, s, t);
+    } else {
+        const int64_t tiles = tiles_m * ((a.N + C::BN - 1) / C::BN);
+        hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
+    }
     return hipGetLastError();
 }
 
 template <bool TAIL>
-static hipError_t launch_prefill_lds128(const GemmArgs &a, hipStream_t s)
+static hipError_t launch_prefill_lds128(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     using C = LdsGeo<128, 128, 2, 2>;
-    const int64_t tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
     const size_t lds = 2 * C::TILE;
-    hipLaunchKernelGGL(prefill_lds128_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
+    const int64_t tiles_m = (a.M + C::BM - 1) / C::BM;
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, C::BN);
+        hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL>), dim3((unsigned)(tiles_m * t.start[t.nseg])),
+                           dim3(C::NT), lds, s, t);
+    } else {
+        const int64_t tiles = tiles_m * ((a.N + C::BN - 1) / C::BN);
+        hipLaunchKernelGGL(prefill_lds128_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -454,7 +533,7 @@ struct DecodeCfg {
 };
 
 template <int MB, int CB, int NW, int BB, bool TAIL>
-__global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
+__device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
 {
     using C = DecodeCfg<MB, CB, NW, BB>;
     __shared__ f32x4 red[NW][C::RED_TILES][WAVE];
@@ -462,7 +541,7 @@ __global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t rowb = K / 2, rows = K / 16;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * CB);
+    const int64_t n0 = blk * (16 * CB);
     const int nchunk = (int)(K / BK);
 
     const uint8_t *wrow[CB];
@@ -611,9 +690,32 @@ __global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
     }
 }
 
-template <int MB, int CB, int NW, int BB>
-static hipError_t run_decode2(const GemmArgs &a, hipStream_t s)
+template <int MB, int CB, int NW, int BB, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode2_kernel(GemmArgs a)
 {
+    decode2_body<MB, CB, NW, BB, TAIL>(a, blockIdx.x);
+}
+
+template <int MB, int CB, int NW, int BB, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode2_seg_kernel(SegTable t)
+{
+    int local;
+    const GemmArgs a = seg_args(t, blockIdx.x, local);
+    decode2_body<MB, CB, NW, BB, TAIL>(a, local);
+}
+
+template <int MB, int CB, int NW, int BB>
+static hipError_t run_decode2(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
+{
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, 16 * CB);
+        const dim3 grid((unsigned)t.start[t.nseg]);
+        if (a.k > 0)
+            hipLaunchKernelGGL((decode2_seg_kernel<MB, CB, NW, BB, true>), grid, dim3(64 * NW), 0, s, t);
+        else
+            hipLaunchKernelGGL((decode2_seg_kernel<MB, CB, NW, BB, false>), grid, dim3(64 * NW), 0, s, t);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
     if (a.k > 0)
         hipLaunchKernelGGL((decode2_kernel<MB, CB, NW, BB, true>), grid, dim3(64 * NW), 0, s, a);
@@ -632,7 +734,7 @@ static hipError_t run_decode2(const GemmArgs &a, hipStream_t s)
 // LDS in wave order, then scaled, completed with the side product and stored.
 // ===========================================================================
 template <int MB, int CB, int NW, int CPW, bool TAIL>
-__global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
+__device__ __forceinline__ void decode3_body(const GemmArgs &a, int64_t blk)
 {
     constexpr int T = MB * CB;
     constexpr int RT = (T * NW <= 128) ? T : (128 / NW);      // tiles per LDS round
@@ -642,7 +744,7 @@ __global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t rowb = K / 2, rows = K / 16;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * CB);
+    const int64_t n0 = blk * (16 * CB);
     const int nchunk = (int)(K / BK);
 
     // All loads are unconditional (chunk index clamped, edge rows redirected
@@ -769,6 +871,20 @@ __global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
     }
 }
 
+template <int MB, int CB, int NW, int CPW, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode3_kernel(GemmArgs a)
+{
+    decode3_body<MB, CB, NW, CPW, TAIL>(a, blockIdx.x);
+}
+
+template <int MB, int CB, int NW, int CPW, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode3_seg_kernel(SegTable t)
+{
+    int local;
+    const GemmArgs a = seg_args(t, blockIdx.x, local);
+    decode3_body<MB, CB, NW, CPW, TAIL>(a, local);
+}
+
 // ---------------------------------------------------------------------------
 // Variant for few activation rows (M*K*2 bytes fit in LDS): the workgroup
 // decodes the M real activation rows once into an FP16 LDS copy, and every
@@ -780,7 +896,7 @@ constexpr int XLDS_MAX = 64 * 1024;        // bytes of FP16 activations kept in 
 // SIDE: 0 for k = 0; 1 for k = 32 or 64 (side tiles staged through LDS);
 // 2 for any other k (side operands loaded in the epilogue).
 template <int NW, int CPW, int SIDE>
-__global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
+__device__ __forceinline__ void decode_xlds_body(const GemmArgs &a, int64_t blk)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [M][K] f16, then reduction space
     const int tid = threadIdx.x, lane = tid % WAVE;
@@ -788,7 +904,7 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t rowb = K / 2, rows = K / 16;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = blk * 16;
     const int nchunk = (int)(K / BK);
 
     // the thread's first activation block (codes and scale) is loaded ahead
@@ -934,31 +1050,65 @@ __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
 }
 
 template <int NW, int CPW, int SIDE>
-static hipError_t launch_xlds(const GemmArgs &a, dim3 grid, size_t lds, hipStream_t s)
+__global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
 {
+    decode_xlds_body<NW, CPW, SIDE>(a, blockIdx.x);
+}
+
+template <int NW, int CPW, int SIDE>
+__global__ __launch_bounds__(64 * NW) void decode_xlds_seg_kernel(SegTable t)
+{
+    int local;
+    const GemmArgs a = seg_args(t, blockIdx.x, local);
+    decode_xlds_body<NW, CPW, SIDE>(a, local);
+}
+
+template <int NW, int CPW, int SIDE>
+static hipError_t launch_xlds(const GemmArgs &a, const SegSpec *sp, size_t lds, hipStream_t s)
+{
+    constexpr int LDS_ATTR = XLDS_MAX + 16 * WAVE * 16 + 20 * 128;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, SIDE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, XLDS_MAX + 16 * WAVE * 16 + 20 * 128);
+        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_ATTR);
+    static const hipError_t attr_seg = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&decode_xlds_seg_kernel<NW, CPW, SIDE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_ATTR);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, SIDE>), grid, dim3(64 * NW), lds, s, a);
+    if (attr_seg != hipSuccess) return attr_seg;
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, 16);
+        hipLaunchKernelGGL((decode_xlds_seg_kernel<NW, CPW, SIDE>), dim3((unsigned)t.start[t.nseg]),
+                           dim3(64 * NW), lds, s, t);
+    } else {
+        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, SIDE>), dim3((unsigned)((a.N + 15) / 16)),
+                           dim3(64 * NW), lds, s, a);
+    }
     return hipGetLastError();
 }
 
 template <int NW, int CPW>
-static hipError_t run_decode_xlds(const GemmArgs &a, hipStream_t s)
+static hipError_t run_decode_xlds(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     // activations, reduction space, side tiles (k <= 64: (16 + M) rows of 128 bytes)
     const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + (size_t)NW * WAVE * 16 +
                        (a.k > 0 ? (size_t)(16 + a.M) * 128 : 0);
-    dim3 grid((unsigned)((a.N + 15) / 16));
-    if (a.k == 32 || a.k == 64) return launch_xlds<NW, CPW, 1>(a, grid, lds, s);
-    if (a.k > 0) return launch_xlds<NW, CPW, 2>(a, grid, lds, s);
-    return launch_xlds<NW, CPW, 0>(a, grid, lds, s);
+    if (a.k == 32 || a.k == 64) return launch_xlds<NW, CPW, 1>(a, sp, lds, s);
+    if (a.k > 0) return launch_xlds<NW, CPW, 2>(a, sp, lds, s);
+    return launch_xlds<NW, CPW, 0>(a, sp, lds, s);
 }
 
 template <int MB, int CB, int NW, int CPW>
-static hipError_t run_decode3(const GemmArgs &a, hipStream_t s)
+static hipError_t run_decode3(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, 16 * CB);
+        const dim3 grid((unsigned)t.start[t.nseg]);
+        if (a.k > 0)
+            hipLaunchKernelGGL((decode3_seg_kernel<MB, CB, NW, CPW, true>), grid, dim3(64 * NW), 0, s, t);
+        else
+            hipLaunchKernelGGL((decode3_seg_kernel<MB, CB, NW, CPW, false>), grid, dim3(64 * NW), 0, s, t);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
     if (a.k > 0)
         hipLaunchKernelGGL((decode3_kernel<MB, CB, NW, CPW, true>), grid, dim3(64 * NW), 0, s, a);
@@ -970,12 +1120,12 @@ static hipError_t run_decode3(const GemmArgs &a, hipStream_t s)
 // waves per workgroup so that each wave holds at most CPW chunks; false when
 // even MAXNW waves would need more (then the looping form is used)
 template <int MB, int CB, int CPW, int MAXNW>
-static bool run_decode3_k(const GemmArgs &a, hipStream_t s, hipError_t &e)
+static bool run_decode3_k(const GemmArgs &a, const SegSpec *sp, hipStream_t s, hipError_t &e)
 {
     const int nchunk = (int)(a.K / BK);
-    if (nchunk <= 4 * CPW) { e = run_decode3<MB, CB, 4, CPW>(a, s); return true; }
-    if (nchunk <= 8 * CPW) { e = run_decode3<MB, CB, 8, CPW>(a, s); return true; }
-    if (MAXNW >= 16 && nchunk <= 16 * CPW) { e = run_decode3<MB, CB, (MAXNW >= 16 ? 16 : 8), CPW>(a, s); return true; }
+    if (nchunk <= 4 * CPW) { e = run_decode3<MB, CB, 4, CPW>(a, sp, s); return true; }
+    if (nchunk <= 8 * CPW) { e = run_decode3<MB, CB, 8, CPW>(a, sp, s); return true; }
+    if (MAXNW >= 16 && nchunk <= 16 * CPW) { e = run_decode3<MB, CB, (MAXNW >= 16 ? 16 : 8), CPW>(a, sp, s); return true; }
     return false;
 }
 
@@ -985,7 +1135,9 @@ size_t gemm_ws_bytes(Path, int64_t, int64_t, int64_t)
     return 0;        // neither datapath needs scratch memory
 }
 
-hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t s)
+// configuration choice and launch; sp != nullptr: the column segments of sp,
+// whose widths sum to a.N
+static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     if (a.M == 0 || a.N == 0) return hipSuccess;
     if (a.K == 0) p = Path::Prefill;    // the decode kernels assume at least one K chunk
@@ -994,8 +1146,8 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
         const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
         const int64_t t256x128 = ((a.M + 255) / 256) * ((a.N + 127) / 128);
         (void)t256x128;
-        if (t256 >= 240) return a.k > 0 ? launch_prefill_lds<true>(a, s) : launch_prefill_lds<false>(a, s);
-        return a.k > 0 ? launch_prefill_lds128<true>(a, s) : launch_prefill_lds128<false>(a, s);
+        if (t256 >= 240) return a.k > 0 ? launch_prefill_lds<true>(a, sp, s) : launch_prefill_lds<false>(a, sp, s);
+        return a.k > 0 ? launch_prefill_lds128<true>(a, sp, s) : launch_prefill_lds128<false>(a, sp, s);
     }
     // weight-streaming decode path; configurations chosen from measured sweeps
     // on MI355X (Qwen3-8B projection shapes, M = 1, 4, 8, 16, 32, 64)
@@ -1004,29 +1156,46 @@ hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t 
     const int64_t colblocks = (a.N + 15) / 16;
     if (a.M <= 16) {
         if (a.M <= 4 && a.M * a.K * 2 <= XLDS_MAX && nchunk >= 2 && nchunk % 2 == 0) {   // 16-byte aligned scale pairs
-            if (nchunk <= 8 * 4) return run_decode_xlds<8, 4>(a, s);
-            if (nchunk <= 16 * 4) return run_decode_xlds<16, 4>(a, s);
-            if (nchunk <= 16 * 6) return run_decode_xlds<16, 6>(a, s);
-            if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, s);
+            if (nchunk <= 8 * 4) return run_decode_xlds<8, 4>(a, sp, s);
+            if (nchunk <= 16 * 4) return run_decode_xlds<16, 4>(a, sp, s);
+            if (nchunk <= 16 * 6) return run_decode_xlds<16, 6>(a, sp, s);
+            if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, sp, s);
         }
         // wide N: 48 columns per workgroup, streaming one chunk at a time
         // (N = 12288: 6-9% faster than the single-round form at M = 8-16);
         // K up to 4096: single round, eight waves of four chunks; longer K:
         // streaming, 16 columns per workgroup (K = 12288: 25% faster than the
         // single round at M = 4-16, whose sixteen waves hold six chunks each)
-        if (colblocks >= 512) return run_decode2<1, 3, 8, 1>(a, s);
-        if (nchunk <= 32) return run_decode3<1, 1, 8, 4>(a, s);
-        return run_decode2<1, 1, 8, 1>(a, s);
+        if (colblocks >= 512) return run_decode2<1, 3, 8, 1>(a, sp, s);
+        if (nchunk <= 32) return run_decode3<1, 1, 8, 4>(a, sp, s);
+        return run_decode2<1, 1, 8, 1>(a, sp, s);
     }
     // M in 17..64: wide N at M <= 32 takes the single-round form with 48
     // columns per workgroup (one workgroup per CU at N = 12288); otherwise
     // the streaming form over 8 waves
     if (a.M <= 32) {
-        if (colblocks >= 512 && run_decode3_k<2, 3, 4, 8>(a, s, e)) return e;
-        return run_decode2<2, 1, 8, 1>(a, s);
+        if (colblocks >= 512 && run_decode3_k<2, 3, 4, 8>(a, sp, s, e)) return e;
+        return run_decode2<2, 1, 8, 1>(a, sp, s);
     }
-    if (colblocks >= 512) return run_decode2<4, 3, 8, 1>(a, s);
-    return run_decode2<4, 1, 8, 2>(a, s);
+    if (colblocks >= 512) return run_decode2<4, 3, 8, 1>(a, sp, s);
+    return run_decode2<4, 1, 8, 2>(a, sp, s);
+}
+
+hipError_t launch_gemm(Path p, const GemmArgs &a, void *, size_t, hipStream_t s)
+{
+    return dispatch_gemm(p, a, nullptr, s);
+}
+
+hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s)
+{
+    // the configuration is chosen for the combined width, as for one call
+    // with N = the sum of the widths
+    GemmArgs b = a;
+    b.N = 0;
+    for (int i = 0; i < nseg; i++) b.N += seg[i].N;
+    if (nseg == 0 || b.M == 0 || b.N == 0) return hipSuccess;
+    const SegSpec sp{seg, nseg};
+    return dispatch_gemm(p, b, &sp, s);
 }
 
 }  // namespace splice

@@ -44,6 +44,24 @@ struct GemmArgs {
 enum class Path { Decode, Prefill };
 size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+// one column segment of a launch that shares the activation operands: its
+// own weights, tensor scale, side columns and output of width N
+struct GemmSeg {
+    const uint8_t *Wq, *Ws;
+    const float *alpha_w;
+    const uint16_t *W_S;
+    float *Y;
+    int64_t ldy, N;
+};
+constexpr int SEG_MAX = 8;
+struct SegSpec {
+    const GemmSeg *seg;
+    int nseg;
+};
+// the products of a's activation operands (Xq, Xs, alpha_x, X_S, M, K, k)
+// with each segment's weights, in one launch (a's weight and output fields
+// are ignored); 1 <= nseg <= SEG_MAX
+hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s);
 // independent products sharing N, K and k (groups[i].N/K/k equal), one launch
 // per 32 groups; groups with M == 0 are skipped
 hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s);

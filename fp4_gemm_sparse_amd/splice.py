@@ -27,6 +27,7 @@ PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 SELECT_VARIANCE, SELECT_SECOND_MOMENT = 0, 1
 DECODE_MAX_M = 64
 FUSED_MAX_M = 4
+SEG_MAX = 8
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -43,6 +44,11 @@ class SpliceError(RuntimeError):
 class _Group(ctypes.Structure):
     _fields_ = [("Xq", _vp), ("Xs", _vp), ("alpha_x", _vp), ("X_S", _vp), ("Wq", _vp), ("Ws", _vp),
                 ("alpha_w", _vp), ("W_S", _vp), ("M", _i64), ("Y", _vp)]
+
+
+class _Seg(ctypes.Structure):
+    _fields_ = [("Wq", _vp), ("Ws", _vp), ("alpha_w", _vp), ("W_S", _vp), ("N", _i64), ("Y", _vp),
+                ("ldy", _i64)]
 
 
 _SIGS = {
@@ -71,6 +77,8 @@ _SIGS = {
     "splice_gemm_grouped": (ctypes.c_int, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32, _vp, _sz,
                                            _vp]),
     "splice_grouped_workspace_size": (_sz, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32]),
+    "splice_gemm_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, ctypes.POINTER(_Seg),
+                                         _i32, ctypes.c_int, _vp]),
 }
 
 _lib = None
@@ -307,6 +315,24 @@ def probe_mfma_f16(iters, workgroups, sink):
     """Measurement aid: 4 * iters 32x32x16 FP16 MFMAs per wave, 4 waves per
     workgroup (sink float32 [workgroups * 4])."""
     _check("splice_probe_mfma_f16", lib().splice_probe_mfma_f16(iters, workgroups, _p(sink), _stream()))
+
+
+def splice_gemm_multi(Xq, Xs, alpha_x, X_S, weights, path=PATH_AUTO, out=None):
+    """One launch of the products of one set of activation packs with several
+    weight packs.  weights: list of (Wq, Ws, alpha_w, W_S) (W_S None when
+    k == 0); out: list of fp32 outputs [M, N_i] or None.  Returns the outputs."""
+    M, K = Xq.shape[0], Xq.shape[1] * 2
+    k = 0 if X_S is None else X_S.shape[1]
+    if out is None:
+        out = [torch.empty(M, w[0].shape[0], dtype=torch.float32, device=Xq.device) for w in weights]
+    arr = (_Seg * max(len(weights), 1))()
+    for i, (w, Y) in enumerate(zip(weights, out)):
+        arr[i] = _Seg(_p(w[0]), _p(w[1]), _p(w[2]), _p(w[3]) if k else None, w[0].shape[0], _p(Y),
+                      Y.stride(0))
+    _check("splice_gemm_multi",
+           lib().splice_gemm_multi(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, M, K, k, arr,
+                                   len(weights), path, _stream()))
+    return out
 
 
 def splice_gemm_grouped(groups, N, K, k, ws=None):

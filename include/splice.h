@@ -207,6 +207,39 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
                              const float *alpha_w, const uint16_t *W_S, int64_t M, int64_t N,
                              int64_t K, int32_t k, float *Y, int64_t ldy, splice_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * SpliceGEMM of one set of activation operands against several weight
+ * matrices in one launch (Sec. 4.2 Eq. 5 and Sec. 5.1 dual-path execution,
+ * per product): the projections that read the same layer input -- q, k and v,
+ * or gate and up -- share X's packs, alpha_x and X_S, since the protected
+ * channels S are chosen from that input's statistics.  Each segment has its
+ * own weight packs, alpha_w, W_S and output.
+ *   Xq, Xs, alpha_x, X_S, M, K, k: as for splice_gemm.
+ *   segs   HOST array of nseg (1 .. SPLICE_SEG_MAX) entries; in each, Wq, Ws,
+ *          alpha_w, W_S, Y and ldy are as splice_gemm's for a product of
+ *          width N (N >= 0; 0 skips the segment).
+ *   path   as for splice_gemm; the kernel configuration is chosen for M and
+ *          the sum of the widths, as one call of that width would choose it.
+ * Each segment's Y equals splice_gemm's for that segment alone: bit for bit
+ * on the prefill path (every tile size sums K in the same order), and on the
+ * decode path whenever the call alone would pick the same configuration (for
+ * the Qwen3-8B q/k/v and gate/up widths it does); within the GEMM tolerance
+ * otherwise.  Errors as splice_gemm, checked per segment before anything is
+ * launched.  No workspace; nothing is allocated. */
+#define SPLICE_SEG_MAX 8
+typedef struct {
+    const uint8_t *Wq, *Ws;
+    const float *alpha_w;
+    const uint16_t *W_S;
+    int64_t N;
+    float *Y;
+    int64_t ldy;
+} splice_weight_seg;
+
+int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
+                      int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs, int32_t nseg,
+                      int path, splice_stream_t stream);
+
 /* Workspace bytes splice_gemm / nvfp4_gemm need for this shape (k is
  * ignored by the current kernels but part of the contract). */
 size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);

@@ -18,7 +18,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = splice.header_functions()
     assert {"splice_select_channels", "splice_quantize_nvfp4", "splice_gemm", "nvfp4_gemm",
-            "splice_compute_alpha", "splice_gemm_grouped", "splice_workspace_size"} <= set(names)
+            "splice_compute_alpha", "splice_gemm_grouped", "splice_workspace_size",
+            "splice_gemm_multi"} <= set(names)
     for n in names:
         assert getattr(L, n) is not None
 
@@ -124,6 +125,30 @@ def test_grouped_argument_errors(L):
     empty = (G * 1)()
     empty[0] = G(None, None, None, None, None, None, None, None, 0, None)    # M = 0 group
     assert L.splice_gemm_grouped(empty, 1, 64, 256, 8, None, 0, None) == splice.OK
+
+
+def test_multi_argument_errors(L):
+    S = splice._Seg
+    good = S(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 64)
+
+    def call(segs, n, M=4, K=256, k=8, path=0, XS=FAKE):
+        return L.splice_gemm_multi(FAKE, FAKE, FAKE, XS, M, K, k, segs, n, path, None)
+    one = (S * 1)(good)
+    assert call(one, 0) == splice.ERR_INVALID_ARG                       # no segment
+    assert call(one, splice.SEG_MAX + 1) == splice.ERR_INVALID_ARG      # too many
+    assert call(None, 1) == splice.ERR_INVALID_ARG
+    two = (S * 2)(good, S(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 32))        # ldy < N
+    assert call(two, 2) == splice.ERR_INVALID_ARG
+    two = (S * 2)(good, S(FAKE, FAKE, None, FAKE, 64, FAKE, 64))        # no alpha_w
+    assert call(two, 2) == splice.ERR_INVALID_ARG
+    two = (S * 2)(good, S(FAKE + 4, FAKE, FAKE, FAKE, 64, FAKE, 64))    # misaligned codes
+    assert call(two, 2) == splice.ERR_INVALID_ARG
+    assert call(one, 1, XS=None) == splice.ERR_INVALID_ARG               # k > 0 without X_S
+    assert call(one, 1, K=144) == splice.ERR_UNSUPPORTED
+    assert call(one, 1, M=65, path=splice.PATH_DECODE) == splice.ERR_INVALID_ARG
+    assert call(one, 1, M=0) == splice.OK                                # nothing to do
+    empty = (S * 2)(S(None, None, None, None, 0, None, 0), S(None, None, None, None, 0, None, 0))
+    assert call(empty, 2) == splice.OK                                   # zero widths
 
 
 def fused(L, M=1, N=64, K=1024, k=8, **over):

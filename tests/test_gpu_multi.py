@@ -1,0 +1,147 @@
+"""GPU parity of splice_gemm_multi, one launch over several weight matrices
+that share the activation operands, through the C ABI.
+
+Against separate splice_gemm calls on the same packs: bit-identical on the
+prefill path (every tile size sums K in the same order) and on the decode
+path wherever one call of the combined width picks the configuration each
+call alone picks -- here, whenever the combined width stays below the wide
+form's threshold, and for the Qwen3-8B q/k/v and gate/up pairs.  Against the
+oracle: the tolerance in gpu_util, segment by segment.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_gemm_sparse_amd import splice as S
+from fp4_gemm_sparse_amd import synth
+from gpu_util import assert_gemm_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+WIDE_COLBLOCKS = 512        # decode: 16-column blocks from which the wide form is chosen
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def packs(X, Ws, k, seed):
+    """Device packs of X and of each weight matrix, with X's top-k channels
+    from a warm-up batch drawn like X."""
+    Xw = dev(synth.activations(7, seed % 4, 256, X.shape[1], 2 + 10 * seed, "student", n_out=8))
+    idx, ax, _ = S.select_channels(Xw, k)
+    xq = S.quantize_nvfp4(dev(X), idx, ax)
+    wp = []
+    for W in Ws:
+        Wd = dev(W)
+        aw = S.compute_alpha(Wd, idx)
+        wq = S.quantize_nvfp4(Wd, idx, aw)
+        wp.append((wq[0], wq[1], aw, wq[2] if k else None))
+    packs.idx = idx
+    return xq, ax, wp
+
+
+def separate(xq, ax, wp, k, path):
+    return [S.splice_gemm(xq[0], xq[1], ax, xq[2] if k else None, *w, path=path) for w in wp]
+
+
+def same_config(M, widths, path):
+    if path == S.PATH_PREFILL or M > S.DECODE_MAX_M:
+        return True
+    wide = [(n + 15) // 16 >= WIDE_COLBLOCKS for n in widths]
+    return all(w == ((sum(widths) + 15) // 16 >= WIDE_COLBLOCKS) for w in wide)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 20, 40, 64, 100, 300])
+@pytest.mark.parametrize("k", [0, 8, 64])
+def test_ragged_segments(M, k):
+    """Five segments of ragged widths (one empty) against separate calls and
+    the oracle; K = 1024."""
+    K, widths = 1024, [100, 17, 0, 300, 64]
+    g = np.random.default_rng(M * 10 + k)
+    X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
+    Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
+    xq, ax, wp = packs(X, Ws, k, M + k)
+    path = S.PATH_AUTO
+    Ym = S.splice_gemm_multi(xq[0], xq[1], ax, xq[2] if k else None, wp, path=path)
+    Yd = separate(xq, ax, wp, k, path)
+    torch.cuda.synchronize()
+    exact = same_config(M, widths, path)
+    xo = (host(xq[0]), host(xq[1]), np.float32(ax.item()), host(xq[2]))
+    for i, (a, b) in enumerate(zip(Ym, Yd)):
+        assert a.shape == (M, widths[i])
+        if exact:
+            assert torch.equal(a, b), f"segment {i}"
+        if widths[i] == 0:
+            continue
+        wo = (host(wp[i][0]), host(wp[i][1]), np.float32(wp[i][2].item()),
+              host(wp[i][3]) if k else np.zeros((widths[i], 0), np.uint16))
+        Yo = O.splice_gemm(xo[0], xo[1], xo[2], xo[3] if k else None, wo[0], wo[1], wo[2],
+                           wo[3] if k else None)
+        assert_gemm_close(host(a), Yo, f"M={M} k={k} segment {i}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64, 512])
+@pytest.mark.parametrize("group", ["qkv", "gate_up"])
+def test_layer_groups_bit_identical(M, group):
+    """The projections that read one Qwen3-8B layer input, in one launch, give
+    the separate calls' bits (M = 512: the prefill path)."""
+    names = ["q", "k", "v"] if group == "qkv" else ["gate", "up"]
+    K = synth.QWEN3_8B[names[0]][0]
+    g = np.random.default_rng(5)
+    X = synth.activations(synth.CFG_DECODE, 0, M, K, 3, "student")
+    Ws = [synth.to_bf16(g.normal(0, 0.02, (synth.QWEN3_8B[n][1], K))) for n in names]
+    xq, ax, wp = packs(X, Ws, 64, 1)
+    Ym = S.splice_gemm_multi(xq[0], xq[1], ax, xq[2], wp)
+    Yd = separate(xq, ax, wp, 64, S.PATH_AUTO)
+    torch.cuda.synchronize()
+    for n, a, b in zip(names, Ym, Yd):
+        assert torch.equal(a, b), f"{group} M={M}: {n}"
+
+
+def test_output_row_stride_and_forced_paths():
+    """Outputs that are column slices of one wider buffer (ldy > N), on both
+    paths."""
+    M, K, widths = 24, 512, [48, 80]
+    g = np.random.default_rng(3)
+    X = synth.to_bf16(g.standard_normal((M, K)))
+    Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
+    xq, ax, wp = packs(X, Ws, 8, 3)
+    for path in (S.PATH_DECODE, S.PATH_PREFILL):
+        buf = torch.full((M, 200), float("nan"), device="cuda")
+        outs = [buf[:, 0:48], buf[:, 60:140]]
+        S.splice_gemm_multi(xq[0], xq[1], ax, xq[2], wp, path=path, out=outs)
+        Yd = separate(xq, ax, wp, 8, path)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], Yd[0]) and torch.equal(outs[1], Yd[1])
+        assert torch.isnan(buf[:, 48:60]).all() and torch.isnan(buf[:, 140:]).all()
+
+
+def test_multi_in_hip_graph():
+    """Captured once and replayed with new activations in place: every replay
+    equals the eager call."""
+    M, K, widths = 4, 1024, [256, 64, 64]
+    g = np.random.default_rng(8)
+    Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
+    X0 = synth.to_bf16(g.standard_normal((M, K)))
+    xq, ax, wp = packs(X0, Ws, 64, 8)
+    idx = packs.idx
+    outs = [torch.empty(M, n, device="cuda") for n in widths]
+    S.splice_gemm_multi(xq[0], xq[1], ax, xq[2], wp, out=outs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        S.splice_gemm_multi(xq[0], xq[1], ax, xq[2], wp, out=outs)
+    for r in range(3):
+        X = synth.to_bf16(g.standard_normal((M, K)))
+        S.quantize_nvfp4(dev(X), idx, ax, out=xq)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = S.splice_gemm_multi(xq[0], xq[1], ax, xq[2], wp)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {r}"
