@@ -39,6 +39,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 matrix peak
 K_PROT = 64
 M_PREFILL = 8192
 DECODE_MS = (1, 8, 32, 64)
+# the layer's GEMM launches: the projections that read one input share one
+LAUNCHES = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 FUSED_MS = (1, 2, 4)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_splice_gemm_traffic_qwen3_8b.md")
 COPY_ELEMS = 128 << 20            # fp32 elements of the calibration copy (512 MiB each way)
@@ -156,26 +158,31 @@ def main():
     gemm_events = []
 
     def step(record):
-        done = set()
-        for n in names:
-            p = P[n]
-            g = p["grp"]
-            if id(g) not in done:
-                done.add(id(g))
-                g["stats"].count = 0
-                S.select_channels(g["Xw"], K_PROT, g["stats"], out=(g["idx"], g["ax"]))
-                S.quantize_nvfp4(g["X"], g["idx"], g["ax"], out=g["xpack"])
-            S.compute_alpha(p["W"], p["idx"], out=p["aw"], ws=alpha_ws)
-            S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
+        for launch in LAUNCHES:
+            g = P[launch[0]]["grp"]
+            g["stats"].count = 0
+            S.select_channels(g["Xw"], K_PROT, g["stats"], out=(g["idx"], g["ax"]))
+            S.quantize_nvfp4(g["X"], g["idx"], g["ax"], out=g["xpack"])
+            for n in launch:
+                p = P[n]
+                S.compute_alpha(p["W"], p["idx"], out=p["aw"], ws=alpha_ws)
+                S.quantize_nvfp4(p["W"], p["idx"], p["aw"], out=p["wpack"])
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            xq, xs, xS = p["xpack"]
-            wq, ws, wS = p["wpack"]
-            S.splice_gemm(xq, xs, p["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])
+            xq, xs, xS = g["xpack"]
+            if len(launch) == 1:
+                p = P[launch[0]]
+                wq, ws, wS = p["wpack"]
+                S.splice_gemm(xq, xs, g["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])
+            else:
+                S.splice_gemm_multi(xq, xs, g["ax"], xS,
+                                    [(P[n]["wpack"][0], P[n]["wpack"][1], P[n]["aw"], P[n]["wpack"][2])
+                                     for n in launch],
+                                    path=S.PATH_PREFILL, out=[P[n]["Y"] for n in launch])
             if record:
                 e1.record(stream)
-                gemm_events.append((n, e0, e1))
+                gemm_events.append(("|".join(launch), e0, e1))
 
     for _ in range(args.warmup):
         step(False)
@@ -191,10 +198,10 @@ def main():
     log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s")
 
     # dominant kernel: the prefill SpliceGEMM launches inside the timed steps
-    per = {n: [] for n in names}
-    for n, a, b in gemm_events:
-        per[n].append(a.elapsed_time(b))
-    gemm_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    per = {}
+    for key, a, b in gemm_events:
+        per.setdefault(key, []).append(a.elapsed_time(b))
+    gemm_ms = {key: float(np.mean(v)) for key, v in per.items()}      # per launch
     flops = {n: 2.0 * M_PREFILL * P[n]["N"] * P[n]["K"] for n in names}
     achieved = sum(flops.values()) / (sum(gemm_ms.values()) * 1e-3) / 1e12
     traffic = read_traffic()
@@ -362,8 +369,9 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         del x16, w16
     tot_sp, tot_nv = sum(sp_ms.values()), sum(nv_ms.values())
     out["prefill"] = {
-        "timing": "median of 50 back-to-back calls on resident inputs, each bracketed by HIP events; "
-                  "gemm_ms_in_step are the same launches inside the timed step, after the "
+        "timing": "median of 50 back-to-back calls on resident inputs, each bracketed by HIP events, "
+                  "one call per projection; gemm_ms_in_step are the timed step's launches, one per "
+                  "layer input (q|k|v and gate|up each in one splice_gemm_multi launch), after the "
                   "preparation kernels",
         "gemm_tflops": round(sum(flops.values()) / (tot_sp * 1e-3) / 1e12, 2),
         "nvfp4_gemm_tflops": round(sum(flops.values()) / (tot_nv * 1e-3) / 1e12, 2),
@@ -371,7 +379,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         "overhead_projection_pct": round(100.0 * (sum(sp_full_ms.values()) - sum(nv_full_ms.values()))
                                          / sum(nv_full_ms.values()), 2),
         "gemm_ms": {n: round(v, 4) for n, v in sp_ms.items()},
-        "gemm_ms_in_step": {n: round(v, 4) for n, v in gemm_ms.items()},
+        "gemm_ms_in_step": {key: round(v, 4) for key, v in gemm_ms.items()},
         "nvfp4_ms": {n: round(v, 4) for n, v in nv_ms.items()},
         "library_fp16_dense": {
             "note": "context only: torch.matmul FP16 x FP16 -> FP16 (hipBLASLt) on the same shapes; "
@@ -465,6 +473,51 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         "timing": "as for decode; per projection, the activation preparation (quantize + gather) "
                   "and the GEMM as two launches, or one fused launch",
         "shapes": fz}
+
+    # ---------------- the decode layer in four launches: q|k|v and gate|up
+    # each in one splice_gemm_multi call (sets of the packed weights walked in
+    # turn, as above), against the seven single calls measured above
+    lay = {}
+    for M in DECODE_MS:
+        t4 = b4 = 0.0
+        per = {}
+        for launch in LAUNCHES:
+            p0 = P[launch[0]]
+            K = p0["K"]
+            Xh = synth.activations(synth.CFG_DECODE, synth.INPUT_STREAM[launch[0]], M, K, 3, "student")
+            X = torch.from_numpy(Xh.view(np.int16)).to(dev)
+            xq = S.quantize_nvfp4(X, p0["idx"], p0["ax"])
+            Ys = [torch.empty(M, P[n]["N"], dtype=torch.float32, device=dev) for n in launch]
+            wb = sum(pack_bytes(P[n]["wpack"]) for n in launch)
+            nset = copies_for(wb)
+            sets = [[(P[n]["wpack"][0], P[n]["wpack"][1], P[n]["aw"], P[n]["wpack"][2]) for n in launch]]
+            sets += [[(P[n]["wpack"][0].clone(), P[n]["wpack"][1].clone(), P[n]["aw"],
+                       P[n]["wpack"][2].clone()) for n in launch] for _ in range(nset - 1)]
+
+            def call(i):
+                w = sets[i % nset]
+                if len(launch) == 1:
+                    S.splice_gemm(xq[0], xq[1], p0["ax"], xq[2], *w[0], out=Ys[0])
+                else:
+                    S.splice_gemm_multi(xq[0], xq[1], p0["ax"], xq[2], w, out=Ys)
+            t = graph_timed(torch, call, max(args.decode_iters, nset))
+            del sets
+            torch.cuda.empty_cache()
+            per["|".join(launch)] = round(t * 1e3, 2)
+            t4 += t
+            b4 += (M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
+                   + sum(P[n]["N"] * K * (0.5 + 1 / 16) + 2 * P[n]["N"] * K_PROT + 4 * M * P[n]["N"]
+                         for n in launch))
+        t7 = sum(dec[f"{n}@M{M}"]["us"] for n in names) * 1e-3
+        lay[f"M{M}"] = {"us_four_launches": round(t4 * 1e3, 2), "us_seven_launches": round(t7 * 1e3, 2),
+                        "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "launches_us": per}
+        log(f"decode layer in four launches M={M}: {lay[f'M{M}']}")
+    out["decode_layer_four_launches"] = {
+        "timing": "as for decode; q|k|v and gate|up each one splice_gemm_multi launch, o and down "
+                  "one splice_gemm each; activation bytes counted once per launch",
+        "shapes": lay}
 
     # ---------------- grouped MoE stand-in
     counts = synth.moe_counts()
@@ -640,28 +693,35 @@ def read_traffic():
 def profile_workload(torch, S, host, names, dev):
     """A plain fp32 multiply-by-one over COPY_ELEMS elements (reads and writes
     exactly 4*COPY_ELEMS bytes each) for counter calibration, then three
-    prefill SpliceGEMMs per projection in the launch configuration the
-    timed step uses."""
+    prefill SpliceGEMM launches per layer input, as the timed step makes
+    them."""
     src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    for n in names:
-        h = host[n]
+    for launch in LAUNCHES:
+        h = host[launch[0]]
         X = torch.from_numpy(h["X"].view(np.int16)).to(dev)
-        W = torch.from_numpy(h["W"].view(np.int16)).to(dev)
         Xw = torch.from_numpy(h["X_warm"].view(np.int16)).to(dev)
         idx, ax, _ = S.select_channels(Xw, K_PROT)
-        aw = S.compute_alpha(W, idx)
         xq, xs, xS = S.quantize_nvfp4(X, idx, ax)
-        wq, ws, wS = S.quantize_nvfp4(W, idx, aw)
-        Y = torch.empty(X.shape[0], W.shape[0], dtype=torch.float32, device=dev)
+        wts, outs = [], []
+        for n in launch:
+            W = torch.from_numpy(host[n]["W"].view(np.int16)).to(dev)
+            aw = S.compute_alpha(W, idx)
+            wq, ws, wS = S.quantize_nvfp4(W, idx, aw)
+            wts.append((wq, ws, aw, wS))
+            outs.append(torch.empty(X.shape[0], W.shape[0], dtype=torch.float32, device=dev))
+            del W
         for _ in range(3):
-            S.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS, path=S.PATH_PREFILL, out=Y)
+            if len(launch) == 1:
+                S.splice_gemm(xq, xs, ax, xS, *wts[0], path=S.PATH_PREFILL, out=outs[0])
+            else:
+                S.splice_gemm_multi(xq, xs, ax, xS, wts, path=S.PATH_PREFILL, out=outs)
         torch.cuda.synchronize()
-        log(f"profile workload: {n} done")
+        log(f"profile workload: {'|'.join(launch)} done")
 
 
 def _db_rows(db, sql):
@@ -685,7 +745,8 @@ def summarize(trace_db, fetch_db, write_db):
            "Command (repo root, MI355X):", "",
            "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run -- "
            "python3 bench.py --steps 3 --warmup 1 --no-cpu --no-extra", "",
-           "Four passes of the step (one warm-up, three timed) over the seven projections.", "",
+           "Four passes of the step (one warm-up, three timed) over the seven projections, in four "
+           "GEMM launches (q|k|v and gate|up each one splice_gemm_multi launch).", "",
            "| kernel | calls | avg us | total ms | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
     for name, n, avg, tot, mn, mx in rows:
         out.append(f"| `{name[:90]}` | {n} | {avg / 1e3:.2f} | {tot / 1e6:.3f} | {mn / 1e3:.2f} | "
@@ -712,11 +773,17 @@ def summarize(trace_db, fetch_db, write_db):
     cw = copy_kib / float(np.mean(pick(write, "MulFunctor")))
     gf = pick(fetch, "prefill")
     gw = pick(write, "prefill")
-    # algorithmic bytes of the seven projections: codes, scales and side columns
-    # of X and W read once, Y written once
+    # algorithmic bytes of the four launches: codes, scales and side columns of
+    # X and of every W read once, Y written once
     from fp4_gemm_sparse_amd.synth import QWEN3_8B
-    alg = [M_PREFILL * K * (0.5 + 1 / 16) + 2 * M_PREFILL * K_PROT + N * K * (0.5 + 1 / 16)
-           + 2 * N * K_PROT + 4 * M_PREFILL * N for K, N in QWEN3_8B.values()]
+    alg = []
+    for launch in LAUNCHES:
+        K = QWEN3_8B[launch[0]][0]
+        b = M_PREFILL * K * (0.5 + 1 / 16) + 2 * M_PREFILL * K_PROT
+        for n in launch:
+            N = QWEN3_8B[n][1]
+            b += N * K * (0.5 + 1 / 16) + 2 * N * K_PROT + 4 * M_PREFILL * N
+        alg.append(b)
     f_b = float(np.mean(gf)) * cf * 1024
     w_b = float(np.mean(gw)) * cw * 1024
     out = ["# HBM traffic: prefill SpliceGEMM, Qwen3-8B layer projections (M = 8192, k = 64)", "",
@@ -729,7 +796,8 @@ def summarize(trace_db, fetch_db, write_db):
            "gpurun_out/pmc_write/run_results.db", "",
            f"Calibration: fp32 multiply-by-one over {COPY_ELEMS} elements ({copy_kib:.0f} KiB read, "
            f"{copy_kib:.0f} KiB written); FETCH_SIZE scale {cf:.4f}, WRITE_SIZE scale {cw:.4f}.",
-           f"Prefill SpliceGEMM dispatches: {len(gf)} (3 per projection, 7 projections).", "",
+           f"Prefill SpliceGEMM dispatches: {len(gf)} (3 per launch; 4 launches: q|k|v, o, "
+           "gate|up, down).", "",
            f"- fetch_bytes_per_launch: {f_b:.0f}",
            f"- write_bytes_per_launch: {w_b:.0f}",
            f"- hbm_bytes_per_launch: {f_b + w_b:.0f}",
