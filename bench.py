@@ -74,7 +74,7 @@ def kernel_source_hash():
     so a comment edit does not void counter figures taken on the same code."""
     import re
     h = hashlib.sha256()
-    for f in ("common.hpp", "gemm.hip"):
+    for f in ("common.hpp", "segments.hpp", "gemm.hip"):
         src = open(os.path.join(ROOT, "fp4_gemm_sparse_amd", "csrc", f)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         src = re.sub(r"//[^\n]*", "", src)
@@ -475,11 +475,14 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         "shapes": fz}
 
     # ---------------- the decode layer in four launches: q|k|v and gate|up
-    # each in one splice_gemm_multi call (sets of the packed weights walked in
-    # turn, as above), against the seven single calls measured above
+    # each in one splice_gemm_multi call, o and down alone (sets of the packed
+    # weights walked in turn, as above), against the seven single calls
+    # measured above; for M <= FUSED_MAX_M also with the activation
+    # preparation: one quantize per input then the four launches, against the
+    # four fused-preparation launches
     lay = {}
-    for M in DECODE_MS:
-        t4 = b4 = 0.0
+    for M in sorted(set(DECODE_MS) | set(FUSED_MS)):
+        t4 = b4 = t2p = tfp = 0.0
         per = {}
         for launch in LAUNCHES:
             p0 = P[launch[0]]
@@ -494,29 +497,52 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             sets += [[(P[n]["wpack"][0].clone(), P[n]["wpack"][1].clone(), P[n]["aw"],
                        P[n]["wpack"][2].clone()) for n in launch] for _ in range(nset - 1)]
 
-            def call(i):
+            def gemm(i):
                 w = sets[i % nset]
                 if len(launch) == 1:
                     S.splice_gemm(xq[0], xq[1], p0["ax"], xq[2], *w[0], out=Ys[0])
                 else:
                     S.splice_gemm_multi(xq[0], xq[1], p0["ax"], xq[2], w, out=Ys)
-            t = graph_timed(torch, call, max(args.decode_iters, nset))
+
+            def two(i):
+                S.quantize_nvfp4(X, p0["idx"], p0["ax"], out=xq)
+                gemm(i)
+
+            def fused(i):
+                S.splice_gemm_decode_fused_multi(X, p0["idx"], p0["ax"], sets[i % nset], out=Ys)
+            iters = max(args.decode_iters, nset)
+            key = "|".join(launch)
+            if M in DECODE_MS:
+                t = graph_timed(torch, gemm, iters)
+                per[key] = round(t * 1e3, 2)
+                t4 += t
+                b4 += (M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
+                       + sum(P[n]["N"] * K * (0.5 + 1 / 16) + 2 * P[n]["N"] * K_PROT + 4 * M * P[n]["N"]
+                             for n in launch))
+            if M in FUSED_MS:
+                a2, af = graph_timed_pair(torch, two, fused, iters)
+                t2p += a2
+                tfp += af
             del sets
             torch.cuda.empty_cache()
-            per["|".join(launch)] = round(t * 1e3, 2)
-            t4 += t
-            b4 += (M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
-                   + sum(P[n]["N"] * K * (0.5 + 1 / 16) + 2 * P[n]["N"] * K_PROT + 4 * M * P[n]["N"]
-                         for n in launch))
-        t7 = sum(dec[f"{n}@M{M}"]["us"] for n in names) * 1e-3
-        lay[f"M{M}"] = {"us_four_launches": round(t4 * 1e3, 2), "us_seven_launches": round(t7 * 1e3, 2),
-                        "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
-                        "frac_hbm": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                        "launches_us": per}
-        log(f"decode layer in four launches M={M}: {lay[f'M{M}']}")
+        r = {}
+        if M in DECODE_MS:
+            t7 = sum(dec[f"{n}@M{M}"]["us"] for n in names) * 1e-3
+            r.update({"us_four_launches": round(t4 * 1e3, 2), "us_seven_launches": round(t7 * 1e3, 2),
+                      "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "launches_us": per})
+        if M in FUSED_MS:
+            r.update({"us_with_prep_two_call": round(t2p * 1e3, 2),
+                      "us_with_prep_fused": round(tfp * 1e3, 2),
+                      "prep_fused_speedup": round(t2p / tfp, 3)})
+        lay[f"M{M}"] = r
+        log(f"decode layer in four launches M={M}: {r}")
     out["decode_layer_four_launches"] = {
         "timing": "as for decode; q|k|v and gate|up each one splice_gemm_multi launch, o and down "
-                  "one splice_gemm each; activation bytes counted once per launch",
+                  "one splice_gemm each; activation bytes counted once per launch. With preparation: "
+                  "quantize + GEMM per input against splice_gemm_decode_fused_multi (one launch per "
+                  "input), timed in alternation",
         "shapes": lay}
 
     # ---------------- grouped MoE stand-in

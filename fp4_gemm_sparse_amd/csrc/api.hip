@@ -252,6 +252,44 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
     return hip_status(launch_gemm_fused(a, hs(stream)));
 }
 
+int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t *idx,
+                                   const float *alpha_x, int64_t M, int64_t K, int32_t k,
+                                   const splice_weight_seg *segs, int32_t nseg, splice_stream_t stream)
+{
+    if (nseg < 1 || nseg > SPLICE_SEG_MAX || !segs) return SPLICE_ERR_INVALID_ARG;
+    GemmSeg seg[SEG_MAX];
+    int64_t total = 0;
+    for (int32_t i = 0; i < nseg; i++) {
+        const splice_weight_seg &w = segs[i];
+        // each segment as its own fused call would be checked
+        if (M < 0 || w.N < 0) return SPLICE_ERR_INVALID_ARG;
+        int rc = check_k(K, k);
+        if (rc) return rc;
+        if (M > SPLICE_FUSED_MAX_M) return SPLICE_ERR_UNSUPPORTED;
+        if (M > 0 && w.N > 0) {
+            if (!w.Y || !alpha_x || !w.alpha_w || w.ldy < w.N) return SPLICE_ERR_INVALID_ARG;
+            if (!aligned(w.Y, 4) || !aligned(alpha_x, 4) || !aligned(w.alpha_w, 4))
+                return SPLICE_ERR_INVALID_ARG;
+            if (K > 0) {
+                if (!X || !w.Wq || !w.Ws || ldx < K || (k > 0 && (!idx || !w.W_S)))
+                    return SPLICE_ERR_INVALID_ARG;
+                if (!fused_decode_ok(M, K)) return SPLICE_ERR_UNSUPPORTED;
+                if (!aligned(X, 16) || ldx % 8 != 0) return SPLICE_ERR_UNSUPPORTED;
+                if (!aligned(w.Wq, 16) || !aligned(w.Ws, 8) || (k > 0 && !aligned(idx, 4)))
+                    return SPLICE_ERR_INVALID_ARG;
+                if (k > 0 && !aligned(w.W_S, (k % 8 == 0) ? 16 : 2)) return SPLICE_ERR_INVALID_ARG;
+            }
+        }
+        seg[i] = GemmSeg{w.Wq, w.Ws, w.alpha_w, w.W_S, w.Y, w.ldy, w.N};
+        total += w.N;
+    }
+    if (total > (int64_t)1 << 30) return SPLICE_ERR_UNSUPPORTED;
+    if (M == 0 || total == 0) return SPLICE_OK;
+    GemmArgs base{nullptr, nullptr, alpha_x, nullptr, nullptr, nullptr, nullptr, nullptr, M, total, K, k,
+                  nullptr, 0, X, ldx, idx};
+    return hip_status(launch_gemm_fused_seg(base, seg, nseg, hs(stream)));
+}
+
 int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *len, float log_tau,
                       int64_t k1_num, int64_t k1_den, int64_t k2, uint8_t *keep, int32_t *g1,
                       int32_t *g2, float *adv, int64_t adv_cols, int64_t lda,

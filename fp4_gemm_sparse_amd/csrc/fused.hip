@@ -28,6 +28,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "nvfp4.hpp"
+#include "segments.hpp"
 
 namespace splice {
 
@@ -56,7 +57,7 @@ __device__ __forceinline__ bf16x8 gather_side8(const uint16_t *row, const int32_
 }  // namespace
 
 template <int NW, int CPW, int CB, int XPT, bool TAIL>
-__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
+__device__ __forceinline__ void decode_fused_body(const GemmArgs &a, int64_t blk)
 {
     // [M][K] FP16 activations, then [NW][CB][64] f32x4 partial sums (the
     // protected-channel mask, and idx when k <= 64, use that space until the
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t rowb = K / 2, rows = K / 16, nb = K / 16;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * CB);
+    const int64_t n0 = blk * (16 * CB);
     const int nchunk = (int)(K / FBK);
     const int k = a.k;
     const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
@@ -260,40 +261,64 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
     }
 }
 
+template <int NW, int CPW, int CB, int XPT, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(GemmArgs a)
+{
+    decode_fused_body<NW, CPW, CB, XPT, TAIL>(a, blockIdx.x);
+}
+
+// over column segments (the projections that read the same rows of X)
+template <int NW, int CPW, int CB, int XPT, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode_fused_seg_kernel(SegTable t)
+{
+    int local;
+    const GemmArgs a = seg_args(t, blockIdx.x, local);
+    decode_fused_body<NW, CPW, CB, XPT, TAIL>(a, local);
+}
+
+template <int NW, int CPW, int CB, int XPT, bool TAIL>
+static hipError_t launch_fused(const GemmArgs &a, const SegSpec *sp, size_t lds, int lds_max, hipStream_t s)
+{
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&decode_fused_kernel<NW, CPW, CB, XPT, TAIL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+    static const hipError_t attr_seg = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&decode_fused_seg_kernel<NW, CPW, CB, XPT, TAIL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+    if (attr != hipSuccess) return attr;
+    if (attr_seg != hipSuccess) return attr_seg;
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, 16 * CB);
+        hipLaunchKernelGGL((decode_fused_seg_kernel<NW, CPW, CB, XPT, TAIL>), dim3((unsigned)t.start[t.nseg]),
+                           dim3(64 * NW), lds, s, t);
+    } else {
+        hipLaunchKernelGGL((decode_fused_kernel<NW, CPW, CB, XPT, TAIL>),
+                           dim3((unsigned)((a.N + 16 * CB - 1) / (16 * CB))), dim3(64 * NW), lds, s, a);
+    }
+    return hipGetLastError();
+}
+
 template <int NW, int CPW, int CB, int XPT>
-static hipError_t run_fused_x(const GemmArgs &a, hipStream_t s)
+static hipError_t run_fused_x(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     constexpr int red_bytes = NW * CB * WAVE * 16;
     constexpr int side_bytes = (CB * 16 + 4) * 128;                  // W_S and X_S tiles, k <= 64
     constexpr int lds_max = 4 * (NW * CPW * FBK) * 2 + red_bytes + side_bytes;   // largest M and K
     static_assert(lds_max <= F_LDS, "fused decode LDS budget");
     const size_t lds = (size_t)((a.M * a.K * 2 + 15) & ~(int64_t)15) + red_bytes + (a.k > 0 ? side_bytes : 0);
-    const dim3 grid((unsigned)((a.N + 16 * CB - 1) / (16 * CB)));
-    if (a.k > 0) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_fused_kernel<NW, CPW, CB, XPT, true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((decode_fused_kernel<NW, CPW, CB, XPT, true>), grid, dim3(64 * NW), lds, s, a);
-    } else {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_fused_kernel<NW, CPW, CB, XPT, false>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((decode_fused_kernel<NW, CPW, CB, XPT, false>), grid, dim3(64 * NW), lds, s, a);
-    }
-    return hipGetLastError();
+    if (a.k > 0) return launch_fused<NW, CPW, CB, XPT, true>(a, sp, lds, lds_max, s);
+    return launch_fused<NW, CPW, CB, XPT, false>(a, sp, lds, lds_max, s);
 }
 
 // half blocks of X per thread loaded ahead of the weights: all of them when
 // they are at most four, else the first four
 template <int NW, int CPW, int CB>
-static hipError_t run_fused(const GemmArgs &a, hipStream_t s)
+static hipError_t run_fused(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     const int64_t items = a.M * a.K / 8;
-    if (items <= 64 * NW) return run_fused_x<NW, CPW, CB, 1>(a, s);
-    if (items <= 2 * 64 * NW) return run_fused_x<NW, CPW, CB, 2>(a, s);
-    return run_fused_x<NW, CPW, CB, 4>(a, s);
+    if (items <= 64 * NW) return run_fused_x<NW, CPW, CB, 1>(a, sp, s);
+    if (items <= 2 * 64 * NW) return run_fused_x<NW, CPW, CB, 2>(a, sp, s);
+    return run_fused_x<NW, CPW, CB, 4>(a, sp, s);
 }
 
 // The FP16 copy of the M rows must fit the LDS budget and K must be whole
@@ -309,19 +334,36 @@ bool fused_decode_ok(int64_t M, int64_t K)
 // chunks, which spreads their larger preparation over twice the lanes, and
 // 48 columns per workgroup for wide N, so that fewer workgroups repeat it.
 // Larger K: the two-call kernel's configurations.
+// configuration choice for a.N columns (the sum of the widths when sp is set)
+static hipError_t dispatch_fused(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
+{
+    const int nchunk = (int)(a.K / FBK);
+    const int64_t colblocks = (a.N + 15) / 16;
+    if (nchunk <= 8 * 4) {
+        if (a.M == 1) return run_fused<8, 4, 1>(a, sp, s);
+        return colblocks >= 512 ? run_fused<16, 2, 3>(a, sp, s) : run_fused<16, 2, 1>(a, sp, s);
+    }
+    if (nchunk <= 16 * 4) return run_fused<16, 4, 1>(a, sp, s);
+    if (nchunk <= 16 * 6) return run_fused<16, 6, 1>(a, sp, s);
+    return run_fused<16, 8, 1>(a, sp, s);
+}
+
 hipError_t launch_gemm_fused(const GemmArgs &a, hipStream_t s)
 {
     if (a.M == 0 || a.N == 0) return hipSuccess;
     if (a.K == 0) return launch_gemm(Path::Prefill, a, nullptr, 0, s);   // Y = 0 (k <= K)
-    const int nchunk = (int)(a.K / FBK);
-    const int64_t colblocks = (a.N + 15) / 16;
-    if (nchunk <= 8 * 4) {
-        if (a.M == 1) return run_fused<8, 4, 1>(a, s);
-        return colblocks >= 512 ? run_fused<16, 2, 3>(a, s) : run_fused<16, 2, 1>(a, s);
-    }
-    if (nchunk <= 16 * 4) return run_fused<16, 4, 1>(a, s);
-    if (nchunk <= 16 * 6) return run_fused<16, 6, 1>(a, s);
-    return run_fused<16, 8, 1>(a, s);
+    return dispatch_fused(a, nullptr, s);
+}
+
+hipError_t launch_gemm_fused_seg(const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s)
+{
+    GemmArgs b = a;
+    b.N = 0;
+    for (int i = 0; i < nseg; i++) b.N += seg[i].N;
+    if (nseg == 0 || b.M == 0 || b.N == 0) return hipSuccess;
+    if (b.K == 0) return launch_gemm_seg(Path::Prefill, b, seg, nseg, s);   // Y = 0 (k <= K)
+    const SegSpec sp{seg, nseg};
+    return dispatch_fused(b, &sp, s);
 }
 
 }  // namespace splice

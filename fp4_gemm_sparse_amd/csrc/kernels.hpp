@@ -62,6 +62,8 @@ struct SegSpec {
 // with each segment's weights, in one launch (a's weight and output fields
 // are ignored); 1 <= nseg <= SEG_MAX
 hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s);
+// launch_gemm_fused over column segments (a's weight and output fields ignored)
+hipError_t launch_gemm_fused_seg(const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s);
 // independent products sharing N, K and k (groups[i].N/K/k equal), one launch
 // per 32 groups; groups with M == 0 are skipped
 hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s);

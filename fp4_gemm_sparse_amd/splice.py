@@ -79,6 +79,8 @@ _SIGS = {
     "splice_grouped_workspace_size": (_sz, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32]),
     "splice_gemm_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, ctypes.POINTER(_Seg),
                                          _i32, ctypes.c_int, _vp]),
+    "splice_gemm_decode_fused_multi": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i32,
+                                                      ctypes.POINTER(_Seg), _i32, _vp]),
 }
 
 _lib = None
@@ -332,6 +334,25 @@ def splice_gemm_multi(Xq, Xs, alpha_x, X_S, weights, path=PATH_AUTO, out=None):
     _check("splice_gemm_multi",
            lib().splice_gemm_multi(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, M, K, k, arr,
                                    len(weights), path, _stream()))
+    return out
+
+
+def splice_gemm_decode_fused_multi(X, idx, alpha_x, weights, out=None):
+    """splice_gemm_decode_fused over several weight packs in one launch.
+    weights: list of (Wq, Ws, alpha_w, W_S); out: list of fp32 [M, N_i] or None."""
+    X = _bf16(X)
+    M, K = X.shape
+    idx = _idx(idx, X.device)
+    k = idx.numel()
+    if out is None:
+        out = [torch.empty(M, w[0].shape[0], dtype=torch.float32, device=X.device) for w in weights]
+    arr = (_Seg * max(len(weights), 1))()
+    for i, (w, Y) in enumerate(zip(weights, out)):
+        arr[i] = _Seg(_p(w[0]), _p(w[1]), _p(w[2]), _p(w[3]) if k else None, w[0].shape[0], _p(Y),
+                      Y.stride(0))
+    _check("splice_gemm_decode_fused_multi",
+           lib().splice_gemm_decode_fused_multi(_p(X), X.stride(0), _p(idx) if k else None, _p(alpha_x),
+                                                M, K, k, arr, len(weights), _stream()))
     return out
 
 

@@ -240,6 +240,19 @@ int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x
                       int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs, int32_t nseg,
                       int path, splice_stream_t stream);
 
+/* splice_gemm_decode_fused over column segments: the bf16 rows X (M <=
+ * SPLICE_FUSED_MAX_M), idx and alpha_x as for splice_gemm_decode_fused,
+ * shared; segs a HOST array of nseg (1 .. SPLICE_SEG_MAX) weight segments as
+ * for splice_gemm_multi.  One launch prepares X in every workgroup and
+ * multiplies it by the workgroup's segment.  Each segment's Y equals
+ * splice_gemm_decode_fused's for that segment alone wherever that call
+ * would pick the same configuration (the choice depends on the combined width
+ * only through the 48-column form for wide products); within the GEMM
+ * tolerance otherwise.  Errors as splice_gemm_decode_fused, per segment. */
+int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t *idx,
+                                   const float *alpha_x, int64_t M, int64_t K, int32_t k,
+                                   const splice_weight_seg *segs, int32_t nseg, splice_stream_t stream);
+
 /* Workspace bytes splice_gemm / nvfp4_gemm need for this shape (k is
  * ignored by the current kernels but part of the contract). */
 size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(L):
     names = splice.header_functions()
     assert {"splice_select_channels", "splice_quantize_nvfp4", "splice_gemm", "nvfp4_gemm",
             "splice_compute_alpha", "splice_gemm_grouped", "splice_workspace_size",
-            "splice_gemm_multi"} <= set(names)
+            "splice_gemm_multi", "splice_gemm_decode_fused_multi"} <= set(names)
     for n in names:
         assert getattr(L, n) is not None
 
@@ -149,6 +149,25 @@ def test_multi_argument_errors(L):
     assert call(one, 1, M=0) == splice.OK                                # nothing to do
     empty = (S * 2)(S(None, None, None, None, 0, None, 0), S(None, None, None, None, 0, None, 0))
     assert call(empty, 2) == splice.OK                                   # zero widths
+
+
+def test_fused_multi_argument_errors(L):
+    S = splice._Seg
+    good = S(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 64)
+
+    def call(segs, n, M=1, K=1024, k=8, X=FAKE, ldx=1024):
+        return L.splice_gemm_decode_fused_multi(X, ldx, FAKE, FAKE, M, K, k, segs, n, None)
+    one = (S * 1)(good)
+    assert call(one, 0) == splice.ERR_INVALID_ARG
+    assert call(one, splice.SEG_MAX + 1) == splice.ERR_INVALID_ARG
+    assert call(None, 1) == splice.ERR_INVALID_ARG
+    assert call(one, 1, M=splice.FUSED_MAX_M + 1) == splice.ERR_UNSUPPORTED
+    assert call(one, 1, X=None) == splice.ERR_INVALID_ARG
+    assert call(one, 1, ldx=1000) == splice.ERR_INVALID_ARG
+    assert call(one, 1, K=1040, ldx=1040) == splice.ERR_UNSUPPORTED     # K % 128
+    two = (S * 2)(good, S(FAKE, FAKE, FAKE, None, 64, FAKE, 64))        # k > 0 without W_S
+    assert call(two, 2) == splice.ERR_INVALID_ARG
+    assert call(one, 1, M=0) == splice.OK
 
 
 def fused(L, M=1, N=64, K=1024, k=8, **over):

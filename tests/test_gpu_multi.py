@@ -145,3 +145,51 @@ def test_multi_in_hip_graph():
         torch.cuda.synchronize()
         for a, b in zip(outs, ref):
             assert torch.equal(a, b), f"replay {r}"
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("group", ["qkv", "gate_up"])
+def test_fused_prep_layer_groups(M, group):
+    """The fused-preparation decode over the projections of one input: the
+    bits of splice_gemm_decode_fused per projection (same configuration), and
+    the oracle's product on sampled columns."""
+    names = ["q", "k", "v"] if group == "qkv" else ["gate", "up"]
+    K = synth.QWEN3_8B[names[0]][0]
+    g = np.random.default_rng(9)
+    X = synth.activations(synth.CFG_DECODE, 0, M, K, 3, "student")
+    Ws = [synth.to_bf16(g.normal(0, 0.02, (synth.QWEN3_8B[n][1], K))) for n in names]
+    xq, ax, wp = packs(X, Ws, 64, 2)
+    idx = packs.idx
+    Xd = dev(X)
+    Ym = S.splice_gemm_decode_fused_multi(Xd, idx, ax, wp)
+    Yf = [S.splice_gemm_decode_fused(Xd, idx, ax, *w) for w in wp]
+    torch.cuda.synchronize()
+    xo = O.quantize_nvfp4(X, host(idx), np.float32(ax.item()))
+    for i, (n, a, b) in enumerate(zip(names, Ym, Yf)):
+        widths = [w[0].shape[0] for w in wp]
+        if same_config(M, widths, S.PATH_DECODE):
+            assert torch.equal(a, b), f"{group} M={M}: {n}"
+        cols = np.arange(0, widths[i], 97)
+        wq, ws, aw, wS = (host(wp[i][0])[cols], host(wp[i][1])[cols], np.float32(wp[i][2].item()),
+                          host(wp[i][3])[cols])
+        Yo = O.splice_gemm(xo[0], xo[1], np.float32(ax.item()), xo[2], wq, ws, aw, wS)
+        assert_gemm_close(host(a)[:, cols], Yo, f"{group} M={M}: {n} vs oracle")
+
+
+def test_fused_prep_ragged_segments():
+    """Ragged widths, one empty, K = 256 and 1024, against the per-segment
+    fused call."""
+    g = np.random.default_rng(4)
+    for M, K in ((1, 256), (3, 1024), (4, 1024)):
+        widths = [40, 0, 130, 16]
+        X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
+        Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
+        xq, ax, wp = packs(X, Ws, 8, 5)
+        idx = packs.idx
+        Xd = dev(X)
+        Ym = S.splice_gemm_decode_fused_multi(Xd, idx, ax, wp)
+        Yf = [S.splice_gemm_decode_fused(Xd, idx, ax, *w) for w in wp]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(Ym, Yf)):
+            assert a.shape == (M, widths[i])
+            assert torch.equal(a, b), f"M={M} K={K} segment {i}"
