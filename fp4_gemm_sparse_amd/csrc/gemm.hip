@@ -847,7 +847,7 @@ constexpr int XLDS_MAX = 64 * 1024;        // bytes of FP16 activations kept in 
 
 // SIDE: 0 for k = 0; 1 for k = 32 or 64 (side tiles staged through LDS);
 // 2 for any other k (side operands loaded in the epilogue).
-template <int NW, int CPW, int SIDE>
+template <int NW, int CPW, int SIDE, int XPT>
 __device__ __forceinline__ void decode_xlds_body(const GemmArgs &a, int64_t blk)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];   // [M][K] f16, then reduction space
@@ -859,13 +859,19 @@ __device__ __forceinline__ void decode_xlds_body(const GemmArgs &a, int64_t blk)
     const int64_t n0 = blk * 16;
     const int nchunk = (int)(K / BK);
 
-    // the thread's first activation block (codes and scale) is loaded ahead
-    // of the weights: loads complete in issue order, so the decode into LDS
-    // below need not wait for the weight stream
+    // the thread's first XPT activation blocks (codes and scale) are loaded
+    // ahead of the weights: loads complete in issue order, so the decode into
+    // LDS below need not wait for the weight stream
     const int64_t nbx = K / 16;
-    const int64_t it0 = tid < M * nbx ? tid : 0;
-    const u32x2 xc0 = *reinterpret_cast<const u32x2 *>(a.Xq + (it0 / nbx) * rowb + (it0 % nbx) * 8);
-    const unsigned xs0 = a.Xs[(it0 / nbx) * rows + it0 % nbx];
+    u32x2 xc[XPT];
+    unsigned xsb[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; j++) {
+        const int64_t it = tid + (int64_t)j * 64 * NW;
+        const int64_t itc = it < M * nbx ? it : 0;
+        xc[j] = *reinterpret_cast<const u32x2 *>(a.Xq + (itc / nbx) * rowb + (itc % nbx) * 8);
+        xsb[j] = a.Xs[(itc / nbx) * rows + itc % nbx];
+    }
     __builtin_amdgcn_sched_barrier(0);     // keep these loads ahead of the weight loads
 
     // weights of this wave: chunks [c0, c0 + CPW) of each of its 16 rows,
@@ -909,13 +915,21 @@ __device__ __forceinline__ void decode_xlds_body(const GemmArgs &a, int64_t blk)
     // decode the M activation rows into LDS: one 16-channel block per item
     {
         const int64_t nb = K / 16;
-        for (int64_t it = tid; it < M * nb; it += 64 * NW) {
+        auto put = [&](int64_t it, u32x2 c, unsigned sbyte) {
             const int64_t m = it / nb, b = it - m * nb;
-            const u32x2 c = (it == tid) ? xc0 : *reinterpret_cast<const u32x2 *>(a.Xq + m * rowb + b * 8);
-            const f16x2 sc = e4m3_pair((it == tid) ? xs0 : a.Xs[m * rows + b]);
+            const f16x2 sc = e4m3_pair(sbyte);
             f16x8 *dst = reinterpret_cast<f16x8 *>(xl + (m * K + b * 16) * 2);
             dst[0] = decode8(c.x, sc);
             dst[1] = decode8(c.y, sc);
+        };
+#pragma unroll
+        for (int j = 0; j < XPT; j++) {
+            const int64_t it = tid + (int64_t)j * 64 * NW;
+            if (it < M * nb) put(it, xc[j], xsb[j]);
+        }
+        for (int64_t it = tid + (int64_t)XPT * 64 * NW; it < M * nb; it += 64 * NW) {
+            const int64_t m = it / nb, b = it - m * nb;
+            put(it, *reinterpret_cast<const u32x2 *>(a.Xq + m * rowb + b * 8), a.Xs[m * rows + b]);
         }
     }
     const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
@@ -1001,41 +1015,50 @@ __device__ __forceinline__ void decode_xlds_body(const GemmArgs &a, int64_t blk)
     }
 }
 
-template <int NW, int CPW, int SIDE>
+template <int NW, int CPW, int SIDE, int XPT>
 __global__ __launch_bounds__(64 * NW) void decode_xlds_kernel(GemmArgs a)
 {
-    decode_xlds_body<NW, CPW, SIDE>(a, blockIdx.x);
+    decode_xlds_body<NW, CPW, SIDE, XPT>(a, blockIdx.x);
 }
 
-template <int NW, int CPW, int SIDE>
+template <int NW, int CPW, int SIDE, int XPT>
 __global__ __launch_bounds__(64 * NW) void decode_xlds_seg_kernel(SegTable t)
 {
     int local;
     const GemmArgs a = seg_args(t, blockIdx.x, local);
-    decode_xlds_body<NW, CPW, SIDE>(a, local);
+    decode_xlds_body<NW, CPW, SIDE, XPT>(a, local);
 }
 
-template <int NW, int CPW, int SIDE>
-static hipError_t launch_xlds(const GemmArgs &a, const SegSpec *sp, size_t lds, hipStream_t s)
+template <int NW, int CPW, int SIDE, int XPT>
+static hipError_t launch_xlds_x(const GemmArgs &a, const SegSpec *sp, size_t lds, hipStream_t s)
 {
     constexpr int LDS_ATTR = XLDS_MAX + 16 * WAVE * 16 + 20 * 128;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, SIDE>),
+        reinterpret_cast<const void *>(&decode_xlds_kernel<NW, CPW, SIDE, XPT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_ATTR);
     static const hipError_t attr_seg = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_xlds_seg_kernel<NW, CPW, SIDE>),
+        reinterpret_cast<const void *>(&decode_xlds_seg_kernel<NW, CPW, SIDE, XPT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_ATTR);
     if (attr != hipSuccess) return attr;
     if (attr_seg != hipSuccess) return attr_seg;
     if (sp) {
         const SegTable t = make_seg_table(a, *sp, 16);
-        hipLaunchKernelGGL((decode_xlds_seg_kernel<NW, CPW, SIDE>), dim3((unsigned)t.start[t.nseg]),
+        hipLaunchKernelGGL((decode_xlds_seg_kernel<NW, CPW, SIDE, XPT>), dim3((unsigned)t.start[t.nseg]),
                            dim3(64 * NW), lds, s, t);
     } else {
-        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, SIDE>), dim3((unsigned)((a.N + 15) / 16)),
+        hipLaunchKernelGGL((decode_xlds_kernel<NW, CPW, SIDE, XPT>), dim3((unsigned)((a.N + 15) / 16)),
                            dim3(64 * NW), lds, s, a);
     }
     return hipGetLastError();
+}
+
+// activation blocks per thread loaded ahead of the weights: all of them when
+// they are at most two per thread (the rest, if any, behind the weights)
+template <int NW, int CPW, int SIDE>
+static hipError_t launch_xlds(const GemmArgs &a, const SegSpec *sp, size_t lds, hipStream_t s)
+{
+    if (a.M * a.K / 16 <= 64 * NW) return launch_xlds_x<NW, CPW, SIDE, 1>(a, sp, lds, s);
+    return launch_xlds_x<NW, CPW, SIDE, 2>(a, sp, lds, s);
 }
 
 template <int NW, int CPW>
