@@ -482,7 +482,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     # four fused-preparation launches
     lay = {}
     for M in sorted(set(DECODE_MS) | set(FUSED_MS)):
-        t4 = b4 = t2p = tfp = 0.0
+        t4 = t4n = b4 = t2p = tfp = 0.0
         per = {}
         for launch in LAUNCHES:
             p0 = P[launch[0]]
@@ -504,6 +504,15 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                 else:
                     S.splice_gemm_multi(xq[0], xq[1], p0["ax"], xq[2], w, out=Ys)
 
+            def gemm_nv(i):
+                # the uncompensated NVFP4 product on the same packs (k = 0)
+                w = sets[i % nset]
+                if len(launch) == 1:
+                    S.nvfp4_gemm(xq[0], xq[1], p0["ax"], w[0][0], w[0][1], w[0][2], out=Ys[0])
+                else:
+                    S.splice_gemm_multi(xq[0], xq[1], p0["ax"], None, [(q[0], q[1], q[2], None) for q in w],
+                                        out=Ys)
+
             def two(i):
                 S.quantize_nvfp4(X, p0["idx"], p0["ax"], out=xq)
                 gemm(i)
@@ -513,9 +522,10 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             iters = max(args.decode_iters, nset)
             key = "|".join(launch)
             if M in DECODE_MS:
-                t = graph_timed(torch, gemm, iters)
+                t, tn = graph_timed_pair(torch, gemm, gemm_nv, iters)
                 per[key] = round(t * 1e3, 2)
                 t4 += t
+                t4n += tn
                 b4 += (M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
                        + sum(P[n]["N"] * K * (0.5 + 1 / 16) + 2 * P[n]["N"] * K_PROT + 4 * M * P[n]["N"]
                              for n in launch))
@@ -529,6 +539,8 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         if M in DECODE_MS:
             t7 = sum(dec[f"{n}@M{M}"]["us"] for n in names) * 1e-3
             r.update({"us_four_launches": round(t4 * 1e3, 2), "us_seven_launches": round(t7 * 1e3, 2),
+                      "us_four_launches_nvfp4": round(t4n * 1e3, 2),
+                      "overhead_pct": round(100.0 * (t4 - t4n) / t4n, 2),
                       "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
                       "frac_hbm": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                       "launches_us": per})
