@@ -66,6 +66,8 @@ def parse():
                     help="write the profiles/ summaries from rocprofv3 result databases")
     ap.add_argument("--summarize-extras", metavar="TRACE_DB",
                     help="write the profiles/ kernel-time summary of a full run (all extras)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DB",
+                    help="write the profiles/ summary of SQ counter passes over --profile-workload")
     return ap.parse_args()
 
 
@@ -89,6 +91,9 @@ def main():
         return
     if args.summarize_extras:
         summarize_extras(args.summarize_extras)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
@@ -844,6 +849,63 @@ def summarize(trace_db, fetch_db, write_db):
     path = TRAFFIC_FILE
     open(path, "w").write("\n".join(out) + "\n")
     print("wrote", path)
+
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "prefill_splice_gemm_counters_qwen3_8b.md")
+COUNTER_PASSES = (
+    "SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
+    "SQ_INSTS_VALU SQ_INSTS_LDS SQ_WAVES GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_WAVE_CYCLES "
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE",
+)
+
+
+def summarize_counters(dbs):
+    """Per-dispatch averages of SQ counters for the prefill SpliceGEMM launches
+    of --profile-workload (one rocprofv3 --pmc pass per database)."""
+    vals = {}
+    for db in dbs:
+        r = _db_rows(db, "select kernel_name, dispatch_id, counter_name, sum(value) from "
+                         "counters_collection group by kernel_name, dispatch_id, counter_name")
+        for name, _, cname, v in r:
+            if "prefill" in name:
+                vals.setdefault(cname, []).append(v)
+    avg = {c: float(np.mean(v)) for c, v in vals.items()}
+    from fp4_gemm_sparse_amd.synth import QWEN3_8B
+    flops = np.mean([sum(2.0 * M_PREFILL * QWEN3_8B[n][1] * QWEN3_8B[n][0] for n in launch)
+                     for launch in LAUNCHES])
+    out = ["# SQ counters: prefill SpliceGEMM, Qwen3-8B layer launches (M = 8192, k = 64)", "",
+           "Commands (repo root, MI355X), one counter pass each:", ""]
+    for i, ps in enumerate(COUNTER_PASSES):
+        out.append(f"    rocprofv3 --pmc {ps} -d gpurun_out/pmc_sq{i} -o run -- python3 bench.py "
+                   "--profile-workload")
+    out += ["    python3 bench.py --summarize-counters gpurun_out/pmc_sq0/run_results.db "
+            "gpurun_out/pmc_sq1/run_results.db", "",
+            "Averages per dispatch over the 12 prefill GEMM dispatches (3 per launch: q|k|v, o, "
+            "gate|up, down), summed over the GPU as the counters report them.", "",
+            "| counter | per dispatch |", "|---|---:|"]
+    for c in sorted(avg):
+        out.append(f"| {c} | {avg[c]:.4g} |")
+    mfma_expected = flops / (2 * 32 * 32 * 16)
+    out += ["", "Derived:", "",
+            f"- 32x32x16 MFMAs a launch needs on average: {mfma_expected:.4g} "
+            f"(SQ_INSTS_MFMA / that = {avg.get('SQ_INSTS_MFMA', float('nan')) / mfma_expected:.3f})"]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "SQ_BUSY_CU_CYCLES" in avg:
+        out.append(f"- SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES) = "
+                   f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * avg['SQ_BUSY_CU_CYCLES']):.3f}")
+    if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+        out.append(f"- VALU instructions (MFMA included) per MFMA: "
+                   f"{avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}; LDS instructions per MFMA: "
+                   f"{avg.get('SQ_INSTS_LDS', float('nan')) / avg['SQ_INSTS_MFMA']:.2f}")
+    if "SQ_WAIT_INST_LDS" in avg and "SQ_WAVE_CYCLES" in avg:
+        out.append(f"- SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES = {avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f}; "
+                   f"SQ_WAIT_ANY / SQ_WAVE_CYCLES = {avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg:
+        out.append(f"- SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = "
+                   f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.4f}")
+    out.append(f"- kernel_source_sha: {kernel_source_hash()}")
+    open(COUNTER_FILE, "w").write("\n".join(out) + "\n")
+    print("wrote", COUNTER_FILE)
 
 
 def summarize_extras(trace_db):
