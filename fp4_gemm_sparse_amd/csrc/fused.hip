@@ -5,16 +5,17 @@
 //
 // For M <= 4 token rows.  A workgroup owns 16*CB output channels and the
 // whole K; wave w multiplies K chunks (128 channels) w*CPW .. w*CPW+CPW-1.
-//  1. Every independent global load is issued first: the thread's half
+//  1. Every independent global load is issued first: the thread's 16-channel
 //     blocks of X, its idx entry and its share of the W_S tile ahead of the
 //     wave's weight codes and scales.  Loads complete in issue order, so the
 //     preparation can start while the weights are still on their way.
 //  2. The protected-channel mask is built in LDS from idx.
-//  3. Each 16-channel block of the M rows is masked, quantized by two lanes
-//     (eight elements each) with the scale, key and code functions of
-//     nvfp4.hpp that the quantize kernel uses, and decoded into an FP16 copy
-//     of X in LDS -- the bits the two-call form would decode from its packed
-//     codes.
+//  3. Each 16-channel block of the M rows is masked, quantized by one lane
+//     with the block functions of nvfp4.hpp that the quantize kernel uses,
+//     and decoded into an FP16 copy of X in LDS -- the bits the two-call form
+//     would decode from its packed codes.  One lane per block computes the
+//     block's scale and keys once; split over two lanes, both would compute
+//     them, which measured 5-15% slower on the Qwen3-8B shapes.
 //  4. Each wave multiplies its chunks on v_mfma_f32_16x16x32_f16 (A from the
 //     LDS copy, B decoded from registers); partial sums meet in LDS in wave
 //     order.  The waves that finish a column block add the BF16 side product
@@ -22,8 +23,9 @@
 //     thread alike and passed on through LDS: Y = fma(alpha_x*alpha_w, acc,
 //     side), as in the two-call kernel.
 // With the same wave configuration as the two-call decode kernel for few
-// rows, the chunk split, the MFMA order and the reduction order are the same,
-// and Y is bit-identical to it.  Every workgroup repeats the preparation of the
+// rows (every K <= 4096, and the larger K that kernel takes), the chunk
+// split, the MFMA order and the reduction order are the same, and Y is
+// bit-identical to it.  Every workgroup repeats the preparation of the
 // few rows: that replaces a launch and the HBM round trip of Xq/Xs/X_S.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -61,8 +63,8 @@ __device__ __forceinline__ void decode_fused_body(const GemmArgs &a, int64_t blk
 {
     // [M][K] FP16 activations, then [NW][CB][64] f32x4 partial sums (the
     // protected-channel mask, and idx when k <= 64, use that space until the
-    // main loop), then the W_S and X_S tiles.  XPT: half blocks of X per
-    // thread loaded up front.
+    // main loop), then the W_S and X_S tiles.  XPT: blocks of X per thread
+    // loaded up front.
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     constexpr int NT = 64 * NW;
     const int tid = threadIdx.x, lane = tid % WAVE;
@@ -76,17 +78,19 @@ __device__ __forceinline__ void decode_fused_body(const GemmArgs &a, int64_t blk
     const int64_t red_off = (M * K * 2 + 15) & ~(int64_t)15;
 
     // 1. independent global loads: X and idx first, then the weights
-    // half blocks of X: item i = (row, block, half) with i = 2 * (m * nb + b) + h
-    const int64_t items = 2 * M * nb;
-    auto half_ptr = [&](int64_t it) {
-        const int64_t q = it >> 1, m = q / nb;
-        return a.X + m * a.ldx + (q - m * nb) * 16 + (it & 1) * 8;
+    // blocks of X: item q = m * nb + b (fewer than 2^31: M <= 4, K <= 2^14)
+    const int items = (int)(M * nb);
+    auto blk_ptr = [&](int q) {
+        const int m = q / (int)nb;
+        return reinterpret_cast<const u32x4 *>(a.X + m * a.ldx + (int64_t)(q - m * (int)nb) * 16);
     };
-    u32x4 xv[XPT];
+    u32x4 xv[XPT][2];
 #pragma unroll
     for (int j = 0; j < XPT; j++) {
-        const int64_t it = tid + (int64_t)j * NT;
-        xv[j] = *reinterpret_cast<const u32x4 *>(half_ptr(it < items ? it : 0));
+        const int q = tid + j * NT;
+        const u32x4 *p = blk_ptr(q < items ? q : 0);
+        xv[j][0] = p[0];
+        xv[j][1] = p[1];
     }
     const int32_t my_idx = (TAIL && tid < k) ? a.idx[tid] : -1;
     // W_S tile for k = 32 or 64 (CB*16 rows x k): SWD dwords per thread,
@@ -144,28 +148,31 @@ __device__ __forceinline__ void decode_fused_body(const GemmArgs &a, int64_t blk
         __syncthreads();
     }
 
-    // 3. quantize and decode the M rows into LDS, two lanes per block (items
-    // and NT are even, so both lanes of a block are in the same iteration)
+    // 3. quantize and decode the M rows into LDS, one lane per block (block
+    // q = m * nb + b lands at byte 32 q of the [M][K] FP16 copy)
     {
         const TensorScale ts = tensor_scale(*a.alpha_x);
-        auto prep = [&](const u32x4 v, int64_t it) {
-            unsigned w[4] = {v.x, v.y, v.z, v.w};
-            const int64_t q = it >> 1, b = q % nb;
+        auto prep = [&](const u32x4 v0, const u32x4 v1, int q) {
+            Block16 x{{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w}};
             if (TAIL) {
-                const unsigned mk = (block_mask16(smask, b) >> ((it & 1) * 8)) & 0xFFu;
-                if (mk) clear_protected_half(w, mk);
+                const unsigned mk = block_mask16(smask, q % (int)nb);
+                if (mk) clear_protected(x, mk);
             }
-            unsigned c;
-            const f16x2 sc = e4m3_pair(quantize_half_block(w, ts, c));
-            *reinterpret_cast<f16x8 *>(xl + (q * 16 + (it & 1) * 8) * 2) = decode8(c, sc);
+            u32x2 c;
+            const f16x2 sc = e4m3_pair(quantize_block(x, ts, c));
+            f16x8 *dst = reinterpret_cast<f16x8 *>(xl + (int64_t)q * 32);
+            dst[0] = decode8(c.x, sc);
+            dst[1] = decode8(c.y, sc);
         };
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
-            const int64_t it = tid + (int64_t)j * NT;
-            if (it < items) prep(xv[j], it);
+            const int q = tid + j * NT;
+            if (q < items) prep(xv[j][0], xv[j][1], q);
         }
-        for (int64_t it = tid + (int64_t)XPT * NT; it < items; it += NT)
-            prep(*reinterpret_cast<const u32x4 *>(half_ptr(it)), it);
+        for (int q = tid + XPT * NT; q < items; q += NT) {
+            const u32x4 *p = blk_ptr(q);
+            prep(p[0], p[1], q);
+        }
     }
     // the side tiles' LDS home, after the reduction space: W_S [CB*16][kd]
     // dwords, then X_S [M][k] bf16
@@ -310,12 +317,12 @@ static hipError_t run_fused_x(const GemmArgs &a, const SegSpec *sp, hipStream_t 
     return launch_fused<NW, CPW, CB, XPT, false>(a, sp, lds, lds_max, s);
 }
 
-// half blocks of X per thread loaded ahead of the weights: all of them when
-// they are at most four, else the first four
+// 16-channel blocks of X per thread loaded ahead of the weights: all of them
+// when they are at most four, else the first four
 template <int NW, int CPW, int CB>
 static hipError_t run_fused(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
-    const int64_t items = a.M * a.K / 8;
+    const int64_t items = a.M * a.K / 16;
     if (items <= 64 * NW) return run_fused_x<NW, CPW, CB, 1>(a, sp, s);
     if (items <= 2 * 64 * NW) return run_fused_x<NW, CPW, CB, 2>(a, sp, s);
     return run_fused_x<NW, CPW, CB, 4>(a, sp, s);
@@ -328,21 +335,22 @@ bool fused_decode_ok(int64_t M, int64_t K)
     return M >= 1 && M <= 4 && K >= FBK && K % FBK == 0 && K <= 16 * 8 * FBK && M * K * 2 <= F_XMAX;
 }
 
-// Wave configurations from sweeps on MI355X (Qwen3-8B shapes, graph replay).
-// K <= 4096: one row takes the two-call kernel's eight waves of four chunks
-// (the two forms then agree bit for bit); more rows take sixteen waves of two
-// chunks, which spreads their larger preparation over twice the lanes, and
-// 48 columns per workgroup for wide N, so that fewer workgroups repeat it.
-// Larger K: the two-call kernel's configurations.
+// Wave configurations from sweeps on MI355X (Qwen3-8B shapes, graph replay,
+// weights streamed from HBM).  K <= 4096: the two-call kernel's eight waves of
+// four chunks (the two forms then agree bit for bit), with 48 columns per
+// workgroup for wide N at two or more rows, so that fewer workgroups repeat
+// the preparation (at two and four rows 8-18% faster than sixteen waves of
+// two chunks, once each lane quantizes whole blocks).  Larger K: the two-call
+// kernel's configurations.  The column grouping leaves each column's
+// arithmetic as it is, so a call over several weight matrices gives the bits
+// of one call per matrix.
 // configuration choice for a.N columns (the sum of the widths when sp is set)
 static hipError_t dispatch_fused(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
 {
     const int nchunk = (int)(a.K / FBK);
     const int64_t colblocks = (a.N + 15) / 16;
-    if (nchunk <= 8 * 4) {
-        if (a.M == 1) return run_fused<8, 4, 1>(a, sp, s);
-        return colblocks >= 512 ? run_fused<16, 2, 3>(a, sp, s) : run_fused<16, 2, 1>(a, sp, s);
-    }
+    if (nchunk <= 8 * 4)
+        return (a.M > 1 && colblocks >= 512) ? run_fused<8, 4, 3>(a, sp, s) : run_fused<8, 4, 1>(a, sp, s);
     if (nchunk <= 16 * 4) return run_fused<16, 4, 1>(a, sp, s);
     if (nchunk <= 16 * 6) return run_fused<16, 6, 1>(a, sp, s);
     return run_fused<16, 8, 1>(a, sp, s);

@@ -251,34 +251,4 @@ __device__ __forceinline__ unsigned quantize_block(const Block16 &x, const Tenso
     return sc;
 }
 
-// Half a block per lane: the lane holds elements 8h .. 8h+7 as four words
-// (protected lanes already +0) and lane ^ 1 holds the other half; both lanes
-// must call this together.  Returns the block's scale byte and the lane's
-// eight codes; the decisions are those of quantize_block.
-__device__ __forceinline__ unsigned quantize_half_block(const unsigned (&w)[4], const TensorScale &ts,
-                                                        unsigned &codes)
-{
-    u16x2 m = {0, 0};
-#pragma unroll
-    for (int t = 0; t < 4; t++)
-        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[t] & 0x7FFF7FFFu));
-    unsigned am = max((unsigned)m.x, (unsigned)m.y);
-    am = max(am, (unsigned)__shfl_xor((int)am, 1));
-    const unsigned sc = block_scale(am, ts);
-    const Keys ks = block_keys(sc, ts);
-    codes = pack_nibbles(code_word(w[0], ks), code_word(w[1], ks), code_word(w[2], ks), code_word(w[3], ks));
-    return sc;
-}
-
-// Sets the protected elements (bit e of m, 8 elements) of four words to +0.
-__device__ __forceinline__ void clear_protected_half(unsigned (&w)[4], unsigned m)
-{
-    const unsigned spread = (m & 0x55u) | ((m & 0xAAu) << 15);
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-        const unsigned b = (spread >> (2 * t)) & 0x00010001u;
-        w[t] &= ~((b << 16) - b);
-    }
-}
-
 }  // namespace splice

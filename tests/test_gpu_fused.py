@@ -25,10 +25,9 @@ XLDS_BYTES = 64 * 1024     # FP16 activations the two-call decode keeps in LDS
 
 def same_kernel(M, K):
     """The two-call decode runs the kernel the fused call mirrors, with the
-    same waves: an even chunk count and X in its LDS budget; K <= 4096 only
-    for one row (more rows take sixteen waves in the fused form)."""
+    same waves: an even chunk count and X in its LDS budget."""
     nchunk = K // 128
-    return M * K * 2 <= XLDS_BYTES and nchunk % 2 == 0 and (nchunk > 32 or M == 1)
+    return M * K * 2 <= XLDS_BYTES and nchunk % 2 == 0
 
 
 @pytest.fixture(scope="module", autouse=True)
