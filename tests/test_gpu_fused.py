@@ -81,7 +81,7 @@ CASES = [(1, 16, 256, 0), (1, 100, 1024, 5), (2, 48, 512, 64), (3, 130, 1024, 32
          (1, 50, 12288, 64), (4, 40, 12288, 64), (3, 24, 16384, 16), (1, 33, 16384, 128),
          (2, 64, 256, 256), (4, 17, 768, 7), (1, 40, 128, 16), (3, 60, 384, 64),
          (2, 90, 1152, 0), (1, 8200, 1024, 64), (2, 8195, 512, 5), (4, 8240, 4096, 32),
-         (1, 8192, 640, 0)]
+         (1, 8192, 640, 0), (3, 8210, 2048, 64), (3, 8192, 4096, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,k", CASES)
