@@ -179,10 +179,10 @@ def test_fused_prep_layer_groups(M, group):
 
 
 def test_fused_prep_ragged_segments():
-    """Ragged widths, one empty, K = 256 and 1024, against the per-segment
-    fused call."""
+    """Ragged widths, one empty, K = 256 and 1024, and K = 12288 (sixteen
+    waves of six chunks), against the per-segment fused call."""
     g = np.random.default_rng(4)
-    for M, K in ((1, 256), (3, 1024), (4, 1024)):
+    for M, K in ((1, 256), (3, 1024), (4, 1024), (2, 12288), (4, 12288)):
         widths = [40, 0, 130, 16]
         X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
         Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
