@@ -72,6 +72,62 @@ def test_alpha_and_quantize_bit_exact(R, K, k):
         assert np.array_equal(host(side_g), side_o), "side"
 
 
+def every_amax_blocks(seed):
+    """One 16-element block per positive finite bf16 magnitude pattern p
+    (0 .. 0x7F7F), p at one position, the other elements random patterns of
+    magnitude <= p, every sign random: bf16 bits [blocks, 16]."""
+    g = np.random.default_rng(seed)
+    p = np.arange(0x7F80, dtype=np.int64)
+    mag = (g.random((p.size, 16)) * (p[:, None] + 1)).astype(np.int64)
+    mag[np.arange(p.size), p % 16] = p
+    sign = g.integers(0, 2, (p.size, 16)) << 15
+    return (mag | sign).astype(np.uint16)
+
+
+def test_quantize_every_block_amax():
+    """Scale byte and codes of a block whose amax is each bf16 magnitude in
+    turn, for alphas on both sides of the fp32/fp64 threshold switch, tiny and
+    large: bit-exact against the oracle."""
+    B = every_amax_blocks(11)
+    A = np.zeros((2040 * 16, 16), np.uint16)
+    A[:B.shape[0]] = B
+    A = A.reshape(2040, 256)
+    idx = np.zeros(0, np.int32)
+    Ad, idxd = dev(A), dev(idx)
+    for alpha in (O.compute_alpha(A, idx), np.float32(1.0), np.float32(3.7e-3),
+                  np.float32(2.0 ** -80), np.float32(2.0 ** -80 * 0.75), np.float32(2.0 ** -120),
+                  np.float32(2.0 ** 60)):
+        c_o, s_o, _ = O.quantize_nvfp4(A, idx, alpha)
+        c_g, s_g, _ = S.quantize_nvfp4(Ad, idxd, dev(np.array([alpha], np.float32)))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(s_g), s_o), f"scales, alpha={alpha!r}"
+        assert np.array_equal(host(c_g), c_o), f"codes, alpha={alpha!r}"
+
+
+def test_fused_prep_every_block_amax():
+    """The fused decode's own preparation over the same blocks, four rows of
+    4096 channels a call: its product equals the two-call form's bit for bit
+    (the same wave configuration), on both threshold paths."""
+    B = every_amax_blocks(12)
+    nb = 4 * 4096 // 16
+    A = np.zeros((-(-B.shape[0] // nb) * nb, 16), np.uint16)
+    A[:B.shape[0]] = B
+    W = synth.to_bf16(np.random.default_rng(13).normal(0, 0.02, (16, 4096)))
+    idx = dev(np.zeros(0, np.int32))
+    Wd = dev(W)
+    aw = S.compute_alpha(Wd, idx)
+    wq = S.quantize_nvfp4(Wd, idx, aw)
+    for alpha in (np.float32(2.0 ** -8), np.float32(2.0 ** -80 * 0.75)):
+        ax = dev(np.array([alpha], np.float32))
+        for c in range(A.shape[0] // nb):
+            X = dev(A[c * nb:(c + 1) * nb].reshape(4, 4096))
+            Yf = S.splice_gemm_decode_fused(X, idx, ax, wq[0], wq[1], aw, None)
+            xq = S.quantize_nvfp4(X, idx, ax)
+            Y2 = S.splice_gemm(xq[0], xq[1], ax, None, wq[0], wq[1], aw, None, path=S.PATH_DECODE)
+            torch.cuda.synchronize()
+            assert torch.equal(Yf, Y2), f"alpha={alpha!r} slab {c}"
+
+
 def test_quantize_all_protected_and_strided_rows():
     A = special_rows(9, 64, 3)
     idx = np.arange(64, dtype=np.int32)
