@@ -189,8 +189,11 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x,
  * (splice_quantize_nvfp4(X, idx, alpha_x), then splice_gemm on the decode
  * path): one launch instead of two and no Xq/Xs/X_S buffers.  Y is
  * bit-identical to the two-call form where both use the same chunk split and
- * summation order (K/128 even, M*K <= 32768, and M == 1 when K <= 4096), and
- * within the GEMM tolerance otherwise.
+ * summation order (K/128 even and M*K <= 32768), and within the GEMM
+ * tolerance otherwise.  Every workgroup repeats the preparation of the M
+ * rows: the single launch pays at one and two rows; at four rows of a wide
+ * (N >= 8192) or deep (K > 4096) product the separate quantize launch costs
+ * less than the repeated preparation.
  *   X       bf16 [M, K] in (DEVICE), row stride ldx (multiple of 8, 16-byte
  *           aligned rows)
  *   idx     int32 [k] in (DEVICE): the protected channels, distinct, in
@@ -245,10 +248,10 @@ int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x
  * shared; segs a HOST array of nseg (1 .. SPLICE_SEG_MAX) weight segments as
  * for splice_gemm_multi.  One launch prepares X in every workgroup and
  * multiplies it by the workgroup's segment.  Each segment's Y equals
- * splice_gemm_decode_fused's for that segment alone wherever that call
- * would pick the same configuration (the choice depends on the combined width
- * only through the 48-column form for wide products); within the GEMM
- * tolerance otherwise.  Errors as splice_gemm_decode_fused, per segment. */
+ * splice_gemm_decode_fused's for that segment alone, bit for bit: the
+ * combined width only decides how many columns a workgroup takes (48 for wide
+ * products at two or more rows), never a column's arithmetic.  Errors as
+ * splice_gemm_decode_fused, per segment. */
 int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t *idx,
                                    const float *alpha_x, int64_t M, int64_t K, int32_t k,
                                    const splice_weight_seg *segs, int32_t nseg, splice_stream_t stream);

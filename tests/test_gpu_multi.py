@@ -195,3 +195,21 @@ def test_fused_prep_ragged_segments():
         for i, (a, b) in enumerate(zip(Ym, Yf)):
             assert a.shape == (M, widths[i])
             assert torch.equal(a, b), f"M={M} K={K} segment {i}"
+
+
+def test_fused_prep_combined_width_crosses_wide_form():
+    """Two segments of 256 and 257 column blocks: alone each takes 16 columns
+    per workgroup, together (513 blocks) the 48-column form; the bits do not
+    change."""
+    g = np.random.default_rng(6)
+    M, K, widths = 2, 1024, [4096, 4100]
+    X = synth.to_bf16(g.standard_normal((M, K)))
+    Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
+    xq, ax, wp = packs(X, Ws, 64, 6)
+    idx = packs.idx
+    Xd = dev(X)
+    Ym = S.splice_gemm_decode_fused_multi(Xd, idx, ax, wp)
+    Yf = [S.splice_gemm_decode_fused(Xd, idx, ax, *w) for w in wp]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(Ym, Yf)):
+        assert torch.equal(a, b), f"segment {i}"
