@@ -39,7 +39,8 @@ int check_gemm(const GemmArgs &a, int path)
     if (!a.Y || !a.alpha_x || !a.alpha_w) return SPLICE_ERR_INVALID_ARG;
     if (a.K > 0 && (!a.Xq || !a.Xs || !a.Wq || !a.Ws)) return SPLICE_ERR_INVALID_ARG;
     if (a.k > 0 && (!a.X_S || !a.W_S)) return SPLICE_ERR_INVALID_ARG;
-    if (!aligned(a.Xq, 16) || !aligned(a.Wq, 16) || !aligned(a.Xs, 8) || !aligned(a.Ws, 8) ||
+    // the kernels load codes and (in the decode path) scales as 16-byte vectors
+    if (!aligned(a.Xq, 16) || !aligned(a.Wq, 16) || !aligned(a.Xs, 16) || !aligned(a.Ws, 16) ||
         !aligned(a.Y, 4))
         return SPLICE_ERR_INVALID_ARG;
     const uintptr_t side_al = (a.k % 8 == 0) ? 16 : 2;
@@ -207,7 +208,7 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const
 
 int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
                       int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs, int32_t nseg,
-                      int path, splice_stream_t stream)
+                      void *ws, size_t ws_bytes, int path, splice_stream_t stream)
 {
     static_assert(SPLICE_SEG_MAX == SEG_MAX, "segment limit");
     if (nseg < 1 || nseg > SPLICE_SEG_MAX || !segs) return SPLICE_ERR_INVALID_ARG;
@@ -223,8 +224,11 @@ int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x
     }
     if (total > (int64_t)1 << 30) return SPLICE_ERR_UNSUPPORTED;   // launch units fit an int
     if (M == 0 || total == 0) return SPLICE_OK;
+    const Path p = choose_path(M, path);
+    const size_t need = gemm_ws_bytes(p, M, total, K);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16))) return SPLICE_ERR_WORKSPACE;
     GemmArgs base{Xq, Xs, alpha_x, X_S, nullptr, nullptr, nullptr, nullptr, M, total, K, k, nullptr, 0};
-    return hip_status(launch_gemm_seg(choose_path(M, path), base, seg, nseg, hs(stream)));
+    return hip_status(launch_gemm_seg(p, base, seg, nseg, ws, hs(stream)));
 }
 
 int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
@@ -243,7 +247,7 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
         if (!X || !Wq || !Ws || ldx < K || (k > 0 && (!idx || !W_S))) return SPLICE_ERR_INVALID_ARG;
         if (!fused_decode_ok(M, K)) return SPLICE_ERR_UNSUPPORTED;
         if (!aligned(X, 16) || ldx % 8 != 0) return SPLICE_ERR_UNSUPPORTED;
-        if (!aligned(Wq, 16) || !aligned(Ws, 8) || (k > 0 && !aligned(idx, 4)))
+        if (!aligned(Wq, 16) || !aligned(Ws, 16) || (k > 0 && !aligned(idx, 4)))
             return SPLICE_ERR_INVALID_ARG;
         if (k > 0 && !aligned(W_S, (k % 8 == 0) ? 16 : 2)) return SPLICE_ERR_INVALID_ARG;
     }
@@ -275,7 +279,7 @@ int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t
                     return SPLICE_ERR_INVALID_ARG;
                 if (!fused_decode_ok(M, K)) return SPLICE_ERR_UNSUPPORTED;
                 if (!aligned(X, 16) || ldx % 8 != 0) return SPLICE_ERR_UNSUPPORTED;
-                if (!aligned(w.Wq, 16) || !aligned(w.Ws, 8) || (k > 0 && !aligned(idx, 4)))
+                if (!aligned(w.Wq, 16) || !aligned(w.Ws, 16) || (k > 0 && !aligned(idx, 4)))
                     return SPLICE_ERR_INVALID_ARG;
                 if (k > 0 && !aligned(w.W_S, (k % 8 == 0) ? 16 : 2)) return SPLICE_ERR_INVALID_ARG;
             }
@@ -315,6 +319,15 @@ int splice_probe_mfma_f16(int64_t iters, int64_t workgroups, float *sink, splice
     if (iters < 0 || workgroups <= 0 || workgroups > 65536 || !sink || !aligned(sink, 4))
         return SPLICE_ERR_INVALID_ARG;
     return hip_status(launch_mfma_rate(iters, workgroups, sink, hs(stream)));
+}
+
+int splice_probe_stream_read(const void *src, int64_t bytes, int64_t workgroups, uint32_t *sink,
+                             splice_stream_t stream)
+{
+    if (bytes < 0 || bytes % 16 != 0 || workgroups <= 0 || workgroups > 65536 || !sink ||
+        !aligned(sink, 4) || (bytes > 0 && (!src || !aligned(src, 16))))
+        return SPLICE_ERR_INVALID_ARG;
+    return hip_status(launch_stream_read(src, bytes, workgroups, sink, hs(stream)));
 }
 
 size_t splice_grouped_workspace_size(const splice_group *, int32_t, int64_t, int64_t, int32_t)

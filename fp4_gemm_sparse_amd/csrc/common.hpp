@@ -74,11 +74,17 @@ __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c)
 // Workgroup barrier that makes this wave's LDS writes visible but, unlike
 // __syncthreads(), does not wait for outstanding global loads (the fence of
 // __syncthreads() would drain a prefetch issued for a later pipeline stage).
+// The wait and the barrier builtins touch no memory as far as the compiler's
+// IR passes know, so an empty asm statement with a memory clobber on each side
+// keeps LDS loads and stores from being moved across the barrier; the
+// scheduling barrier does the same for the machine scheduler.
 __device__ __forceinline__ void lds_barrier()
 {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maximum
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
 }
 
 // 8 bf16 values (16 bytes) of a side buffer row, zero past `valid` elements.

@@ -369,7 +369,7 @@ hipError_t launch_gemm_fused_seg(const GemmArgs &a, const GemmSeg *seg, int nseg
     b.N = 0;
     for (int i = 0; i < nseg; i++) b.N += seg[i].N;
     if (nseg == 0 || b.M == 0 || b.N == 0) return hipSuccess;
-    if (b.K == 0) return launch_gemm_seg(Path::Prefill, b, seg, nseg, s);   // Y = 0 (k <= K)
+    if (b.K == 0) return launch_gemm_seg(Path::Prefill, b, seg, nseg, nullptr, s);   // Y = 0 (k <= K)
     const SegSpec sp{seg, nseg};
     return dispatch_fused(b, &sp, s);
 }

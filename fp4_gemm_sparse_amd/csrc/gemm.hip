@@ -1107,20 +1107,18 @@ static bool run_decode3_k(const GemmArgs &a, const SegSpec *sp, hipStream_t s, h
 // ===========================================================================
 size_t gemm_ws_bytes(Path, int64_t, int64_t, int64_t)
 {
-    return 0;        // neither datapath needs scratch memory
+    return 0;        // neither datapath keeps partial results in device memory
 }
 
 // configuration choice and launch; sp != nullptr: the column segments of sp,
 // whose widths sum to a.N
-static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, hipStream_t s)
+static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, void *ws, hipStream_t s)
 {
     if (a.M == 0 || a.N == 0) return hipSuccess;
     if (a.K == 0) p = Path::Prefill;    // the decode kernels assume at least one K chunk
     if (p == Path::Prefill) {
         // largest tile that still gives every CU a tile
         const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-        const int64_t t256x128 = ((a.M + 255) / 256) * ((a.N + 127) / 128);
-        (void)t256x128;
         if (t256 >= 240) return a.k > 0 ? launch_prefill_lds<true>(a, sp, s) : launch_prefill_lds<false>(a, sp, s);
         return a.k > 0 ? launch_prefill_lds128<true>(a, sp, s) : launch_prefill_lds128<false>(a, sp, s);
     }
@@ -1156,12 +1154,12 @@ static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, hi
     return run_decode2<4, 1, 8, 2>(a, sp, s);
 }
 
-hipError_t launch_gemm(Path p, const GemmArgs &a, void *, size_t, hipStream_t s)
+hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t s)
 {
-    return dispatch_gemm(p, a, nullptr, s);
+    return dispatch_gemm(p, a, nullptr, ws, s);
 }
 
-hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s)
+hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, void *ws, hipStream_t s)
 {
     // the configuration is chosen for the combined width, as for one call
     // with N = the sum of the widths
@@ -1170,7 +1168,7 @@ hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int ns
     for (int i = 0; i < nseg; i++) b.N += seg[i].N;
     if (nseg == 0 || b.M == 0 || b.N == 0) return hipSuccess;
     const SegSpec sp{seg, nseg};
-    return dispatch_gemm(p, b, &sp, s);
+    return dispatch_gemm(p, b, &sp, ws, s);
 }
 
 }  // namespace splice

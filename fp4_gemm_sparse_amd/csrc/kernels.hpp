@@ -61,7 +61,7 @@ struct SegSpec {
 // the products of a's activation operands (Xq, Xs, alpha_x, X_S, M, K, k)
 // with each segment's weights, in one launch (a's weight and output fields
 // are ignored); 1 <= nseg <= SEG_MAX
-hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s);
+hipError_t launch_gemm_seg(Path p, const GemmArgs &a, const GemmSeg *seg, int nseg, void *ws, hipStream_t s);
 // launch_gemm_fused over column segments (a's weight and output fields ignored)
 hipError_t launch_gemm_fused_seg(const GemmArgs &a, const GemmSeg *seg, int nseg, hipStream_t s);
 // independent products sharing N, K and k (groups[i].N/K/k equal), one launch
@@ -88,5 +88,9 @@ hipError_t launch_tim_filter(const TimArgs &a, hipStream_t s);
 
 // measurement aid: `workgroups` x 4 waves, each 4 * iters 32x32x16 FP16 MFMAs
 hipError_t launch_mfma_rate(int64_t iters, int64_t workgroups, float *sink, hipStream_t s);
+// measurement aid: a pure read of `bytes` (a multiple of 16) by `workgroups`
+// x 256 threads; sink receives one word per wave
+hipError_t launch_stream_read(const void *src, int64_t bytes, int64_t workgroups, unsigned *sink,
+                              hipStream_t s);
 
 }  // namespace splice

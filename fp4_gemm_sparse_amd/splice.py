@@ -70,6 +70,7 @@ _SIGS = {
                                   _sz, ctypes.c_int, _vp]),
     "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "splice_probe_mfma_f16": (ctypes.c_int, [_i64, _i64, _vp, _vp]),
+    "splice_probe_stream_read": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "splice_tim_filter": (ctypes.c_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _i64, _i64, _i64, _vp,
                                          _vp, _vp, _vp, _i64, _i64, _vp]),
     "splice_gemm_decode_fused": (ctypes.c_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
@@ -78,7 +79,7 @@ _SIGS = {
                                            _vp]),
     "splice_grouped_workspace_size": (_sz, [ctypes.POINTER(_Group), _i32, _i64, _i64, _i32]),
     "splice_gemm_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, ctypes.POINTER(_Seg),
-                                         _i32, ctypes.c_int, _vp]),
+                                         _i32, _vp, _sz, ctypes.c_int, _vp]),
     "splice_gemm_decode_fused_multi": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i32,
                                                       ctypes.POINTER(_Seg), _i32, _vp]),
 }
@@ -246,6 +247,24 @@ def workspace_size(M, N, K, k=0):
     return lib().splice_workspace_size(M, N, K, k)
 
 
+_ws_cache = {}
+
+
+def workspace(nbytes, device):
+    """A zero-filled device workspace of at least nbytes, kept per device and
+    reused: the library returns its split counters to zero after every call,
+    so calls ordered on one stream can share it (concurrent streams need
+    workspaces of their own, passed explicitly).  Grown on demand, which
+    allocates: make a first call outside any graph capture."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = t
+    return t
+
+
 def splice_gemm(Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, path=PATH_AUTO, out=None, ws=None):
     M, K = Xq.shape[0], Xq.shape[1] * 2
     N = Wq.shape[0]
@@ -253,7 +272,7 @@ def splice_gemm(Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, path=PATH_AUTO, out=
     Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
     need = workspace_size(M, N, K, k) if path != PATH_PREFILL else 0
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+        ws = workspace(need, Xq.device)
     _check("splice_gemm",
            lib().splice_gemm(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, _p(Wq), _p(Ws),
                              _p(alpha_w), _p(W_S) if k else None, M, N, K, k, _p(Y), Y.stride(0),
@@ -267,7 +286,7 @@ def nvfp4_gemm(Xq, Xs, alpha_x, Wq, Ws, alpha_w, path=PATH_AUTO, out=None, ws=No
     Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
     need = workspace_size(M, N, K, 0) if path != PATH_PREFILL else 0
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+        ws = workspace(need, Xq.device)
     _check("nvfp4_gemm",
            lib().nvfp4_gemm(_p(Xq), _p(Xs), _p(alpha_x), _p(Wq), _p(Ws), _p(alpha_w), M, N, K, _p(Y),
                             Y.stride(0), _p(ws), 0 if ws is None else ws.numel(), path, _stream()))
@@ -319,12 +338,22 @@ def probe_mfma_f16(iters, workgroups, sink):
     _check("splice_probe_mfma_f16", lib().splice_probe_mfma_f16(iters, workgroups, _p(sink), _stream()))
 
 
-def splice_gemm_multi(Xq, Xs, alpha_x, X_S, weights, path=PATH_AUTO, out=None):
+def probe_stream_read(src, nbytes, workgroups, sink):
+    """Measurement aid: a pure read of the first `nbytes` bytes of the device
+    tensor src by `workgroups` x 256 threads (sink uint32/int32 [workgroups * 4])."""
+    _check("splice_probe_stream_read",
+           lib().splice_probe_stream_read(_p(src), nbytes, workgroups, _p(sink), _stream()))
+
+
+def splice_gemm_multi(Xq, Xs, alpha_x, X_S, weights, path=PATH_AUTO, out=None, ws=None):
     """One launch of the products of one set of activation packs with several
     weight packs.  weights: list of (Wq, Ws, alpha_w, W_S) (W_S None when
     k == 0); out: list of fp32 outputs [M, N_i] or None.  Returns the outputs."""
     M, K = Xq.shape[0], Xq.shape[1] * 2
     k = 0 if X_S is None else X_S.shape[1]
+    need = workspace_size(M, sum(w[0].shape[0] for w in weights), K, k) if path != PATH_PREFILL else 0
+    if ws is None and need:
+        ws = workspace(need, Xq.device)
     if out is None:
         out = [torch.empty(M, w[0].shape[0], dtype=torch.float32, device=Xq.device) for w in weights]
     arr = (_Seg * max(len(weights), 1))()
@@ -333,7 +362,8 @@ def splice_gemm_multi(Xq, Xs, alpha_x, X_S, weights, path=PATH_AUTO, out=None):
                       Y.stride(0))
     _check("splice_gemm_multi",
            lib().splice_gemm_multi(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, M, K, k, arr,
-                                   len(weights), path, _stream()))
+                                   len(weights), _p(ws), 0 if ws is None else ws.numel(), path,
+                                   _stream()))
     return out
 
 

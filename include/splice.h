@@ -166,7 +166,16 @@ int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
  * path: SPLICE_PATH_AUTO (decode path when M <= SPLICE_DECODE_MAX_M),
  *       SPLICE_PATH_DECODE (requires M <= SPLICE_DECODE_MAX_M) or
  *       SPLICE_PATH_PREFILL.
- * ws: splice_workspace_size(M, N, K, k) bytes (0 is allowed when that is 0). */
+ * ws: DEVICE workspace of at least splice_workspace_size(M, N, K, k) bytes,
+ *     16-byte aligned (NULL is allowed when that size is 0; a smaller or
+ *     missing workspace returns SPLICE_ERR_WORKSPACE).  Where the K range is
+ *     split over workgroups it holds one arrival counter per column tile and
+ *     the partial tiles, which the workgroup completing a tile sums in split
+ *     order (so Y does not depend on arrival order).  The counters must be
+ *     zero when the workspace is first used -- zero-fill it once after
+ *     allocating it -- and every call leaves them zero again, so one
+ *     workspace serves any sequence of calls ordered on a stream (calls that
+ *     may run concurrently need workspaces of their own). */
 int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
                 const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
                 int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy,
@@ -228,7 +237,9 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
  * decode path whenever the call alone would pick the same configuration (for
  * the Qwen3-8B q/k/v and gate/up widths it does); within the GEMM tolerance
  * otherwise.  Errors as splice_gemm, checked per segment before anything is
- * launched.  No workspace; nothing is allocated. */
+ * launched.
+ *   ws, ws_bytes  as for splice_gemm, sized by splice_workspace_size(M, sum
+ *          of the widths, K, k). */
 #define SPLICE_SEG_MAX 8
 typedef struct {
     const uint8_t *Wq, *Ws;
@@ -241,7 +252,7 @@ typedef struct {
 
 int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
                       int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs, int32_t nseg,
-                      int path, splice_stream_t stream);
+                      void *ws, size_t ws_bytes, int path, splice_stream_t stream);
 
 /* splice_gemm_decode_fused over column segments: the bf16 rows X (M <=
  * SPLICE_FUSED_MAX_M), idx and alpha_x as for splice_gemm_decode_fused,
@@ -256,8 +267,10 @@ int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t
                                    const float *alpha_x, int64_t M, int64_t K, int32_t k,
                                    const splice_weight_seg *segs, int32_t nseg, splice_stream_t stream);
 
-/* Workspace bytes splice_gemm / nvfp4_gemm need for this shape (k is
- * ignored by the current kernels but part of the contract). */
+/* Workspace bytes splice_gemm / nvfp4_gemm / splice_gemm_multi (N = the sum
+ * of the widths) need for this shape on the path SPLICE_PATH_AUTO takes
+ * (0 on the prefill path; k is part of the contract but does not change the
+ * size).  A few MiB at most for the decode shapes. */
 size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
 
 /* ---------------------------------------------------------------------------
@@ -316,6 +329,16 @@ int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *
  * clock under that load.  sink: float [workgroups * 4] out (DEVICE).
  * 2 * (number of CUs) workgroups put two waves on every SIMD. */
 int splice_probe_mfma_f16(int64_t iters, int64_t workgroups, float *sink, splice_stream_t stream);
+
+/* Measurement aid, not part of the SpliceGEMM path: a pure streaming read of
+ * `bytes` bytes at src (DEVICE, 16-byte aligned, bytes a multiple of 16) by
+ * `workgroups` workgroups of 256 threads, each thread with four 16-byte loads
+ * in flight per round.  Timing it gives the rate at which this GPU streams a
+ * buffer of that size -- the ceiling for a weight-streaming decode call that
+ * reads as many bytes.  sink: uint32 [workgroups * 4] out (DEVICE), one
+ * folded word per wave. */
+int splice_probe_stream_read(const void *src, int64_t bytes, int64_t workgroups, uint32_t *sink,
+                             splice_stream_t stream);
 
 #ifdef __cplusplus
 }

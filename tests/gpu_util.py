@@ -51,16 +51,21 @@ def assert_gemm_close(Y, Yo, what="", terms=None, max_scaled=0):
     1e-6 times that sum: where large products cancel, the fp32 accumulation
     of a K-term dot product errs by a few units in the last place of the
     products, not of the result.  At most `max_scaled` elements may need
-    this."""
+    this.  Returns the number of elements beyond the literal bound
+    max(1e-3 |y_oracle|, 1e-6) that the scaled floor admitted (0 without
+    `terms`); a failure message states that count too."""
     fro, err, lim = gemm_errors(Y, Yo)
     bad = np.argwhere(err > lim)
+    literal = len(bad)
     if bad.size and terms is not None and len(bad) <= max_scaled:
         keep = [b for b in bad if err[tuple(b)] > ELEM_ABS * max(1.0, terms(*b))]
         bad = np.array(keep).reshape(-1, 2)
     msg = ""
     if bad.size:
         i = tuple(bad[0])
-        msg = (f"{what}: {len(bad)} of {err.size} elements outside tolerance; first {i}: "
-               f"gpu {Y[i]!r} oracle {Yo[i]!r}; fro {fro:.3g}")
+        msg = (f"{what}: {len(bad)} of {err.size} elements outside tolerance "
+               f"({literal} beyond the literal floor, at most {max_scaled} may use the scaled "
+               f"one); first {i}: gpu {Y[i]!r} oracle {Yo[i]!r}; fro {fro:.3g}")
     assert fro <= FRO_TOL, f"{what}: relative Frobenius error {fro:.3g}"
     assert not bad.size, msg
+    return literal

@@ -52,6 +52,8 @@ def gemm(L, M=64, N=64, K=256, k=8, path=0, ws=None, wsb=0, **over):
     (dict(Xq=None), splice.ERR_INVALID_ARG),
     (dict(XS=None), splice.ERR_INVALID_ARG),
     (dict(Xq=FAKE + 4), splice.ERR_INVALID_ARG),      # misaligned codes
+    (dict(Ws=FAKE + 8), splice.ERR_INVALID_ARG),      # scales are loaded as 16-byte vectors
+    (dict(Xs=FAKE + 8), splice.ERR_INVALID_ARG),
     (dict(ldy=10), splice.ERR_INVALID_ARG),
     (dict(M=0), splice.OK),                           # no-op
     (dict(N=0), splice.OK),
@@ -61,10 +63,9 @@ def test_gemm_argument_errors(L, kw, code):
 
 
 def test_gemm_workspace_size(L):
-    # no GEMM path keeps partial results in device memory: the workspace is
-    # empty for decode, prefill and degenerate shapes alike
-    for M, N, K, k in ((1, 1024, 4096, 64), (64, 12288, 4096, 64), (8192, 4096, 4096, 64),
-                       (0, 1024, 4096, 64), (1, 4096, 12288, 0)):
+    # the decode path keeps no partial results in device memory
+    for M, N, K, k in ((1, 1024, 4096, 64), (64, 12288, 4096, 64), (0, 1024, 4096, 64),
+                       (1, 4096, 12288, 0)):
         assert L.splice_workspace_size(M, N, K, k) == 0
 
 
@@ -132,7 +133,7 @@ def test_multi_argument_errors(L):
     good = S(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 64)
 
     def call(segs, n, M=4, K=256, k=8, path=0, XS=FAKE):
-        return L.splice_gemm_multi(FAKE, FAKE, FAKE, XS, M, K, k, segs, n, path, None)
+        return L.splice_gemm_multi(FAKE, FAKE, FAKE, XS, M, K, k, segs, n, None, 0, path, None)
     one = (S * 1)(good)
     assert call(one, 0) == splice.ERR_INVALID_ARG                       # no segment
     assert call(one, splice.SEG_MAX + 1) == splice.ERR_INVALID_ARG      # too many
@@ -142,6 +143,8 @@ def test_multi_argument_errors(L):
     two = (S * 2)(good, S(FAKE, FAKE, None, FAKE, 64, FAKE, 64))        # no alpha_w
     assert call(two, 2) == splice.ERR_INVALID_ARG
     two = (S * 2)(good, S(FAKE + 4, FAKE, FAKE, FAKE, 64, FAKE, 64))    # misaligned codes
+    assert call(two, 2) == splice.ERR_INVALID_ARG
+    two = (S * 2)(good, S(FAKE, FAKE + 8, FAKE, FAKE, 64, FAKE, 64))    # scales 8-byte aligned
     assert call(two, 2) == splice.ERR_INVALID_ARG
     assert call(one, 1, XS=None) == splice.ERR_INVALID_ARG               # k > 0 without X_S
     assert call(one, 1, K=144) == splice.ERR_UNSUPPORTED
@@ -166,6 +169,8 @@ def test_fused_multi_argument_errors(L):
     assert call(one, 1, ldx=1000) == splice.ERR_INVALID_ARG
     assert call(one, 1, K=1040, ldx=1040) == splice.ERR_UNSUPPORTED     # K % 128
     two = (S * 2)(good, S(FAKE, FAKE, FAKE, None, 64, FAKE, 64))        # k > 0 without W_S
+    assert call(two, 2) == splice.ERR_INVALID_ARG
+    two = (S * 2)(good, S(FAKE, FAKE + 8, FAKE, FAKE, 64, FAKE, 64))    # scales 8-byte aligned
     assert call(two, 2) == splice.ERR_INVALID_ARG
     assert call(one, 1, M=0) == splice.OK
 
@@ -196,6 +201,7 @@ def fused(L, M=1, N=64, K=1024, k=8, **over):
     (dict(Y=None), splice.ERR_INVALID_ARG),
     (dict(ldy=10), splice.ERR_INVALID_ARG),
     (dict(Wq=FAKE + 4), splice.ERR_INVALID_ARG),           # misaligned codes
+    (dict(Ws=FAKE + 8), splice.ERR_INVALID_ARG),           # scales are loaded as 16-byte vectors
     (dict(idx=FAKE + 2), splice.ERR_INVALID_ARG),
 ])
 def test_fused_decode_argument_errors(L, kw, code):
@@ -271,3 +277,10 @@ def test_probe_argument_errors(L):
     assert f(16, 0, FAKE, None) == splice.ERR_INVALID_ARG
     assert f(16, 8, None, None) == splice.ERR_INVALID_ARG
     assert f(16, 8, FAKE + 2, None) == splice.ERR_INVALID_ARG
+    r = L.splice_probe_stream_read
+    assert r(FAKE, 100, 8, FAKE, None) == splice.ERR_INVALID_ARG       # not a multiple of 16
+    assert r(FAKE, -16, 8, FAKE, None) == splice.ERR_INVALID_ARG
+    assert r(FAKE, 1 << 20, 0, FAKE, None) == splice.ERR_INVALID_ARG
+    assert r(FAKE + 8, 1 << 20, 8, FAKE, None) == splice.ERR_INVALID_ARG  # misaligned source
+    assert r(None, 1 << 20, 8, FAKE, None) == splice.ERR_INVALID_ARG
+    assert r(FAKE, 1 << 20, 8, None, None) == splice.ERR_INVALID_ARG

@@ -438,9 +438,10 @@ def test_prefill_full_size_every_row(name):
     assert np.array_equal(host(gx[0]), o["xq"]) and np.array_equal(host(gx[1]), o["xs"])
     assert np.array_equal(host(gw[0]), o["wq"]) and np.array_equal(host(gw[1]), o["ws"])
     # 33.5 M outputs of 4096-term dot products: allow the scaled floor for at
-    # most 8 elements whose products cancel
-    assert_gemm_close(host(Y), o["Y"], f"prefill {name}, all rows",
-                      terms=lambda i, j: product_magnitudes(o, i, j), max_scaled=8)
+    # most 8 elements whose products cancel, and report how many needed it
+    n = assert_gemm_close(host(Y), o["Y"], f"prefill {name}, all rows",
+                          terms=lambda i, j: product_magnitudes(o, i, j), max_scaled=8)
+    print(f"prefill {name}, all {M * p['N']} outputs: {n} beyond the literal 1e-6 floor")
 
 
 def test_grouped_moe_sampled():
