@@ -3,6 +3,7 @@
 #include "../../include/splice.h"
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -186,7 +187,49 @@ int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda, 
 size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t)
 {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
-    return gemm_ws_bytes(M <= SPLICE_DECODE_MAX_M ? Path::Decode : Path::Prefill, M, N, K);
+    // enough for whichever path a call takes (the decode path needs none)
+    return std::max(gemm_ws_bytes(Path::Decode, M, N, K), gemm_ws_bytes(Path::Prefill, M, N, K));
+}
+
+int splice_gemm_plan(int64_t M, int64_t N, int64_t K, int path, int32_t *plan)
+{
+    if (!plan || M <= 0 || N <= 0 || K < 0 || K % 16 != 0) return SPLICE_ERR_INVALID_ARG;
+    if (path != SPLICE_PATH_AUTO && path != SPLICE_PATH_DECODE && path != SPLICE_PATH_PREFILL)
+        return SPLICE_ERR_INVALID_ARG;
+    if (path == SPLICE_PATH_DECODE && M > SPLICE_DECODE_MAX_M) return SPLICE_ERR_INVALID_ARG;
+    gemm_plan_info(choose_path(M, path), M, N, K, nullptr, 0, plan);
+    return SPLICE_OK;
+}
+
+int splice_multi_plan(int64_t M, int64_t K, const splice_weight_seg *segs, int32_t nseg, int path,
+                      int32_t *plan)
+{
+    if (!plan || !segs || nseg < 1 || nseg > SPLICE_SEG_MAX || M <= 0 || K < 0 || K % 16 != 0)
+        return SPLICE_ERR_INVALID_ARG;
+    if (path != SPLICE_PATH_AUTO && path != SPLICE_PATH_DECODE && path != SPLICE_PATH_PREFILL)
+        return SPLICE_ERR_INVALID_ARG;
+    if (path == SPLICE_PATH_DECODE && M > SPLICE_DECODE_MAX_M) return SPLICE_ERR_INVALID_ARG;
+    GemmSeg seg[SEG_MAX];
+    int64_t N = 0;
+    for (int32_t i = 0; i < nseg; i++) {
+        if (segs[i].N < 0) return SPLICE_ERR_INVALID_ARG;
+        seg[i] = GemmSeg{nullptr, nullptr, nullptr, nullptr, nullptr, 0, segs[i].N};
+        N += segs[i].N;
+    }
+    if (N == 0) return SPLICE_ERR_INVALID_ARG;
+    gemm_plan_info(choose_path(M, path), M, N, K, seg, nseg, plan);
+    return SPLICE_OK;
+}
+
+size_t splice_multi_workspace_size(int64_t M, int64_t K, int32_t, const splice_weight_seg *segs,
+                                   int32_t nseg)
+{
+    if (M <= 0 || K <= 0 || !segs || nseg < 1 || nseg > SPLICE_SEG_MAX) return 0;
+    GemmSeg seg[SEG_MAX];
+    for (int32_t i = 0; i < nseg; i++)
+        seg[i] = GemmSeg{nullptr, nullptr, nullptr, nullptr, nullptr, 0, segs[i].N > 0 ? segs[i].N : 0};
+    return std::max(gemm_seg_ws_bytes(Path::Decode, M, K, seg, nseg),
+                    gemm_seg_ws_bytes(Path::Prefill, M, K, seg, nseg));
 }
 
 int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
@@ -225,7 +268,7 @@ int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x
     if (total > (int64_t)1 << 30) return SPLICE_ERR_UNSUPPORTED;   // launch units fit an int
     if (M == 0 || total == 0) return SPLICE_OK;
     const Path p = choose_path(M, path);
-    const size_t need = gemm_ws_bytes(p, M, total, K);
+    const size_t need = gemm_seg_ws_bytes(p, M, K, seg, nseg);
     if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16))) return SPLICE_ERR_WORKSPACE;
     GemmArgs base{Xq, Xs, alpha_x, X_S, nullptr, nullptr, nullptr, nullptr, M, total, K, k, nullptr, 0};
     return hip_status(launch_gemm_seg(p, base, seg, nseg, ws, hs(stream)));

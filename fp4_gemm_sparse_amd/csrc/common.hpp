@@ -13,6 +13,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int WAVE = 64;
 constexpr int NVFP4_BLOCK = 16;
@@ -84,6 +85,15 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left at their maximum
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(0): every global load and store this wave has issued has
+// completed (for a device-coherent store: it is visible to every workgroup).
+__device__ __forceinline__ void wait_vmem()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt left at their maximum
     asm volatile("" ::: "memory");
 }
 

@@ -18,6 +18,8 @@
 #include "kernels.hpp"
 #include "segments.hpp"
 
+#include <algorithm>
+
 namespace splice {
 
 constexpr int BK = 128;              // channels per decode-path K chunk
@@ -28,13 +30,17 @@ constexpr int SCALE_ROW = BK / 16;   // 8 scale bytes per row per chunk
 // Prefill path
 // ===========================================================================
 // XCD-aware tile order: consecutive workgroups go to different XCDs round
-// robin, so each XCD is handed a contiguous range of tiles; inside it tiles
-// walk GM tile-rows at a time so neighbours share operand rows in L2.
-__device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_n, int &tm, int &tn)
+// robin, so each XCD is handed a contiguous range of work items; inside it
+// tiles walk GM tile-rows at a time so neighbours share operand rows in L2.
+__device__ __forceinline__ int xcd_order(int wg, int nwg)
 {
     const int q = nwg / 8, r = nwg % 8;
     const int x = wg % 8, local = wg / 8;
-    const int tile = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+__device__ __forceinline__ void group_tile(int tile, int tiles_m, int tiles_n, int &tm, int &tn)
+{
     constexpr int GM = 8;
     const int per_group = GM * tiles_n;
     const int group = tile / per_group;
@@ -44,6 +50,33 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
     tm = first_m + in % gsz;
     tn = in / gsz;
 }
+
+__device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    group_tile(xcd_order(wg, nwg), tiles_m, tiles_n, tm, tn);
+}
+
+// with the K range split nsplit ways: the splits of a tile are consecutive
+// work items, so they usually run side by side on one XCD
+__device__ __forceinline__ void tile_split_of(int wg, int nwg, int nsplit, int tiles_m, int tiles_n,
+                                              int &tm, int &tn, int &split)
+{
+    const int item = xcd_order(wg, nwg);
+    const int tile = item / nsplit;
+    split = item - tile * nsplit;
+    group_tile(tile, tiles_m, tiles_n, tm, tn);
+}
+
+// K split over workgroups: the workgroups of one output tile each sum a range
+// of K steps; the partial tiles go to the workspace and the workgroup that
+// completes the tile's arrival count adds them in split order and finishes the
+// tile.  wtile numbers the tile's counter and partial slots.
+struct SplitK {
+    int split = 0, nsplit = 1;
+    int64_t wtile = 0;
+    unsigned *cnt = nullptr;
+    float *part = nullptr;
+};
 
 // ===========================================================================
 // LDS-decode prefill tile: each workgroup decodes every NVFP4 element of its
@@ -89,8 +122,17 @@ struct LdsGeo {
     static_assert(UNITS * NT == ROWS * 2 && FM * 32 == WM && FN * 32 == WN, "tile geometry");
 };
 // One BM x BN output tile (tm, tn) with WGM x WGN waves (see LdsGeo).
-template <int BM, int BN, int WGM, int WGN, bool TAIL>
-__device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint8_t *lds)
+// PF: register stages of operand codes in flight.  The codes of step t are
+// loaded PF steps ahead (at the end of step t - 1 - PF) and decoded during
+// step t - 1, so a load has PF - 1 full steps of matrix work to arrive; with
+// PF = 1 it is issued just before the barrier that precedes its use, which is
+// enough where eight waves keep the matrix cores busy (the 256 x 256 tile)
+// but exposes the load latency every step for the 128 x 128 tile's few waves.
+// SPLIT: the kernel may split K over workgroups (sk.nsplit > 1); only then is
+// the partial-tile epilogue compiled in.
+template <int BM, int BN, int WGM, int WGN, bool TAIL, int PF = 1, bool SPLIT = false>
+__device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint8_t *lds,
+                                         const SplitK &sk = SplitK{})
 {
     using C = LdsGeo<BM, BN, WGM, WGN>;
     constexpr int NT = C::NT, UNITS = C::UNITS;
@@ -101,7 +143,12 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int64_t rowb = K / 2, rows = K / 16;
-    const int nk = (int)(K / C::BKL);
+    // this workgroup's K steps [kt0, kt0 + nk) of 64 channels
+    const int nk_all = (int)(K / C::BKL);
+    const int nsplit = SPLIT ? sk.nsplit : 1;
+    const int per_split = (nk_all + nsplit - 1) / nsplit;
+    const int kt0 = SPLIT ? sk.split * per_split : 0;
+    const int nk = max(0, min(nk_all - kt0, per_split));
 
     // decode units of this thread: unit i = LDS row (tid + NT*i)/2 (X rows
     // first, then W rows), channel half tid%2.  Rows past the edge read row 0
@@ -121,21 +168,22 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         ucode[i] = (isx ? a.Xq : a.Wq) + rr0 * rowb + half * 16;
         uscale[i] = (isx ? a.Xs : a.Ws) + rr0 * rows + half * 2;
     }
-    u32x4 pc[UNITS];
-    unsigned ps[UNITS];
-    auto gload = [&](int kt) {
+    // register stage r holds the codes of the steps t with t % PF == r
+    u32x4 pc[PF][UNITS];
+    unsigned ps[PF][UNITS];
+    auto gload = [&](int r, int kt) {
 #pragma unroll
         for (int i = 0; i < UNITS; i++) {
-            pc[i] = *reinterpret_cast<const u32x4 *>(ucode[i] + (int64_t)kt * 32);
-            ps[i] = *reinterpret_cast<const uint16_t *>(uscale[i] + (int64_t)kt * 4);
+            pc[r][i] = *reinterpret_cast<const u32x4 *>(ucode[i] + (int64_t)kt * 32);
+            ps[r][i] = *reinterpret_cast<const uint16_t *>(uscale[i] + (int64_t)kt * 4);
         }
     };
-    // piece d (8 channels) of every unit into `tile`
-    auto decode_piece = [&](uint8_t *tile, int d) {
+    // piece d (8 channels) of every unit of stage r into `tile`
+    auto decode_piece = [&](uint8_t *tile, int r, int d) {
 #pragma unroll
         for (int i = 0; i < UNITS; i++) {
-            const f16x2 sc = e4m3_pair(d < 2 ? (ps[i] & 0xFFu) : ((ps[i] >> 8) & 0xFFu));
-            *reinterpret_cast<f16x8 *>(tile + f16_off(urow[i], half * 4 + d)) = decode8(pc[i][d], sc);
+            const f16x2 sc = e4m3_pair(d < 2 ? (ps[r][i] & 0xFFu) : ((ps[r][i] >> 8) & 0xFFu));
+            *reinterpret_cast<f16x8 *>(tile + f16_off(urow[i], half * 4 + d)) = decode8(pc[r][i][d], sc);
         }
     };
 
@@ -148,14 +196,20 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
             for (int q = 0; q < 16; q++) acc[i][j][q] = 0.f;
 
     if (nk > 0) {
-        gload(0);
 #pragma unroll
-        for (int d = 0; d < 4; d++) decode_piece(lds, d);
-        gload(min(1, nk - 1));
+        for (int r = 0; r < PF; r++) gload(r, kt0 + min(r, nk - 1));
+#pragma unroll
+        for (int d = 0; d < 4; d++) decode_piece(lds, 0, d);
+        gload(0, kt0 + min(PF, nk - 1));
     }
     __syncthreads();
     const int arow = wm * C::WM + rr, brow = C::BM + wn * C::WN + rr;
-    for (int kt = 0; kt < nk; kt++) {
+    for (int kb = 0; kb < nk; kb += PF)
+#pragma unroll
+    for (int u = 0; u < PF; u++) {
+        const int kt = kb + u;
+        if (kt >= nk) break;
+        const int rs = (u + 1) % PF;         // stage holding step kt + 1
         const uint8_t *cur = lds + (kt & 1) * C::TILE;
         uint8_t *nxt = lds + ((kt + 1) & 1) * C::TILE;
         f16x8 a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
@@ -173,7 +227,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
                 for (int j = 0; j < C::FN; j++)
                     b1[j] = *reinterpret_cast<const f16x8 *>(cur + f16_off(brow + j * 32, (s + 1) * 2 + g));
             }
-            decode_piece(nxt, s);     // on the last step this fills the idle buffer
+            decode_piece(nxt, rs, s);     // on the last step this fills the idle buffer
 #pragma unroll
             for (int j = 0; j < C::FN; j++)
 #pragma unroll
@@ -186,8 +240,67 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        gload(min(kt + 2, nk - 1));
-        lds_barrier();      // the prefetch of step kt+2 stays in flight
+        gload(rs, kt0 + min(kt + 1 + PF, nk - 1));
+        lds_barrier();      // the prefetches of steps kt+2 .. kt+1+PF stay in flight
+    }
+
+    // ---- K split over workgroups: the partial tile goes to the workspace with
+    // device-coherent 8-byte stores (they bypass the non-coherent caches, so no
+    // cache needs flushing); once every wave's stores have completed, one
+    // thread counts the workgroup in.  The workgroup that completes the count
+    // reads every split's partial with device-coherent loads, sums them in
+    // split order and finishes the tile; it returns the count to zero.
+    if (SPLIT && sk.nsplit > 1) {
+        __shared__ int last_flag;
+        constexpr int NWV = NT / WAVE;
+        uint64_t *pt = reinterpret_cast<uint64_t *>(sk.part) + sk.wtile * (int64_t)sk.nsplit * (C::BM * C::BN / 2);
+        auto slot = [&](int sp, int i, int j, int q) {
+            return pt + ((((int64_t)sp * NWV + wave) * C::FM + i) * C::FN + j) * 8 * WAVE + q * WAVE + lane;
+        };
+#pragma unroll
+        for (int i = 0; i < C::FM; i++)
+#pragma unroll
+            for (int j = 0; j < C::FN; j++)
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    const f32x2 v = {acc[i][j][2 * q], acc[i][j][2 * q + 1]};
+                    __hip_atomic_store(slot(sk.split, i, j, q), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(sk.cnt + sk.wtile, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = prev == (unsigned)(sk.nsplit - 1);
+            if (last) __hip_atomic_store(sk.cnt + sk.wtile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = last;
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        // one split at a time: every load of the split is issued before any
+        // is used (the compiler keeps device-coherent loads in program order,
+        // so loads interleaved with the sums would each wait for the last)
+        for (int sp = 0; sp < sk.nsplit; sp++) {
+            uint64_t v[C::FM][C::FN][8];
+#pragma unroll
+            for (int i = 0; i < C::FM; i++)
+#pragma unroll
+                for (int j = 0; j < C::FN; j++)
+#pragma unroll
+                    for (int q = 0; q < 8; q++)
+                        v[i][j][q] = __hip_atomic_load(slot(sp, i, j, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int i = 0; i < C::FM; i++)
+#pragma unroll
+                for (int j = 0; j < C::FN; j++)
+#pragma unroll
+                    for (int q = 0; q < 8; q++) {
+                        const f32x2 t = __builtin_bit_cast(f32x2, v[i][j][q]);
+                        acc[i][j][2 * q] = sp == 0 ? t.x : acc[i][j][2 * q] + t.x;
+                        acc[i][j][2 * q + 1] = sp == 0 ? t.y : acc[i][j][2 * q + 1] + t.y;
+                    }
+        }
     }
 
     // ---- epilogue: Y = alpha_x*alpha_w * acc + X_S W_S^T
@@ -315,28 +428,46 @@ __global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
     lds_tile<256, 256, 2, 4, TAIL>(a, tm, tn, lds);
 }
 
+// code stages in flight for the 128 x 128 tile (one wave per SIMD per
+// workgroup): three measured 5-9% faster than one at M = 65..1024
+constexpr int PF128 = 3;
+
 // 128 x 128 tiles, four waves of 64 x 64 (two workgroups per CU): for grids
-// too small for the 256 x 256 tile
+// too small for the 256 x 256 tile; where even these tiles leave CUs idle,
+// the K range is split nsplit ways (cnt and part in the workspace)
 template <bool TAIL>
-__global__ __launch_bounds__(256) void prefill_lds128_kernel(GemmArgs a)
+__global__ __launch_bounds__(256) void prefill_lds128_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tiles_m = (int)((a.M + 127) / 128), tiles_n = (int)((a.N + 127) / 128);
-    int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    lds_tile<128, 128, 2, 2, TAIL>(a, tm, tn, lds);
+    int tm, tn, split;
+    tile_split_of(blockIdx.x, gridDim.x, nsplit, tiles_m, tiles_n, tm, tn, split);
+    SplitK sk;
+    sk.split = split;
+    sk.nsplit = nsplit;
+    sk.wtile = (int64_t)tm * tiles_n + tn;
+    sk.cnt = cnt;
+    sk.part = part;
+    lds_tile<128, 128, 2, 2, TAIL, PF128, true>(a, tm, tn, lds, sk);
 }
 
 // the same tiles over column segments: tile columns numbered across them
 template <int BT, int WGN, bool TAIL>
-__global__ __launch_bounds__(64 * 2 * WGN) void prefill_seg_kernel(SegTable t)
+__global__ __launch_bounds__(64 * 2 * WGN) void prefill_seg_kernel(SegTable t, int nsplit, unsigned *cnt,
+                                                                   float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tiles_m = (int)((t.a.M + BT - 1) / BT);
-    int tm, tn, local;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, t.start[t.nseg], tm, tn);
+    const int tiles_m = (int)((t.a.M + BT - 1) / BT), tiles_n = t.start[t.nseg];
+    int tm, tn, local, split;
+    tile_split_of(blockIdx.x, gridDim.x, nsplit, tiles_m, tiles_n, tm, tn, split);
     const GemmArgs a = seg_args(t, tn, local);
-    lds_tile<BT, BT, 2, WGN, TAIL>(a, tm, local, lds);
+    SplitK sk;
+    sk.split = split;
+    sk.nsplit = nsplit;
+    sk.wtile = (int64_t)tm * tiles_n + tn;
+    sk.cnt = cnt;
+    sk.part = part;
+    lds_tile<BT, BT, 2, WGN, TAIL, (BT == 128 ? PF128 : 1), (BT == 128)>(a, tm, local, lds, sk);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,7 +509,55 @@ __global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
     const GroupDesc &d = ga.g[e];
     const GemmArgs a{d.Xq, d.Xs, d.alpha_x, d.X_S, d.Wq, d.Ws, d.alpha_w, d.W_S,
                      d.M, ga.N, ga.K, ga.k, d.Y, ga.N};
-    lds_tile<BM, BN, 2, 2, TAIL>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
+    lds_tile<BM, BN, 2, 2, TAIL, PF128>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill plan: the 256 x 256 tile when its grid fills the GPU, else the
+// 128 x 128 tile.  Below 128 tiles the K range is also split, as many ways as
+// keep the workgroups within 256 and each split at least eight 64-channel
+// steps: at M = 65..1024 on the Qwen3-8B shapes that count was the fastest
+// measured or within 1 us of it (q at M = 128: 52 us unsplit, 27 us in eight
+// splits; down: 148 -> 40 us).  The partial tiles take at most 256 x 64 KB.
+struct PrefillPlan {
+    bool big;
+    int nsplit;
+    int64_t tiles;     // output tiles (of the chosen size)
+    size_t ws;         // workspace: tile counters, then nsplit partial tiles each
+};
+
+// The arrival counters sit in a fixed region at the front of the workspace,
+// one slot per output tile, whatever the shape: splits happen only below
+// SPLIT_MAX_TILES tiles, so a call never reads another shape's partial tiles
+// as counters, and every call leaves all of them zero.
+constexpr int64_t SPLIT_MAX_TILES = 128;
+constexpr int64_t SPLIT_WORKGROUPS = 256;     // tiles x splits at most
+constexpr int64_t SPLIT_MIN_STEPS = 8;        // 64-channel K steps per split at least
+constexpr size_t SPLIT_COUNTER_BYTES = 1024;
+static_assert(SPLIT_MAX_TILES * 4 <= (int64_t)SPLIT_COUNTER_BYTES, "counter region");
+
+// tiles_n128: tile columns at 128 (the segment launch counts them per segment)
+static PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, int64_t tiles_n128)
+{
+    PrefillPlan p{false, 1, 0, 0};
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 >= 240) {
+        p.big = true;
+        p.tiles = t256;
+        return p;
+    }
+    p.tiles = ((M + 127) / 128) * tiles_n128;
+    const int64_t nk = K / LdsCfg::BKL;
+    if (p.tiles < SPLIT_MAX_TILES && p.tiles > 0) {
+        int64_t sp = std::min<int64_t>(SPLIT_WORKGROUPS / p.tiles, nk / SPLIT_MIN_STEPS);
+        if (sp > 1) {
+            const int64_t per = (nk + sp - 1) / sp;
+            sp = (nk + per - 1) / per;          // every split holds at least one step
+        }
+        p.nsplit = (int)std::max<int64_t>(sp, 1);
+    }
+    if (p.nsplit > 1) p.ws = SPLIT_COUNTER_BYTES + (size_t)p.tiles * p.nsplit * 128 * 128 * 4;
+    return p;
 }
 
 template <bool TAIL>
@@ -399,7 +578,7 @@ static hipError_t launch_prefill_lds(const GemmArgs &a, const SegSpec *sp, hipSt
     if (sp) {
         const SegTable t = make_seg_table(a, *sp, C::BN);
         hipLaunchKernelGGL((prefill_seg_kernel<256, 4, TAIL>), dim3((unsigned)(tiles_m * t.start[t.nseg])),
-                           dim3(C::NT), lds, s, t);
+                           dim3(C::NT), lds, s, t, 1, (unsigned *)nullptr, (float *)nullptr);
     } else {
         const int64_t tiles = tiles_m * ((a.N + C::BN - 1) / C::BN);
         hipLaunchKernelGGL(prefill_lds_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
@@ -408,18 +587,20 @@ static hipError_t launch_prefill_lds(const GemmArgs &a, const SegSpec *sp, hipSt
 }
 
 template <bool TAIL>
-static hipError_t launch_prefill_lds128(const GemmArgs &a, const SegSpec *sp, hipStream_t s)
+static hipError_t launch_prefill_lds128(const GemmArgs &a, const SegSpec *sp, const PrefillPlan &p, void *ws,
+                                        hipStream_t s)
 {
     using C = LdsGeo<128, 128, 2, 2>;
     const size_t lds = 2 * C::TILE;
-    const int64_t tiles_m = (a.M + C::BM - 1) / C::BM;
+    unsigned *cnt = p.nsplit > 1 ? static_cast<unsigned *>(ws) : nullptr;
+    float *part = p.nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + SPLIT_COUNTER_BYTES)
+                               : nullptr;
+    const dim3 grid((unsigned)(p.tiles * p.nsplit));
     if (sp) {
         const SegTable t = make_seg_table(a, *sp, C::BN);
-        hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL>), dim3((unsigned)(tiles_m * t.start[t.nseg])),
-                           dim3(C::NT), lds, s, t);
+        hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL>), grid, dim3(C::NT), lds, s, t, p.nsplit, cnt, part);
     } else {
-        const int64_t tiles = tiles_m * ((a.N + C::BN - 1) / C::BN);
-        hipLaunchKernelGGL(prefill_lds128_kernel<TAIL>, dim3((unsigned)tiles), dim3(C::NT), lds, s, a);
+        hipLaunchKernelGGL(prefill_lds128_kernel<TAIL>, grid, dim3(C::NT), lds, s, a, p.nsplit, cnt, part);
     }
     return hipGetLastError();
 }
@@ -1092,66 +1273,135 @@ static hipError_t run_decode3(const GemmArgs &a, const SegSpec *sp, hipStream_t 
     return hipGetLastError();
 }
 
-// waves per workgroup so that each wave holds at most CPW chunks; false when
-// even MAXNW waves would need more (then the looping form is used)
-template <int MB, int CB, int CPW, int MAXNW>
-static bool run_decode3_k(const GemmArgs &a, const SegSpec *sp, hipStream_t s, hipError_t &e)
+// ===========================================================================
+// tile columns of the 128-column tiles over the segments of sp (or of a.N)
+static int64_t tiles_n128(int64_t N, const GemmSeg *seg, int nseg)
 {
-    const int nchunk = (int)(a.K / BK);
-    if (nchunk <= 4 * CPW) { e = run_decode3<MB, CB, 4, CPW>(a, sp, s); return true; }
-    if (nchunk <= 8 * CPW) { e = run_decode3<MB, CB, 8, CPW>(a, sp, s); return true; }
-    if (MAXNW >= 16 && nchunk <= 16 * CPW) { e = run_decode3<MB, CB, (MAXNW >= 16 ? 16 : 8), CPW>(a, sp, s); return true; }
-    return false;
+    if (!seg) return (N + 127) / 128;
+    int64_t t = 0;
+    for (int i = 0; i < nseg; i++) t += (seg[i].N + 127) / 128;
+    return t;
+}
+
+size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K)
+{
+    // the decode path keeps no partial results in device memory
+    if (p != Path::Prefill || M <= 0 || N <= 0 || K <= 0) return 0;
+    return plan_prefill(M, N, K, tiles_n128(N, nullptr, 0)).ws;
+}
+
+size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int nseg)
+{
+    int64_t N = 0;
+    for (int i = 0; i < nseg; i++) N += seg[i].N;
+    if (p != Path::Prefill || M <= 0 || N <= 0 || K <= 0) return 0;
+    return plan_prefill(M, N, K, tiles_n128(N, seg, nseg)).ws;
 }
 
 // ===========================================================================
-size_t gemm_ws_bytes(Path, int64_t, int64_t, int64_t)
+// Configuration choice (plan_gemm) and launch (dispatch_gemm).
+// Decode configurations come from measured sweeps on MI355X (Qwen3-8B
+// projection shapes, M = 1, 4, 8, 16, 32, 64):
+//  - M <= 4 with the FP16 activations fitting 64 KB of LDS: the LDS form,
+//    eight waves of four chunks up to K = 4096, sixteen waves beyond;
+//  - M <= 16: wide N (>= 8192 columns) 48 columns per workgroup streaming one
+//    chunk at a time (N = 12288: 6-9% faster than the single-round form at
+//    M = 8-16); K up to 4096 single round, eight waves of four chunks; longer
+//    K streaming, 16 columns per workgroup (K = 12288: 25% faster than the
+//    single round at M = 4-16, whose sixteen waves hold six chunks each);
+//  - M in 17..32: wide N with K <= 4096 the single-round form with 48 columns
+//    per workgroup (one workgroup per CU at N = 12288); otherwise streaming
+//    over 8 waves;
+//  - M in 33..64: streaming, 48 columns per workgroup for wide N.
+enum class Kern { P256, P128, XL8_4, XL16_4, XL16_6, XL16_8, D2_1_3, D3_1_1, D2_1_1, D3_2_3_W4, D3_2_3_W8,
+                  D2_2_1, D2_4_3, D2_4_1 };
+
+struct GemmPlan {
+    Path path;
+    Kern kern;
+    int rows, cols;         // output tile of one workgroup
+    PrefillPlan pp;         // prefill: tile size, K split, workspace
+};
+
+static GemmPlan plan_gemm(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg *seg, int nseg)
 {
-    return 0;        // neither datapath keeps partial results in device memory
+    GemmPlan g{};
+    g.pp = PrefillPlan{false, 1, 0, 0};
+    if (K == 0) p = Path::Prefill;      // the decode kernels assume at least one K chunk
+    g.path = p;
+    if (p == Path::Prefill) {
+        // largest tile that still gives every CU a tile, then a K split
+        g.pp = plan_prefill(M, N, K, tiles_n128(N, seg, nseg));
+        g.kern = g.pp.big ? Kern::P256 : Kern::P128;
+        g.rows = g.cols = g.pp.big ? 256 : 128;
+        return g;
+    }
+    const int nchunk = (int)(K / BK);
+    const int64_t colblocks = (N + 15) / 16;
+    if (M <= 16) {
+        g.rows = 16;
+        g.cols = 16;
+        // 16-byte aligned scale pairs need an even chunk count
+        if (M <= 4 && M * K * 2 <= XLDS_MAX && nchunk >= 2 && nchunk % 2 == 0 && nchunk <= 16 * 8) {
+            g.kern = nchunk <= 8 * 4 ? Kern::XL8_4 : nchunk <= 16 * 4 ? Kern::XL16_4
+                   : nchunk <= 16 * 6 ? Kern::XL16_6 : Kern::XL16_8;
+        } else if (colblocks >= 512) {
+            g.kern = Kern::D2_1_3;
+            g.cols = 48;
+        } else {
+            g.kern = nchunk <= 32 ? Kern::D3_1_1 : Kern::D2_1_1;
+        }
+    } else if (M <= 32) {
+        g.rows = 32;
+        g.cols = 16;
+        if (colblocks >= 512 && nchunk <= 8 * 4) {
+            g.kern = nchunk <= 4 * 4 ? Kern::D3_2_3_W4 : Kern::D3_2_3_W8;
+            g.cols = 48;
+        } else {
+            g.kern = Kern::D2_2_1;
+        }
+    } else {
+        g.rows = 64;
+        g.cols = colblocks >= 512 ? 48 : 16;
+        g.kern = colblocks >= 512 ? Kern::D2_4_3 : Kern::D2_4_1;
+    }
+    return g;
 }
 
-// configuration choice and launch; sp != nullptr: the column segments of sp,
-// whose widths sum to a.N
+// launch; sp != nullptr: the column segments of sp, whose widths sum to a.N
 static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, void *ws, hipStream_t s)
 {
     if (a.M == 0 || a.N == 0) return hipSuccess;
-    if (a.K == 0) p = Path::Prefill;    // the decode kernels assume at least one K chunk
-    if (p == Path::Prefill) {
-        // largest tile that still gives every CU a tile
-        const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-        if (t256 >= 240) return a.k > 0 ? launch_prefill_lds<true>(a, sp, s) : launch_prefill_lds<false>(a, sp, s);
-        return a.k > 0 ? launch_prefill_lds128<true>(a, sp, s) : launch_prefill_lds128<false>(a, sp, s);
+    const GemmPlan g = plan_gemm(p, a.M, a.N, a.K, sp ? sp->seg : nullptr, sp ? sp->nseg : 0);
+    const bool t = a.k > 0;
+    switch (g.kern) {
+    case Kern::P256: return t ? launch_prefill_lds<true>(a, sp, s) : launch_prefill_lds<false>(a, sp, s);
+    case Kern::P128: return t ? launch_prefill_lds128<true>(a, sp, g.pp, ws, s) : launch_prefill_lds128<false>(a, sp, g.pp, ws, s);
+    case Kern::XL8_4: return run_decode_xlds<8, 4>(a, sp, s);
+    case Kern::XL16_4: return run_decode_xlds<16, 4>(a, sp, s);
+    case Kern::XL16_6: return run_decode_xlds<16, 6>(a, sp, s);
+    case Kern::XL16_8: return run_decode_xlds<16, 8>(a, sp, s);
+    case Kern::D2_1_3: return run_decode2<1, 3, 8, 1>(a, sp, s);
+    case Kern::D3_1_1: return run_decode3<1, 1, 8, 4>(a, sp, s);
+    case Kern::D2_1_1: return run_decode2<1, 1, 8, 1>(a, sp, s);
+    case Kern::D3_2_3_W4: return run_decode3<2, 3, 4, 4>(a, sp, s);
+    case Kern::D3_2_3_W8: return run_decode3<2, 3, 8, 4>(a, sp, s);
+    case Kern::D2_2_1: return run_decode2<2, 1, 8, 1>(a, sp, s);
+    case Kern::D2_4_3: return run_decode2<4, 3, 8, 1>(a, sp, s);
+    case Kern::D2_4_1: return run_decode2<4, 1, 8, 2>(a, sp, s);
     }
-    // weight-streaming decode path; configurations chosen from measured sweeps
-    // on MI355X (Qwen3-8B projection shapes, M = 1, 4, 8, 16, 32, 64)
-    hipError_t e = hipSuccess;
-    const int nchunk = (int)(a.K / BK);
-    const int64_t colblocks = (a.N + 15) / 16;
-    if (a.M <= 16) {
-        if (a.M <= 4 && a.M * a.K * 2 <= XLDS_MAX && nchunk >= 2 && nchunk % 2 == 0) {   // 16-byte aligned scale pairs
-            if (nchunk <= 8 * 4) return run_decode_xlds<8, 4>(a, sp, s);
-            if (nchunk <= 16 * 4) return run_decode_xlds<16, 4>(a, sp, s);
-            if (nchunk <= 16 * 6) return run_decode_xlds<16, 6>(a, sp, s);
-            if (nchunk <= 16 * 8) return run_decode_xlds<16, 8>(a, sp, s);
-        }
-        // wide N: 48 columns per workgroup, streaming one chunk at a time
-        // (N = 12288: 6-9% faster than the single-round form at M = 8-16);
-        // K up to 4096: single round, eight waves of four chunks; longer K:
-        // streaming, 16 columns per workgroup (K = 12288: 25% faster than the
-        // single round at M = 4-16, whose sixteen waves hold six chunks each)
-        if (colblocks >= 512) return run_decode2<1, 3, 8, 1>(a, sp, s);
-        if (nchunk <= 32) return run_decode3<1, 1, 8, 4>(a, sp, s);
-        return run_decode2<1, 1, 8, 1>(a, sp, s);
-    }
-    // M in 17..64: wide N at M <= 32 takes the single-round form with 48
-    // columns per workgroup (one workgroup per CU at N = 12288); otherwise
-    // the streaming form over 8 waves
-    if (a.M <= 32) {
-        if (colblocks >= 512 && run_decode3_k<2, 3, 4, 8>(a, sp, s, e)) return e;
-        return run_decode2<2, 1, 8, 1>(a, sp, s);
-    }
-    if (colblocks >= 512) return run_decode2<4, 3, 8, 1>(a, sp, s);
-    return run_decode2<4, 1, 8, 2>(a, sp, s);
+    return hipErrorInvalidValue;
+}
+
+void gemm_plan_info(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg *seg, int nseg, int32_t out[5])
+{
+    const GemmPlan g = plan_gemm(p, M, N, K, seg, nseg);
+    out[0] = g.path == Path::Decode ? 1 : 2;
+    // every prefill tile size sums K in the same order: one kernel number
+    out[1] = g.path == Path::Prefill ? 0 : (int32_t)g.kern;
+    out[2] = g.rows;
+    out[3] = g.cols;
+    out[4] = g.pp.nsplit;
 }
 
 hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t, hipStream_t s)

@@ -43,6 +43,11 @@ struct GemmArgs {
 };
 enum class Path { Decode, Prefill };
 size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K);
+struct GemmSeg;
+size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int nseg);
+// {path taken (1 decode, 2 prefill), kernel, tile rows, tile columns, K splits}
+// of a call of this shape (seg: the column segments of a multi launch, or null)
+void gemm_plan_info(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg *seg, int nseg, int32_t out[5]);
 hipError_t launch_gemm(Path p, const GemmArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 // one column segment of a launch that shares the activation operands: its
 // own weights, tensor scale, side columns and output of width N

@@ -69,6 +69,10 @@ _SIGS = {
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
                                   _sz, ctypes.c_int, _vp]),
     "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "splice_multi_workspace_size": (_sz, [_i64, _i64, _i32, ctypes.POINTER(_Seg), _i32]),
+    "splice_gemm_plan": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(_i32)]),
+    "splice_multi_plan": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_Seg), _i32, ctypes.c_int,
+                                         ctypes.POINTER(_i32)]),
     "splice_probe_mfma_f16": (ctypes.c_int, [_i64, _i64, _vp, _vp]),
     "splice_probe_stream_read": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "splice_tim_filter": (ctypes.c_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _i64, _i64, _i64, _vp,
@@ -265,12 +269,30 @@ def workspace(nbytes, device):
     return t
 
 
+def gemm_plan(M, N, K, path=PATH_AUTO):
+    """(path taken: 1 decode / 2 prefill, kernel, tile rows, tile columns, K splits)
+    of a splice_gemm call of this shape."""
+    out = (_i32 * 5)()
+    _check("splice_gemm_plan", lib().splice_gemm_plan(M, N, K, path, out))
+    return tuple(out)
+
+
+def multi_plan(M, K, widths, path=PATH_AUTO):
+    """The plan of a splice_gemm_multi call with segments of these widths."""
+    arr = (_Seg * len(widths))()
+    for i, n in enumerate(widths):
+        arr[i] = _Seg(None, None, None, None, n, None, n)
+    out = (_i32 * 5)()
+    _check("splice_multi_plan", lib().splice_multi_plan(M, K, arr, len(widths), path, out))
+    return tuple(out)
+
+
 def splice_gemm(Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, path=PATH_AUTO, out=None, ws=None):
     M, K = Xq.shape[0], Xq.shape[1] * 2
     N = Wq.shape[0]
     k = 0 if X_S is None else X_S.shape[1]
     Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
-    need = workspace_size(M, N, K, k) if path != PATH_PREFILL else 0
+    need = workspace_size(M, N, K, k)
     if ws is None and need:
         ws = workspace(need, Xq.device)
     _check("splice_gemm",
@@ -284,7 +306,7 @@ def nvfp4_gemm(Xq, Xs, alpha_x, Wq, Ws, alpha_w, path=PATH_AUTO, out=None, ws=No
     M, K = Xq.shape[0], Xq.shape[1] * 2
     N = Wq.shape[0]
     Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
-    need = workspace_size(M, N, K, 0) if path != PATH_PREFILL else 0
+    need = workspace_size(M, N, K, 0)
     if ws is None and need:
         ws = workspace(need, Xq.device)
     _check("nvfp4_gemm",
@@ -351,15 +373,15 @@ def splice_gemm_multi(Xq, Xs, alpha_x, X_S, weights, path=PATH_AUTO, out=None, w
     k == 0); out: list of fp32 outputs [M, N_i] or None.  Returns the outputs."""
     M, K = Xq.shape[0], Xq.shape[1] * 2
     k = 0 if X_S is None else X_S.shape[1]
-    need = workspace_size(M, sum(w[0].shape[0] for w in weights), K, k) if path != PATH_PREFILL else 0
-    if ws is None and need:
-        ws = workspace(need, Xq.device)
     if out is None:
         out = [torch.empty(M, w[0].shape[0], dtype=torch.float32, device=Xq.device) for w in weights]
     arr = (_Seg * max(len(weights), 1))()
     for i, (w, Y) in enumerate(zip(weights, out)):
         arr[i] = _Seg(_p(w[0]), _p(w[1]), _p(w[2]), _p(w[3]) if k else None, w[0].shape[0], _p(Y),
                       Y.stride(0))
+    need = lib().splice_multi_workspace_size(M, K, k, arr, len(weights))
+    if ws is None and need:
+        ws = workspace(need, Xq.device)
     _check("splice_gemm_multi",
            lib().splice_gemm_multi(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, M, K, k, arr,
                                    len(weights), _p(ws), 0 if ws is None else ws.numel(), path,

@@ -168,14 +168,16 @@ int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
  *       SPLICE_PATH_PREFILL.
  * ws: DEVICE workspace of at least splice_workspace_size(M, N, K, k) bytes,
  *     16-byte aligned (NULL is allowed when that size is 0; a smaller or
- *     missing workspace returns SPLICE_ERR_WORKSPACE).  Where the K range is
- *     split over workgroups it holds one arrival counter per column tile and
- *     the partial tiles, which the workgroup completing a tile sums in split
- *     order (so Y does not depend on arrival order).  The counters must be
- *     zero when the workspace is first used -- zero-fill it once after
- *     allocating it -- and every call leaves them zero again, so one
- *     workspace serves any sequence of calls ordered on a stream (calls that
- *     may run concurrently need workspaces of their own). */
+ *     missing workspace returns SPLICE_ERR_WORKSPACE).  The prefill path
+ *     splits the K range over workgroups when its output tiles alone would
+ *     leave CUs idle (small M: up to a few hundred rows); the workspace then
+ *     holds one arrival counter per output tile and the fp32 partial tiles,
+ *     which the workgroup completing a tile sums in split order, so Y does not
+ *     depend on arrival order.  The counters must be zero when the workspace
+ *     is first used -- zero-fill it once after allocating it -- and every call
+ *     leaves them zero again, so one workspace serves any sequence of calls
+ *     ordered on a stream (calls that may run concurrently need workspaces of
+ *     their own).  At most about 24 MiB; 0 for large M and on the decode path. */
 int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
                 const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
                 int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy,
@@ -232,14 +234,14 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
  *          width N (N >= 0; 0 skips the segment).
  *   path   as for splice_gemm; the kernel configuration is chosen for M and
  *          the sum of the widths, as one call of that width would choose it.
- * Each segment's Y equals splice_gemm's for that segment alone: bit for bit
- * on the prefill path (every tile size sums K in the same order), and on the
- * decode path whenever the call alone would pick the same configuration (for
- * the Qwen3-8B q/k/v and gate/up widths it does); within the GEMM tolerance
- * otherwise.  Errors as splice_gemm, checked per segment before anything is
- * launched.
- *   ws, ws_bytes  as for splice_gemm, sized by splice_workspace_size(M, sum
- *          of the widths, K, k). */
+ * Each segment's Y equals splice_gemm's for that segment alone bit for bit
+ * whenever the call alone would make the same plan (splice_gemm_plan against
+ * splice_multi_plan: the same path, kernel and K split) -- for the Qwen3-8B
+ * q/k/v and gate/up widths it does at M <= 64 and from M = 1024 on -- and
+ * within the GEMM tolerance otherwise.  Errors as splice_gemm, checked per segment before
+ * anything is launched.
+ *   ws, ws_bytes  as for splice_gemm, sized by splice_multi_workspace_size
+ *          (the output tiles are counted segment by segment). */
 #define SPLICE_SEG_MAX 8
 typedef struct {
     const uint8_t *Wq, *Ws;
@@ -267,11 +269,28 @@ int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t
                                    const float *alpha_x, int64_t M, int64_t K, int32_t k,
                                    const splice_weight_seg *segs, int32_t nseg, splice_stream_t stream);
 
-/* Workspace bytes splice_gemm / nvfp4_gemm / splice_gemm_multi (N = the sum
- * of the widths) need for this shape on the path SPLICE_PATH_AUTO takes
- * (0 on the prefill path; k is part of the contract but does not change the
- * size).  A few MiB at most for the decode shapes. */
+/* Workspace bytes splice_gemm / nvfp4_gemm need for this shape, enough for
+ * whichever path the call takes (k is part of the contract but does not
+ * change the size). */
 size_t splice_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
+
+/* Workspace bytes splice_gemm_multi needs for these segments (HOST array, as
+ * passed to it), enough for whichever path the call takes. */
+size_t splice_multi_workspace_size(int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs,
+                                   int32_t nseg);
+
+/* Diagnostic: the launch a splice_gemm / nvfp4_gemm call (splice_gemm_plan)
+ * or a splice_gemm_multi call (splice_multi_plan) of this shape and path
+ * makes, written to plan[0..5): the path taken (1 decode, 2 prefill), a
+ * kernel number (0 for every prefill tile size: they sum K in the same
+ * order), the output tile of one workgroup (rows, columns) and the number of
+ * K ranges the tile's sum is split into.  Two calls with the same M and K
+ * whose plans agree in path, kernel number and K ranges run the same
+ * arithmetic on every output, so they give the same bits.  Returns SPLICE_ERR_INVALID_ARG for a bad shape,
+ * path or pointer; computes nothing on the GPU. */
+int splice_gemm_plan(int64_t M, int64_t N, int64_t K, int path, int32_t *plan);
+int splice_multi_plan(int64_t M, int64_t K, const splice_weight_seg *segs, int32_t nseg, int path,
+                      int32_t *plan);
 
 /* ---------------------------------------------------------------------------
  * Grouped SpliceGEMM: G independent problems sharing N, K and k (experts of

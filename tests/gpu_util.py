@@ -34,6 +34,24 @@ def scalar(t):
     return np.float32(t.item())
 
 
+def pack_magnitudes(xq, xs, ax, xS, wq, ws, aw, wS):
+    """A function of (row, column) giving the sum over the reduction of |x * w|
+    for that output of the oracle's product of these packs: the dequantized
+    FP4 products and the BF16 side products, in output units."""
+    import oracle as O
+
+    def terms(i, j):
+        dx = O.dequantize(xq[i:i + 1], xs[i:i + 1], ax)[0]
+        dw = O.dequantize(wq[j:j + 1], ws[j:j + 1], aw)[0]
+        t = float(np.abs(dx * dw).sum())
+        if xS is not None and xS.shape[1]:
+            sx = np.array([O.bf16_to_double(b) for b in xS[i]])
+            sw = np.array([O.bf16_to_double(b) for b in wS[j]])
+            t += float(np.abs(sx * sw).sum())
+        return t
+    return terms
+
+
 def gemm_errors(Y, Yo):
     Y = np.asarray(Y, np.float64)
     Yo = np.asarray(Yo, np.float64)

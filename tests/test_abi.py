@@ -63,10 +63,32 @@ def test_gemm_argument_errors(L, kw, code):
 
 
 def test_gemm_workspace_size(L):
-    # the decode path keeps no partial results in device memory
-    for M, N, K, k in ((1, 1024, 4096, 64), (64, 12288, 4096, 64), (0, 1024, 4096, 64),
-                       (1, 4096, 12288, 0)):
+    # the decode path keeps no partial results in device memory; the prefill
+    # path splits K (and needs a workspace) only where its tiles alone leave
+    # CUs idle, and the size covers a call forced onto the prefill path
+    for M, N, K, k in ((8192, 4096, 4096, 64), (4096, 12288, 4096, 64), (0, 1024, 4096, 64)):
         assert L.splice_workspace_size(M, N, K, k) == 0
+    for M, N, K in ((1, 1024, 4096), (64, 4096, 4096), (65, 4096, 4096), (128, 1024, 4096),
+                    (512, 1024, 4096), (200, 300, 12288)):
+        assert 0 < L.splice_workspace_size(M, N, K, 64) <= 17 << 20
+    assert L.splice_workspace_size(8, 1024, 512, 0) == 0        # too few K steps to split
+
+
+def test_gemm_missing_workspace(L):
+    need = L.splice_workspace_size(128, 1024, 4096, 64)
+    assert gemm(L, M=128, N=1024, K=4096, k=64) == splice.ERR_WORKSPACE
+    assert gemm(L, M=128, N=1024, K=4096, k=64, ws=FAKE, wsb=need - 1) == splice.ERR_WORKSPACE
+    assert gemm(L, M=128, N=1024, K=4096, k=64, ws=FAKE + 8, wsb=need) == splice.ERR_WORKSPACE
+
+
+def test_multi_workspace_size(L):
+    S = splice._Seg
+    segs = (S * 3)(S(FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 4096), S(FAKE, FAKE, FAKE, FAKE, 1000, FAKE, 1000),
+                   S(FAKE, FAKE, FAKE, FAKE, 1000, FAKE, 1000))
+    # 128-column tiles are counted per segment: 32 + 8 + 8, more than the 48 of one 6000-wide call
+    multi = L.splice_multi_workspace_size(128, 4096, 64, segs, 3)
+    assert multi >= L.splice_workspace_size(128, 6000, 4096, 64) > 0
+    assert L.splice_multi_workspace_size(8192, 4096, 64, segs, 3) == 0
 
 
 def test_nvfp4_argument_errors(L):

@@ -14,7 +14,7 @@ import torch
 import oracle as O
 from fp4_gemm_sparse_amd import splice as S
 from fp4_gemm_sparse_amd import synth
-from gpu_util import assert_gemm_close, dev, host, scalar
+from gpu_util import pack_magnitudes, assert_gemm_close, dev, host, scalar
 
 pytestmark = pytest.mark.gpu
 
@@ -286,13 +286,8 @@ def oracle_pipeline(X_warm, X, W, k, rows=None, cols=None, idx=None):
 
 def product_magnitudes(o, i, j):
     """Sum over the reduction of |x * w| for output (i, j) of an
-    oracle_pipeline result: the dequantized FP4 products and the BF16 side
-    products, in output units."""
-    dx = O.dequantize(o["xq"][i:i + 1], o["xs"][i:i + 1], o["ax"])[0]
-    dw = O.dequantize(o["wq"][j:j + 1], o["ws"][j:j + 1], o["aw"])[0]
-    sx = np.array([O.bf16_to_double(b) for b in o["xS"][i]])
-    sw = np.array([O.bf16_to_double(b) for b in o["wS"][j]])
-    return float(np.abs(dx * dw).sum() + np.abs(sx * sw).sum())
+    oracle_pipeline result, in output units."""
+    return pack_magnitudes(o["xq"], o["xs"], o["ax"], o["xS"], o["wq"], o["ws"], o["aw"], o["wS"])(i, j)
 
 
 def gpu_pipeline(X_warm, X, W, k, path=S.PATH_AUTO):
