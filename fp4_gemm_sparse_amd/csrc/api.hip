@@ -4,13 +4,58 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include <hip/hip_runtime.h>
 
 using namespace splice;
 
+// ---------------------------------------------------------------------------
+// Workspace of splice_gemm_noalloc: a file-scope device array (each GPU holds
+// its own copy for the life of the process).  Host code never passes the
+// array's name to a kernel -- on the host it only stands for the symbol --
+// but the device address hipGetSymbolAddress returns for the current device,
+// resolved once per device on the first call there.
+static __device__ __align__(256) uint8_t scratch[SPLICE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SPLIT_COUNTER_WORDS = (int)(SPLIT_COUNTER_BYTES / 4);
+
+__global__ void clear_words_kernel(unsigned *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 namespace {
+
+constexpr int NOALLOC_DEVICES = 64;
+std::mutex noalloc_mutex;
+void *noalloc_ptr[NOALLOC_DEVICES];
+
+// the device address of `scratch` on the current device; on the first call
+// there, its counter words are cleared on `s` ahead of any use
+hipError_t noalloc_scratch(hipStream_t s, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= NOALLOC_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(noalloc_mutex);
+    if (!noalloc_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(SPLIT_COUNTER_WORDS), 0, s,
+                           static_cast<unsigned *>(ptr), SPLIT_COUNTER_WORDS);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        noalloc_ptr[dev] = ptr;
+    }
+    *out = noalloc_ptr[dev];
+    return hipSuccess;
+}
 
 constexpr int64_t MAX_K = 65536;
 
@@ -239,6 +284,26 @@ int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, cons
 {
     GemmArgs a{Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy};
     return run_gemm(a, ws, ws_bytes, path, hs(stream));
+}
+
+int splice_gemm_noalloc(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
+                        const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
+                        int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy, int path,
+                        splice_stream_t stream)
+{
+    GemmArgs a{Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy};
+    int rc = check_gemm(a, path);
+    if (rc) return rc;
+    if (a.M == 0 || a.N == 0) return SPLICE_OK;
+    const Path p = choose_path(a.M, path);
+    const size_t need = gemm_ws_bytes(p, a.M, a.N, a.K);
+    if (need > SPLICE_NOALLOC_SCRATCH_BYTES) return SPLICE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = noalloc_scratch(hs(stream), &ws);
+        if (e != hipSuccess) return SPLICE_ERR_HIP;
+    }
+    return hip_status(launch_gemm(p, a, ws, need, hs(stream)));
 }
 
 int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint8_t *Wq,

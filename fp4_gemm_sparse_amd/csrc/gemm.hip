@@ -14,6 +14,7 @@
 // Reduction order: each MFMA consumes whole 8-channel pieces of one or two
 // NVFP4 blocks, A and B with the same channel mapping, so the hardware order
 // only permutes the terms of each dot product; K steps are summed in order.
+#include "../../include/splice.h"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "segments.hpp"
@@ -533,8 +534,10 @@ struct PrefillPlan {
 constexpr int64_t SPLIT_MAX_TILES = 128;
 constexpr int64_t SPLIT_WORKGROUPS = 256;     // tiles x splits at most
 constexpr int64_t SPLIT_MIN_STEPS = 8;        // 64-channel K steps per split at least
-constexpr size_t SPLIT_COUNTER_BYTES = 1024;
 static_assert(SPLIT_MAX_TILES * 4 <= (int64_t)SPLIT_COUNTER_BYTES, "counter region");
+// the largest workspace any shape takes fits the allocation-free entry's array
+static_assert(SPLIT_COUNTER_BYTES + (size_t)SPLIT_WORKGROUPS * 128 * 128 * 4 <= SPLICE_NOALLOC_SCRATCH_BYTES,
+              "no-alloc scratch");
 
 // tiles_n128: tile columns at 128 (the segment launch counts them per segment)
 static PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, int64_t tiles_n128)

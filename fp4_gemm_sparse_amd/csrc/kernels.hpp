@@ -42,6 +42,9 @@ struct GemmArgs {
     const int32_t *idx;
 };
 enum class Path { Decode, Prefill };
+// a K-split launch's workspace: SPLIT_COUNTER_BYTES of arrival counters (one
+// word per output tile), then the partial tiles
+constexpr size_t SPLIT_COUNTER_BYTES = 1024;
 size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K);
 struct GemmSeg;
 size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int nseg);

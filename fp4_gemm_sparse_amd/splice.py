@@ -66,6 +66,8 @@ _SIGS = {
                                              _vp]),
     "splice_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
                                    _vp, _i64, _vp, _sz, ctypes.c_int, _vp]),
+    "splice_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
+                                           _vp, _i64, ctypes.c_int, _vp]),
     "nvfp4_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
                                   _sz, ctypes.c_int, _vp]),
     "splice_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
@@ -299,6 +301,21 @@ def splice_gemm(Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, path=PATH_AUTO, out=
            lib().splice_gemm(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, _p(Wq), _p(Ws),
                              _p(alpha_w), _p(W_S) if k else None, M, N, K, k, _p(Y), Y.stride(0),
                              _p(ws), 0 if ws is None else ws.numel(), path, _stream()))
+    return Y
+
+
+def splice_gemm_noalloc(Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, path=PATH_AUTO, out=None):
+    """splice_gemm with the library's own per-device scratch as workspace:
+    nothing is allocated (out must be given for that; calls that overlap on
+    one GPU race)."""
+    M, K = Xq.shape[0], Xq.shape[1] * 2
+    N = Wq.shape[0]
+    k = 0 if X_S is None else X_S.shape[1]
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    _check("splice_gemm_noalloc",
+           lib().splice_gemm_noalloc(_p(Xq), _p(Xs), _p(alpha_x), _p(X_S) if k else None, _p(Wq), _p(Ws),
+                                     _p(alpha_w), _p(W_S) if k else None, M, N, K, k, _p(Y), Y.stride(0),
+                                     path, _stream()))
     return Y
 
 

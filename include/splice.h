@@ -183,6 +183,23 @@ int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, cons
                 int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy,
                 void *ws, size_t ws_bytes, int path, splice_stream_t stream);
 
+/* splice_gemm for callers that cannot allocate device memory (code under
+ * stream or graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results as splice_gemm (bit for bit), with
+ * the workspace taken from a device array the library holds for the life of
+ * the process, SPLICE_NOALLOC_SCRATCH_BYTES on every GPU it runs on (the
+ * largest workspace any shape needs).  The first call on a device looks the
+ * array up and clears its counters on `stream`; no call allocates or frees
+ * anything.  Every call on a GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams, different threads) race and must be
+ * ordered by the caller.  A shape whose workspace would exceed the array
+ * returns SPLICE_ERR_WORKSPACE; other errors as splice_gemm. */
+#define SPLICE_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u + 1024u)
+int splice_gemm_noalloc(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
+                        const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
+                        int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy, int path,
+                        splice_stream_t stream);
+
 /* Plain NVFP4 GEMM without compensation, the overhead baseline (the paper's
  * uncompensated FP4, Sec. 6.3): splice_gemm with k = 0. */
 int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x,

@@ -91,6 +91,19 @@ def test_multi_workspace_size(L):
     assert L.splice_multi_workspace_size(8192, 4096, 64, segs, 3) == 0
 
 
+def test_noalloc_argument_errors(L):
+    f = L.splice_gemm_noalloc
+    args = lambda **o: [o.get(n, FAKE) for n in ("Xq", "Xs", "ax", "XS", "Wq", "Ws", "aw", "WS")]
+    assert f(*args(), 4, 64, 100, 8, FAKE, 64, 0, None) == splice.ERR_INVALID_ARG      # K % 16
+    assert f(*args(), 4, 64, 144, 8, FAKE, 64, 0, None) == splice.ERR_UNSUPPORTED      # K % 128
+    assert f(*args(Ws=FAKE + 8), 4, 64, 256, 8, FAKE, 64, 0, None) == splice.ERR_INVALID_ARG
+    assert f(*args(), 65, 64, 256, 8, FAKE, 64, splice.PATH_DECODE, None) == splice.ERR_INVALID_ARG
+    assert f(*args(), 0, 64, 256, 8, FAKE, 64, 0, None) == splice.OK                   # no-op
+    # every shape's workspace fits the library's array (16 MiB + 1 KB)
+    for M, N, K in ((65, 64, 17408), (128, 1024, 4096), (100, 128, 65536), (127, 127, 12288)):
+        assert L.splice_workspace_size(M, N, K, 0) <= 16 * 1024 * 1024 + 1024
+
+
 def test_nvfp4_argument_errors(L):
     assert L.nvfp4_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, 4, None, 0, 0, None) \
         == splice.ERR_INVALID_ARG
