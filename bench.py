@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1536, help="token rows of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the value workload")
+    ap.add_argument("--no-forward", action="store_true", help="skip the forward-only step figure")
     ap.add_argument("--profile-workload", action="store_true",
                     help="only the calibration copy and 3 prefill SpliceGEMMs per projection "
                          "(the run that rocprofv3 --pmc passes profile)")
@@ -202,6 +203,37 @@ def main():
     value = flops_step / (ms_step * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s")
 
+    # forward only (the basis of the paper's kernel comparison): per layer
+    # input the activation preparation, then the GEMM launches; statistics,
+    # selection and the weight pre-split are left to the policy update
+    def fwd_step():
+        for launch in LAUNCHES:
+            g = P[launch[0]]["grp"]
+            S.quantize_nvfp4(g["X"], g["idx"], g["ax"], out=g["xpack"])
+            xq, xs, xS = g["xpack"]
+            if len(launch) == 1:
+                p = P[launch[0]]
+                wq, ws, wS = p["wpack"]
+                S.splice_gemm(xq, xs, g["ax"], xS, wq, ws, p["aw"], wS, path=S.PATH_PREFILL, out=p["Y"])
+            else:
+                S.splice_gemm_multi(xq, xs, g["ax"], xS,
+                                    [(P[n]["wpack"][0], P[n]["wpack"][1], P[n]["aw"], P[n]["wpack"][2])
+                                     for n in launch],
+                                    path=S.PATH_PREFILL, out=[P[n]["Y"] for n in launch])
+    ms_fwd = None
+    if not args.no_forward:
+        for _ in range(args.warmup):
+            fwd_step()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(args.steps):
+            fwd_step()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ms_fwd = f0.elapsed_time(f1) / args.steps
+        log(f"forward-only step {ms_fwd:.3f} ms, {flops_step / (ms_fwd * 1e-3) / 1e12:.1f} TFLOP/s")
+
     # dominant kernel: the prefill SpliceGEMM launches inside the timed steps
     per = {}
     for key, a, b in gemm_events:
@@ -239,6 +271,11 @@ def main():
                    "step": "per distinct layer input (q/k/v share one, gate/up share one): stats+select "
                            "and activation prep; per projection: weight alpha+pre-split and SpliceGEMM"},
         "roofline": roofline,
+        "forward_step": None if ms_fwd is None else {
+            "ms": round(ms_fwd, 4), "tflops": round(flops_step / (ms_fwd * 1e-3) / 1e12, 2),
+            "what": "per layer input the activation preparation (quantize + side gather), then the four "
+                    "GEMM launches; the statistics, selection and weight pre-split of the full step run "
+                    "once per policy update"},
         "mfma_f16_measured": {"tflops": round(mfma_measured, 1),
                               "gemm_frac": round(achieved / mfma_measured, 4),
                               "probe": "4 independent v_mfma_f32_32x32x16_f16 chains per wave, "
@@ -249,6 +286,8 @@ def main():
         result.update(extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream))
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, host, names, flops_step / M_PREFILL)
+        if not args.no_extra:
+            result["oracle_vs_gpu"] = oracle_vs_gpu(torch, S, host, names, result)
     print(json.dumps(result), flush=True)
 
 
@@ -326,6 +365,31 @@ def graph_timed_pair(torch, fa, fb, iters, reps=7):
 ROTATE_BYTES = 512 << 20        # distinct weight bytes a rotation walks, > the 256 MB last-level cache
 
 
+class StreamCeiling:
+    """Time of a pure streaming read of n bytes (splice_probe_stream_read),
+    measured like the decode calls: HIP-graph replay walking copies past the
+    last-level cache; the faster of 512 and 1024 workgroups."""
+
+    def __init__(self, torch, S, dev):
+        self.torch, self.S = torch, S
+        self.buf = torch.empty(ROTATE_BYTES + (64 << 20), dtype=torch.uint8, device=dev)
+        self.sink = torch.empty(1024 * 4, dtype=torch.int32, device=dev)
+        self.cache = {}
+
+    def us(self, nbytes):
+        nbytes = int(nbytes) // 16 * 16
+        if nbytes not in self.cache:
+            stride = (nbytes + 4095) // 4096 * 4096
+            nc = max(2, min(copies_for(nbytes), self.buf.numel() // stride))
+            best = None
+            for wgs in (512, 1024):
+                t = graph_timed(self.torch, lambda i: self.S.probe_stream_read(
+                    self.buf[(i % nc) * stride:], nbytes, wgs, self.sink), nc)
+                best = t if best is None else min(best, t)
+            self.cache[nbytes] = best * 1e3
+        return self.cache[nbytes]
+
+
 def copies_for(nbytes):
     """Copies of a weight pack so that one pass over them exceeds ROTATE_BYTES."""
     return max(2, -(-ROTATE_BYTES // int(nbytes)))
@@ -400,7 +464,8 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     # graph walks all of them, so the weights stream from HBM rather than the
     # 256 MB last-level cache.
     dec, fz = {}, {}
-    acc = {M: [0.0, 0.0, 0.0] for M in DECODE_MS}          # bytes, splice time, nvfp4 time
+    acc = {M: [0.0, 0.0, 0.0, 0.0, 0.0] for M in DECODE_MS}   # bytes, splice, nvfp4, projection splice / nvfp4
+    ceil = StreamCeiling(torch, S, dev)
     accf = {M: [0.0, 0.0] for M in FUSED_MS}               # two-call, fused
     rot = {}
     for n in names:
@@ -434,15 +499,32 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
             def fused(i):
                 w = cp[i % ncopy]
                 S.splice_gemm_decode_fused(X, p["idx"], p["ax"], w[0], w[1], p["aw"], w[2], out=Y)
+
+            # the complete projection, activation preparation included (the
+            # paper's kernel comparison), against the uncompensated one: X
+            # quantized with no protected channels, then the plain NVFP4 GEMM
+            ax0 = S.compute_alpha(X, None)
+            xq0 = S.quantize_nvfp4(X, None, ax0)
+
+            def proj_nv(i):
+                w = cp[i % ncopy]
+                S.quantize_nvfp4(X, None, ax0, out=xq0)
+                S.nvfp4_gemm(xq0[0], xq0[1], ax0, w[0], w[1], p["aw"], out=Y)
             if M in DECODE_MS:
                 t, tn = graph_timed_pair(torch, call, call_nv, iters)
+                tp, tpn = graph_timed_pair(torch, two, proj_nv, iters)
                 bts = (N * K * (0.5 + 1 / 16) + 2 * N * K_PROT + M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
                        + 4 * M * N)
+                cu = ceil.us(bts)
                 dec[f"{n}@M{M}"] = {"us": round(t * 1e3, 2), "GBps": round(bts / (t * 1e-3) / 1e9, 1),
-                                    "nvfp4_us": round(tn * 1e3, 2)}
+                                    "nvfp4_us": round(tn * 1e3, 2), "ceiling_us": round(cu, 2),
+                                    "projection_us": round(tp * 1e3, 2),
+                                    "projection_nvfp4_us": round(tpn * 1e3, 2)}
                 acc[M][0] += bts
                 acc[M][1] += t
                 acc[M][2] += tn
+                acc[M][3] += tp
+                acc[M][4] += tpn
             if M in FUSED_MS:
                 a2, af = graph_timed_pair(torch, two, fused, iters)
                 fz[f"{n}@M{M}"] = {"two_call_us": round(a2 * 1e3, 2), "fused_us": round(af * 1e3, 2)}
@@ -452,10 +534,14 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
         torch.cuda.empty_cache()
     tot_b = tot_t = tot_nv = 0.0
     for M in DECODE_MS:
-        bM, tM, nvM = acc[M]
+        bM, tM, nvM, tpM, tpnM = acc[M]
+        cM = sum(dec[f"{n}@M{M}"]["ceiling_us"] for n in names) * 1e-3
         dec[f"M{M}"] = {"GBps": round(bM / (tM * 1e-3) / 1e9, 1),
                         "frac_hbm": round(bM / (tM * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                        "overhead_pct": round(100.0 * (tM - nvM) / nvM, 2)}
+                        "ceiling_GBps": round(bM / (cM * 1e-3) / 1e9, 1),
+                        "frac_ceiling": round(cM / tM, 4),
+                        "overhead_pct": round(100.0 * (tM - nvM) / nvM, 2),
+                        "overhead_projection_pct": round(100.0 * (tpM - tpnM) / tpnM, 2)}
         tot_b += bM
         tot_t += tM
         tot_nv += nvM
@@ -467,6 +553,12 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                                "weights (over 512 MiB per projection); median of 7 replays, "
                                "alternating with the nvfp4_gemm graph; includes each kernel's "
                                "dispatch",
+                     "ceiling": "ceiling_us: a pure streaming read of the call's byte count "
+                                "(splice_probe_stream_read), timed the same way; frac_ceiling = "
+                                "ceiling time / decode time",
+                     "projection": "projection_us: activation quantize + SpliceGEMM; "
+                                   "projection_nvfp4_us: quantize without protection + plain NVFP4 "
+                                   "GEMM (overhead_projection_pct, the basis of the paper's Fig. 10)",
                      "rotation": rot,
                      "shapes": dec}
     for M in FUSED_MS:
@@ -487,7 +579,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     # four fused-preparation launches
     lay = {}
     for M in sorted(set(DECODE_MS) | set(FUSED_MS)):
-        t4 = t4n = b4 = t2p = tfp = 0.0
+        t4 = t4n = b4 = t2p = tfp = c4 = 0.0
         per = {}
         for launch in LAUNCHES:
             p0 = P[launch[0]]
@@ -531,9 +623,11 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                 per[key] = round(t * 1e3, 2)
                 t4 += t
                 t4n += tn
-                b4 += (M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
-                       + sum(P[n]["N"] * K * (0.5 + 1 / 16) + 2 * P[n]["N"] * K_PROT + 4 * M * P[n]["N"]
-                             for n in launch))
+                bl = (M * K * (0.5 + 1 / 16) + 2 * M * K_PROT
+                      + sum(P[n]["N"] * K * (0.5 + 1 / 16) + 2 * P[n]["N"] * K_PROT + 4 * M * P[n]["N"]
+                            for n in launch))
+                b4 += bl
+                c4 += ceil.us(bl) * 1e-3
             if M in FUSED_MS:
                 a2, af = graph_timed_pair(torch, two, fused, iters)
                 t2p += a2
@@ -548,6 +642,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                       "overhead_pct": round(100.0 * (t4 - t4n) / t4n, 2),
                       "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
                       "frac_hbm": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "ceiling_us": round(c4 * 1e3, 2), "frac_ceiling": round(c4 / t4, 4),
                       "launches_us": per})
         if M in FUSED_MS:
             r.update({"us_with_prep_two_call": round(t2p * 1e3, 2),
@@ -561,6 +656,12 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
                   "quantize + GEMM per input against splice_gemm_decode_fused_multi (one launch per "
                   "input), timed in alternation",
         "shapes": lay}
+
+    del ceil
+    torch.cuda.empty_cache()
+
+    # ---------------- token counts between decode and the timed prefill
+    out["m_sweep"] = m_sweep_measurements(torch, S, P, dev, stream)
 
     # ---------------- grouped MoE stand-in
     counts = synth.moe_counts()
@@ -639,6 +740,63 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     return out
 
 
+M_SWEEP = (65, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def m_sweep_measurements(torch, S, P, dev, stream):
+    """Token counts from just above the decode path to 32768 rows (the range
+    of the paper's kernel comparison, Fig. 10) on the q and gate shapes:
+    SpliceGEMM and the plain NVFP4 GEMM on the same packs, with each call's
+    plan (tile, K split).  Rows past the 8192 of the prefill workload repeat
+    its activations.  Up to 2048 rows the weights are walked in copies past
+    the last-level cache (HIP-graph replay); above, each call is
+    compute-bound and timed back to back."""
+    res = {}
+    for n in ("q", "gate"):
+        p = P[n]
+        K, N = p["K"], p["N"]
+        X = p["X"]
+        ncopy = copies_for(pack_bytes(p["wpack"]))
+        cp = [p["wpack"]] + [tuple(t.clone() for t in p["wpack"]) for _ in range(ncopy - 1)]
+        for M in M_SWEEP:
+            reps = -(-M // X.shape[0])
+            Xm = (X if reps == 1 else torch.cat([X] * reps))[:M]
+            xq = S.quantize_nvfp4(Xm, p["idx"], p["ax"])
+            Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+            ws = S.workspace(max(1, S.workspace_size(M, N, K, K_PROT)), dev)
+
+            def sp(i):
+                w = cp[i % ncopy]
+                S.splice_gemm(xq[0], xq[1], p["ax"], xq[2], w[0], w[1], p["aw"], w[2], out=Y, ws=ws,
+                              path=S.PATH_PREFILL)
+
+            def nv(i):
+                w = cp[i % ncopy]
+                S.nvfp4_gemm(xq[0], xq[1], p["ax"], w[0], w[1], p["aw"], out=Y, ws=ws, path=S.PATH_PREFILL)
+            if M <= 2048:
+                t, tn = graph_timed_pair(torch, sp, nv, max(20, ncopy))
+            else:
+                for _ in range(2):
+                    sp(0)
+                    nv(0)
+                t = timed(torch, stream, sp, 10)
+                tn = timed(torch, stream, nv, 10)
+            fl = 2.0 * M * N * K
+            plan = S.gemm_plan(M, N, K, S.PATH_PREFILL)
+            res[f"{n}@M{M}"] = {"us": round(t * 1e3, 2), "nvfp4_us": round(tn * 1e3, 2),
+                                "tflops": round(fl / (t * 1e-3) / 1e12, 1),
+                                "frac_peak": round(fl / (t * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                                "overhead_pct": round(100.0 * (t - tn) / tn, 2),
+                                "tile": plan[2], "k_splits": plan[4]}
+            log(f"m_sweep {n}@M{M}: {res[f'{n}@M{M}']}")
+            del xq, Y, Xm
+        del cp
+        torch.cuda.empty_cache()
+    res["timing"] = ("prefill path; M <= 2048: HIP-graph replay walking weight copies (over 512 MiB), "
+                     "median of 7 replays alternating with nvfp4_gemm; larger M: median of 10 calls")
+    return res
+
+
 def sweep_measurements(torch, S, synth, dev):
     """K=4096, N=12288, M in {64, 4096}: top-k protection for k in {0, 64, 128,
     256} and 64 random channels.  Error is the relative Frobenius distance of
@@ -689,6 +847,69 @@ def sweep_measurements(torch, S, synth, dev):
     return res
 
 
+def oracle_vs_gpu(torch, S, host, names, extras):
+    """The fp64 oracle's product timed per shape on the host cores beside the
+    GPU's time for the same call: the tiny configuration (whole pipeline),
+    every decode shape at M in {1, 8, 32, 64} and the q and o prefill shapes
+    in full; the other prefill shapes on their first 256 rows, scaled to 8192
+    rows and labelled as extrapolated.  The oracle works on its own packs of
+    the same bf16 inputs (quantization timed apart from the product)."""
+    import oracle as O
+    from fp4_gemm_sparse_amd import synth
+    out = {"cores": O.num_threads(), "nproc": os.cpu_count()}
+    # tiny: the whole pipeline on both sides
+    d = synth.tiny()
+    t0 = time.perf_counter()
+    idx, ax, _ = O.select_channels(d["X_warm"], K_PROT)
+    aw = O.compute_alpha(d["W"], idx)
+    xo, wo = O.quantize_nvfp4(d["X"], idx, ax), O.quantize_nvfp4(d["W"], idx, aw)
+    O.splice_gemm(xo[0], xo[1], ax, xo[2], wo[0], wo[1], aw, wo[2])
+    t_cpu = time.perf_counter() - t0
+    dv = lambda a: torch.from_numpy(a.view(np.int16)).cuda()
+    Xw, X, W = dv(d["X_warm"]), dv(d["X"]), dv(d["W"])
+    stream = torch.cuda.current_stream()
+
+    def tiny_gpu(i):
+        gi, gax, _ = S.select_channels(Xw, K_PROT)
+        gaw = S.compute_alpha(W, gi)
+        gx, gw = S.quantize_nvfp4(X, gi, gax), S.quantize_nvfp4(W, gi, gaw)
+        S.splice_gemm(gx[0], gx[1], gax, gx[2], gw[0], gw[1], gaw, gw[2])
+    tiny_gpu(0)
+    out["tiny"] = {"oracle_s": round(t_cpu, 4), "gpu_ms": round(timed(torch, stream, tiny_gpu, 20), 4),
+                   "what": "statistics, selection, both quantizations and the product (M = 128, K = N = 1024)"}
+    # decode shapes and the prefill shapes
+    dec = extras.get("decode", {}).get("shapes", {})
+    pre = extras.get("prefill", {}).get("gemm_ms", {})
+    for n in ("q", "k", "gate", "down"):
+        h = host[n]
+        K, N = h["K"], h["N"]
+        idx, ax, _ = O.select_channels(h["X_warm"], K_PROT)
+        aw = O.compute_alpha(h["W"], idx)
+        t0 = time.perf_counter()
+        wq, ws, wS = O.quantize_nvfp4(h["W"], idx, aw)
+        t_wq = time.perf_counter() - t0
+        Xd = synth.activations(synth.CFG_DECODE, synth.INPUT_STREAM[n], max(DECODE_MS), K, 3, "student")
+        for M in DECODE_MS:
+            xq, xs, xS = O.quantize_nvfp4(Xd[:M], idx, ax)
+            t0 = time.perf_counter()
+            O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
+            t = time.perf_counter() - t0
+            g = dec.get(f"{n}@M{M}", {}).get("us")
+            out[f"{n}@M{M}"] = {"oracle_ms": round(t * 1e3, 3), "gpu_us": g}
+        rows = M_PREFILL if n in ("q", "o") else 256
+        xq, xs, xS = O.quantize_nvfp4(h["X"][:rows], idx, ax)
+        t0 = time.perf_counter()
+        O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
+        t = (time.perf_counter() - t0) * M_PREFILL / rows
+        out[f"{n}@M{M_PREFILL}"] = {"oracle_s": round(t, 3), "gpu_ms": pre.get(n),
+                                    "extrapolated": rows != M_PREFILL, "oracle_rows": rows,
+                                    "oracle_weight_quantize_s": round(t_wq, 3)}
+        log(f"oracle {n}: {out[f'{n}@M{M_PREFILL}']}")
+    out["what"] = ("oracle: the fp64 product on its own packs (OpenMP over output rows; one row uses one "
+                   "thread); gpu: the same call's time from the decode and prefill measurements above")
+    return out
+
+
 def cpu_baseline(args, host, names, flops_per_row):
     """The fp64 oracle on the host cores: the same step as the GPU's
     (statistics, selection and activation preparation once per distinct layer
@@ -712,7 +933,8 @@ def cpu_baseline(args, host, names, flops_per_row):
     dt = time.perf_counter() - t0
     v = flops_per_row * rows / dt / 1e12
     log(f"cpu oracle {dt:.1f}s for {rows} rows")
-    return {"value": v, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+    return {"value": v, "unit": "TFLOP/s", "cores": O.num_threads(), "nproc": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"the whole step for all 7 projections on {rows} of {M_PREFILL} token rows "
                       f"(full warm-up statistics, full weight quantization), {dt:.1f} s"}
 
@@ -780,20 +1002,57 @@ def summarize(trace_db, fetch_db, write_db):
     """Writes the kernel-time summary of a bench run and the HBM traffic of
     the prefill SpliceGEMM (FETCH_SIZE and WRITE_SIZE in KiB per dispatch,
     each scaled by the reading of the same counter for the calibration copy
-    of known size)."""
-    rows = _db_rows(trace_db, "select name, count(*), avg(duration), sum(duration), "
-                              "min(duration), max(duration) from kernels group by name "
-                              "order by sum(duration) desc")
+    of known size).  The kernel times are listed per kernel and launch grid,
+    without the warm-up pass, and the prefill launches' durations give the
+    roofline figure of the step's dominant kernel."""
+    rows = _db_rows(trace_db, "select name, grid_x / workgroup_x, duration from kernels order by start")
+    by = {}
+    for name, wg, dur in rows:
+        by.setdefault((name, wg), []).append(dur)
+    passes = 4           # the profiled command: one warm-up step, three timed
     out = ["# Kernel times: bench step, Qwen3-8B layer prefill (M = 8192, k = 64)", "",
            "Command (repo root, MI355X):", "",
            "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run -- "
-           "python3 bench.py --steps 3 --warmup 1 --no-cpu --no-extra", "",
-           "Four passes of the step (one warm-up, three timed) over the seven projections, in four "
-           "GEMM launches (q|k|v and gate|up each one splice_gemm_multi launch).", "",
-           "| kernel | calls | avg us | total ms | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
-    for name, n, avg, tot, mn, mx in rows:
-        out.append(f"| `{name[:90]}` | {n} | {avg / 1e3:.2f} | {tot / 1e6:.3f} | {mn / 1e3:.2f} | "
-                   f"{mx / 1e3:.2f} |")
+           "python3 bench.py --steps 3 --warmup 1 --no-cpu --no-extra --no-forward", "",
+           "Four passes of the step, one warm-up and three timed, over the seven projections in four "
+           "GEMM launches (q|k|v and gate|up each one splice_gemm_multi launch). One row per kernel and "
+           "launch grid; for kernels launched a multiple of four times the first quarter (the warm-up "
+           "pass) is left out.", "",
+           "| kernel | workgroups | calls | avg us | total ms | min us | max us |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    stats = []
+    for (name, wg), d in by.items():
+        if len(d) % passes == 0 and len(d) >= passes:
+            d = d[len(d) // passes:]
+        stats.append((sum(d), name, wg, d))
+    for tot, name, wg, d in sorted(stats, reverse=True):
+        out.append(f"| `{name[:90]}` | {wg} | {len(d)} | {np.mean(d) / 1e3:.2f} | {tot / 1e6:.3f} | "
+                   f"{min(d) / 1e3:.2f} | {max(d) / 1e3:.2f} |")
+    # the step's GEMM launches: prefill SpliceGEMM kernels, per launch grid
+    from fp4_gemm_sparse_amd.synth import QWEN3_8B
+    grid_flops, grid_launches = {}, {}
+    for launch in LAUNCHES:
+        K = QWEN3_8B[launch[0]][0]
+        Nt = sum(QWEN3_8B[n][1] for n in launch)
+        grid = sum(-(-QWEN3_8B[n][1] // 256) for n in launch) * (M_PREFILL // 256)
+        grid_flops[grid] = grid_flops.get(grid, 0.0) + 2.0 * M_PREFILL * Nt * K
+        grid_launches[grid] = grid_launches.get(grid, 0) + 1
+    gemm = {wg: np.mean(d) for _, name, wg, d in stats if "prefill" in name and wg in grid_flops}
+    if set(gemm) == set(grid_flops):
+        # o and down share a grid (512 workgroups): their average counts twice
+        t = sum(m * grid_launches[wg] for wg, m in gemm.items()) * 1e-9
+        fl = sum(grid_flops.values())
+        ach = fl / t / 1e12
+        out += ["", "Step GEMM launches (prefill SpliceGEMM kernels per launch grid; 512 workgroups: "
+                "o and down, averaged together):", ""]
+        for wg in sorted(gemm):
+            out.append(f"- {wg} workgroups: {gemm[wg] / 1e3:.2f} us per launch, {grid_launches[wg]} "
+                       f"launch(es) per step")
+        out.append(f"- GEMM time of one step (per-launch averages): {t * 1e3:.4f} ms for "
+                   f"{fl / 1e12:.4f} TFLOP")
+        out.append(f"- achieved: {ach:.1f} TFLOP/s = {ach / MFMA_F16_PEAK_TFLOPS:.4f} of "
+                   f"{MFMA_F16_PEAK_TFLOPS:.0f} (the bench line's roofline.achieved times the same "
+                   f"launches with HIP events)")
     path = os.path.join(ROOT, "profiles", "bench_step_kernels_qwen3_8b_prefill.md")
     open(path, "w").write("\n".join(out) + "\n")
     print("wrote", path)
