@@ -664,34 +664,7 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     out["m_sweep"] = m_sweep_measurements(torch, S, P, dev, stream)
 
     # ---------------- grouped MoE stand-in
-    counts = synth.moe_counts()
-    K, N = 4096, 2048
-    groups = []
-    for e, Me in enumerate(counts):
-        Me = int(Me)
-        Xw = torch.from_numpy(synth.activations(synth.CFG_MOE, 100 + e, 512, K, 2, "student").view(np.int16)).to(dev)
-        X = torch.from_numpy(synth.activations(synth.CFG_MOE, 100 + e, max(Me, 1), K, 3, "student").view(np.int16)).to(dev)[:Me]
-        W = torch.from_numpy(synth.weights(synth.CFG_MOE, 200 + e, N, K).view(np.int16)).to(dev)
-        idx, ax, _ = S.select_channels(Xw, K_PROT)
-        aw = S.compute_alpha(W, idx)
-        xq = S.quantize_nvfp4(X, idx, ax) if Me else (torch.zeros(0, K // 2, dtype=torch.uint8, device=dev),
-                                                     torch.zeros(0, K // 16, dtype=torch.uint8, device=dev),
-                                                     torch.zeros(0, K_PROT, dtype=torch.int16, device=dev))
-        wq = S.quantize_nvfp4(W, idx, aw)
-        groups.append(dict(Xq=xq[0], Xs=xq[1], alpha_x=ax, X_S=xq[2], Wq=wq[0], Ws=wq[1], alpha_w=aw, W_S=wq[2],
-                           Y=torch.empty(Me, N, dtype=torch.float32, device=dev)))
-    # copies of every expert's weight packs, walked in turn (over 512 MiB in all)
-    wbytes = len(counts) * (N * K * (0.5 + 1 / 16) + 2 * N * K_PROT)
-    nset = copies_for(wbytes)
-    sets = [groups] + [[dict(g, Wq=g["Wq"].clone(), Ws=g["Ws"].clone(), W_S=g["W_S"].clone()) for g in groups]
-                       for _ in range(nset - 1)]
-    tg = graph_timed(torch, lambda i: S.splice_gemm_grouped(sets[i % nset], N, K, K_PROT), 3 * nset)
-    fl = 2.0 * int(counts.sum()) * N * K
-    out["moe_grouped"] = {"experts": len(counts), "tokens": int(counts.sum()), "max_tokens": int(counts.max()),
-                          "ms": round(tg, 4), "TFLOPs": round(fl / (tg * 1e-3) / 1e12, 2),
-                          "weight_GBps": round(wbytes / (tg * 1e-3) / 1e9, 1),
-                          "weight_copies": nset}
-    del sets
+    out["moe_grouped"] = moe_measurement(torch, S, synth, dev)
     log("moe", out["moe_grouped"])
 
     # ---------------- protected-channel sweep: error vs the BF16 product, time per k
@@ -741,6 +714,45 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
 
 
 M_SWEEP = (65, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def moe_measurement(torch, S, synth, dev):
+    """The grouped MoE stand-in: 32 Zipf-sized experts (N = 2048, K = 4096),
+    weight packs rotated over copies, both launch forms."""
+    out = {}
+    counts = synth.moe_counts()
+    K, N = 4096, 2048
+    groups = []
+    for e, Me in enumerate(counts):
+        Me = int(Me)
+        Xw = torch.from_numpy(synth.activations(synth.CFG_MOE, 100 + e, 512, K, 2, "student").view(np.int16)).to(dev)
+        X = torch.from_numpy(synth.activations(synth.CFG_MOE, 100 + e, max(Me, 1), K, 3, "student").view(np.int16)).to(dev)[:Me]
+        W = torch.from_numpy(synth.weights(synth.CFG_MOE, 200 + e, N, K).view(np.int16)).to(dev)
+        idx, ax, _ = S.select_channels(Xw, K_PROT)
+        aw = S.compute_alpha(W, idx)
+        xq = S.quantize_nvfp4(X, idx, ax) if Me else (torch.zeros(0, K // 2, dtype=torch.uint8, device=dev),
+                                                     torch.zeros(0, K // 16, dtype=torch.uint8, device=dev),
+                                                     torch.zeros(0, K_PROT, dtype=torch.int16, device=dev))
+        wq = S.quantize_nvfp4(W, idx, aw)
+        groups.append(dict(Xq=xq[0], Xs=xq[1], alpha_x=ax, X_S=xq[2], Wq=wq[0], Ws=wq[1], alpha_w=aw, W_S=wq[2],
+                           Y=torch.empty(Me, N, dtype=torch.float32, device=dev)))
+    # copies of every expert's weight packs, walked in turn (over 512 MiB in all)
+    wbytes = len(counts) * (N * K * (0.5 + 1 / 16) + 2 * N * K_PROT)
+    nset = copies_for(wbytes)
+    sets = [groups] + [[dict(g, Wq=g["Wq"].clone(), Ws=g["Ws"].clone(), W_S=g["W_S"].clone()) for g in groups]
+                       for _ in range(nset - 1)]
+    tg = graph_timed(torch, lambda i: S.splice_gemm_grouped(sets[i % nset], N, K, K_PROT), 3 * nset)
+    fl = 2.0 * int(counts.sum()) * N * K
+    # 128 x 128 tiles of the launch, and the flops they issue over the useful ones
+    tiles = int(sum(-(-int(c) // 128) for c in counts)) * (N // 128)
+    out["moe_grouped"] = {"experts": len(counts), "tokens": int(counts.sum()), "max_tokens": int(counts.max()),
+                          "ms": round(tg, 4), "TFLOPs": round(fl / (tg * 1e-3) / 1e12, 2),
+                          "frac_peak": round(fl / (tg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                          "weight_GBps": round(wbytes / (tg * 1e-3) / 1e9, 1),
+                          "tiles_128": tiles, "padded_flop_ratio": round(tiles * 128 * 128 / (int(counts.sum()) * N), 3),
+                          "weight_copies": nset}
+    del sets
+    return out["moe_grouped"]
 
 
 def m_sweep_measurements(torch, S, P, dev, stream):

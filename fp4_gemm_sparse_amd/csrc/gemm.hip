@@ -251,6 +251,42 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     // thread counts the workgroup in.  The workgroup that completes the count
     // reads every split's partial with device-coherent loads, sums them in
     // split order and finishes the tile; it returns the count to zero.
+    // Side operands of the epilogue (k a multiple of 16): staged through the
+    // idle LDS stage buffers, 64 channels per buffer, in the tile's swizzled
+    // 128-byte-row layout.  Thread (r0, cc) moves chunk cc of rows r0 + RS*u;
+    // rows past M or N are clamped and channels past k re-read the last ones
+    // (neither reaches a stored output).
+    const int k = TAIL ? a.k : 0;
+    const bool staged = TAIL && k > 0 && k % 16 == 0;
+    const int kn0 = staged ? min(2 * C::BKL, k) : 0;      // channels of the first pass
+    constexpr int RS = NT / 8, PU = C::ROWS * 8 / NT;
+    auto stage_load = [&](int kp, int ch, u32x4 (&v)[PU]) {
+        const int r0 = tid >> 3, cc = tid & 7;
+        const uint16_t *xp = a.X_S + cc * 8, *wp = a.W_S + cc * 8;
+        const int c = min(kp + ch * C::BKL + cc * 8, k - 8) - cc * 8;
+#pragma unroll
+        for (int u = 0; u < PU; u++) {
+            const int row = r0 + RS * u;
+            v[u] = row < C::BM ? *reinterpret_cast<const u32x4 *>(xp + min(m0 + row, M - 1) * k + c)
+                               : *reinterpret_cast<const u32x4 *>(wp + min(n0 + row - C::BM, N - 1) * k + c);
+        }
+    };
+    auto stage_store = [&](int ch, const u32x4 (&v)[PU]) {
+        const int r0 = tid >> 3, cc = tid & 7;
+#pragma unroll
+        for (int u = 0; u < PU; u++)
+            *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + RS * u, cc)) = v[u];
+    };
+    auto stage = [&](int kp, int kn) {              // all loads of a buffer before its stores
+        for (int ch = 0; ch * C::BKL < kn; ch++) {
+            u32x4 v[PU];
+            stage_load(kp, ch, v);
+            stage_store(ch, v);
+        }
+        lds_barrier();
+    };
+    bool first_staged = false;
+
     if (SPLIT && sk.nsplit > 1) {
         __shared__ int last_flag;
         constexpr int NWV = NT / WAVE;
@@ -279,6 +315,11 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         }
         __syncthreads();
         if (!last_flag) return;
+        // the first 64 side channels are loaded before the partial tiles, so
+        // their latency passes while the partials arrive (loads complete in
+        // issue order: the partials' waits cover them)
+        u32x4 pre[PU];
+        if (staged) stage_load(0, 0, pre);
         // one split at a time: every load of the split is issued before any
         // is used (the compiler keeps device-coherent loads in program order,
         // so loads interleaved with the sums would each wait for the last)
@@ -302,19 +343,25 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
                         acc[i][j][2 * q + 1] = sp == 0 ? t.y : acc[i][j][2 * q + 1] + t.y;
                     }
         }
+        if (staged) {
+            stage_store(0, pre);
+            if (kn0 > C::BKL) {
+                u32x4 v[PU];
+                stage_load(0, 1, v);
+                stage_store(1, v);
+            }
+            lds_barrier();
+            first_staged = true;
+        }
     }
 
     // ---- epilogue: Y = alpha_x*alpha_w * acc + X_S W_S^T
-    // The side operands (k a multiple of 16) go through the idle LDS stage
-    // buffers in passes of up to 128 channels, 64 per buffer, in the same
-    // swizzled 128-byte-row layout; all loads of a buffer are issued before its
-    // stores (rows past M or N clamped, channels past k re-reading the last
-    // ones: neither reaches a stored output).  Per 32-row fragment the side
-    // product goes into a small separate accumulator and the first pass stores
-    // Y = fma(alpha, acc, side), so the FP4 accumulator is only read; further
-    // passes (k > 128) add their side products into Y.
+    // The side operands (k a multiple of 16) go through the LDS stage buffers
+    // (stage above) in passes of up to 128 channels.  Per 32-row fragment the
+    // side product goes into a small separate accumulator and the first pass
+    // stores Y = fma(alpha, acc, side), so the FP4 accumulator is only read;
+    // further passes (k > 128) add their side products into Y.
     const float alpha = (*a.alpha_x) * (*a.alpha_w);
-    const int k = TAIL ? a.k : 0;
     const int64_t mb = m0 + wm * C::WM + g * 4, nb = n0 + wn * C::WN + rr;
     float *yb = a.Y + mb * a.ldy + nb;
     const bool full = m0 + C::BM <= M && n0 + C::BN <= N;
@@ -338,26 +385,6 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
             }
         }
     };
-    const bool staged = TAIL && k > 0 && k % 16 == 0;
-    auto stage = [&](int kp, int kn) {
-        constexpr int RS = NT / 8, PU = C::ROWS * 8 / NT;   // rows r0 + RS*u, chunk cc
-        const int r0 = tid >> 3, cc = tid & 7;
-        const uint16_t *xp = a.X_S + cc * 8, *wp = a.W_S + cc * 8;
-        for (int ch = 0; ch * C::BKL < kn; ch++) {
-            const int c = min(kp + ch * C::BKL + cc * 8, k - 8) - cc * 8;
-            u32x4 v[PU];
-#pragma unroll
-            for (int u = 0; u < PU; u++) {
-                const int row = r0 + RS * u;
-                v[u] = row < C::BM ? *reinterpret_cast<const u32x4 *>(xp + min(m0 + row, M - 1) * k + c)
-                                   : *reinterpret_cast<const u32x4 *>(wp + min(n0 + row - C::BM, N - 1) * k + c);
-            }
-#pragma unroll
-            for (int u = 0; u < PU; u++)
-                *reinterpret_cast<u32x4 *>(lds + ch * C::TILE + f16_off(r0 + RS * u, cc)) = v[u];
-        }
-        lds_barrier();
-    };
     auto side_staged = [&](int i, int kn, f32x16 (&side)[C::FN]) {
         for (int s = 0; s < kn / 16; s++) {
             const uint8_t *tile = lds + (s >> 2) * C::TILE;
@@ -370,8 +397,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
             }
         }
     };
-    const int kn0 = staged ? min(2 * C::BKL, k) : 0;
-    if (staged) stage(0, kn0);
+    if (staged && !first_staged) stage(0, kn0);
 #pragma unroll
     for (int i = 0; i < C::FM; i++) {
         f32x16 side[C::FN];
@@ -433,11 +459,12 @@ __global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
 // workgroup): three measured 5-9% faster than one at M = 65..1024
 constexpr int PF128 = 3;
 
-// 128 x 128 tiles, four waves of 64 x 64 (two workgroups per CU): for grids
+// 128 x 128 tiles, four waves of 64 x 64 (two workgroups per CU, so at most
+// 256 registers per lane: the launch bound says so): for grids
 // too small for the 256 x 256 tile; where even these tiles leave CUs idle,
 // the K range is split nsplit ways (cnt and part in the workspace)
 template <bool TAIL>
-__global__ __launch_bounds__(256) void prefill_lds128_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
+__global__ __launch_bounds__(256, 2) void prefill_lds128_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tiles_m = (int)((a.M + 127) / 128), tiles_n = (int)((a.N + 127) / 128);
@@ -454,7 +481,7 @@ __global__ __launch_bounds__(256) void prefill_lds128_kernel(GemmArgs a, int nsp
 
 // the same tiles over column segments: tile columns numbered across them
 template <int BT, int WGN, bool TAIL>
-__global__ __launch_bounds__(64 * 2 * WGN) void prefill_seg_kernel(SegTable t, int nsplit, unsigned *cnt,
+__global__ __launch_bounds__(64 * 2 * WGN, BT == 128 ? 2 : 1) void prefill_seg_kernel(SegTable t, int nsplit, unsigned *cnt,
                                                                    float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -500,7 +527,7 @@ struct GroupedArgs {
 };
 
 template <int BM, int BN, bool TAIL>
-__global__ __launch_bounds__(256) void grouped_prefill_kernel(GroupedArgs ga)
+__global__ __launch_bounds__(256, 2) void grouped_prefill_kernel(GroupedArgs ga)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int w = blockIdx.x;
