@@ -542,11 +542,14 @@ __global__ __launch_bounds__(256, 2) void grouped_prefill_kernel(GroupedArgs ga)
 
 // ---------------------------------------------------------------------------
 // Prefill plan: the 256 x 256 tile when its grid fills the GPU, else the
-// 128 x 128 tile.  Below 128 tiles the K range is also split, as many ways as
-// keep the workgroups within 256 and each split at least eight 64-channel
-// steps: at M = 65..1024 on the Qwen3-8B shapes that count was the fastest
-// measured or within 1 us of it (q at M = 128: 52 us unsplit, 27 us in eight
-// splits; down: 148 -> 40 us).  The partial tiles take at most 256 x 64 KB.
+// 128 x 128 tile.  At up to 128 tiles the K range is also split, as many ways
+// as keep the workgroups within 256 (one per CU) and each split at least eight
+// 64-channel steps: at M = 65..1024 on the Qwen3-8B shapes that count was the
+// fastest measured or within 1 us of it (q at M = 128: 52 us unsplit, 27 us in
+// eight splits; q at M = 512, 128 tiles: 51.5 -> 37.4 us in two; down at
+// M = 256: 145 -> 52 us in four).  More workgroups than CUs measured slower
+// (gate at M = 65, 96 tiles: 37 us in two splits, 48 us in three; 192 tiles
+// unsplit 55 us, in two 68 us).  The partial tiles take at most 256 x 64 KB.
 struct PrefillPlan {
     bool big;
     int nsplit;
@@ -578,7 +581,7 @@ static PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, int64_t tiles_n
     }
     p.tiles = ((M + 127) / 128) * tiles_n128;
     const int64_t nk = K / LdsCfg::BKL;
-    if (p.tiles < SPLIT_MAX_TILES && p.tiles > 0) {
+    if (p.tiles <= SPLIT_MAX_TILES && p.tiles > 0) {
         int64_t sp = std::min<int64_t>(SPLIT_WORKGROUPS / p.tiles, nk / SPLIT_MIN_STEPS);
         if (sp > 1) {
             const int64_t per = (nk + sp - 1) / sp;

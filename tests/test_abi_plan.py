@@ -19,17 +19,27 @@ def test_decode_and_prefill_paths():
 @pytest.mark.parametrize("M", [65, 128, 256, 512])
 @pytest.mark.parametrize("N", [1024, 4096])
 def test_small_grids_split_k(M, N):
-    """Below 128 tiles of 128 x 128 the K sum is split as many ways as keep
+    """At up to 128 tiles of 128 x 128 the K sum is split as many ways as keep
     the workgroups within 256 and each split at least eight 64-channel steps;
     the workspace holds one partial tile per split."""
     K = 4096
     path, kern, rows, cols, ns = S.gemm_plan(M, N, K)
     tiles = -(-M // 128) * -(-N // 128)
     assert (path, rows, cols) == (2, 128, 128)
-    assert ns == (max(1, min(256 // tiles, K // 64 // 8)) if tiles < 128 else 1)
+    assert ns == (max(1, min(256 // tiles, K // 64 // 8)) if tiles <= 128 else 1)
     assert tiles * ns <= 256
     if ns > 1:
         assert S.workspace_size(M, N, K) >= tiles * ns * 128 * 128 * 4
+
+
+def test_mid_range_plans():
+    """q, k and down at 512 rows split (128, 32 and 128 tiles); gate at 256
+    rows (192 tiles) and q at 2048 rows (512 tiles) fill the GPU unsplit."""
+    assert S.gemm_plan(512, 4096, 4096)[4] == 2
+    assert S.gemm_plan(512, 1024, 4096)[4] == 8
+    assert S.gemm_plan(512, 4096, 12288)[4] == 2
+    assert S.gemm_plan(256, 12288, 4096)[4] == 1
+    assert S.gemm_plan(2048, 4096, 4096)[1:] == (0, 128, 128, 1)
 
 
 def test_split_ranges_are_never_empty():

@@ -35,15 +35,18 @@ def gpu_packs(X_warm, X, W, k):
     return idx, ax, aw, S.quantize_nvfp4(dev(X), idx, ax), S.quantize_nvfp4(Wd, idx, aw)
 
 
-@pytest.mark.parametrize("M", [65, 128, 256])
+@pytest.mark.parametrize("M", [65, 128, 256, 512, 2048])
 @pytest.mark.parametrize("name", ["q", "k", "down"])
 def test_split_prefill_full_size_sampled(name, M):
-    """Qwen3-8B projections at M rows (prefill workload distributions): the
-    plan splits K, and 160 sampled output columns meet the oracle's own
+    """Qwen3-8B projections at M rows (prefill workload distributions) from
+    just above the decode path to 2048 rows: the plan splits K where the
+    grid has at most 128 tiles of 128 x 128 (every case here but q and down
+    at 2048 rows), and 160 sampled output columns meet the oracle's own
     calibration, packs and product."""
     p = synth.projection(synth.CFG_PREFILL, name, M)
     K, N = p["K"], p["N"]
-    assert S.gemm_plan(M, N, K)[4] > 1
+    tiles = -(-M // 128) * -(-N // 128)
+    assert (S.gemm_plan(M, N, K)[4] > 1) == (tiles <= 128)
     cols = np.sort(np.random.default_rng(M + N).choice(N, size=160, replace=False))
     idx_o, ax_o, _ = O.select_channels(p["X_warm"], 64)
     aw_o = O.compute_alpha(p["W"], idx_o)
