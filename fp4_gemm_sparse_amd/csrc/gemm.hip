@@ -205,6 +205,13 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     }
     __syncthreads();
     const int arow = wm * C::WM + rr, brow = C::BM + wn * C::WN + rr;
+    // The main loop for a wave whose first FMV 32-row fragments hold rows
+    // inside M: it reads and multiplies only those (the others would only feed
+    // outputs that are never stored).  FMV = FM everywhere but in the last
+    // tile row of a product whose M is not a multiple of the tile; each count
+    // is its own branch-free copy of the loop.
+    auto main_loop = [&](auto fmv) {
+    constexpr int FMV = decltype(fmv)::value;
     for (int kb = 0; kb < nk; kb += PF)
 #pragma unroll
     for (int u = 0; u < PF; u++) {
@@ -215,14 +222,14 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         uint8_t *nxt = lds + ((kt + 1) & 1) * C::TILE;
         f16x8 a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
 #pragma unroll
-        for (int i = 0; i < C::FM; i++) a0[i] = *reinterpret_cast<const f16x8 *>(cur + f16_off(arow + i * 32, g));
+        for (int i = 0; i < FMV; i++) a0[i] = *reinterpret_cast<const f16x8 *>(cur + f16_off(arow + i * 32, g));
 #pragma unroll
         for (int j = 0; j < C::FN; j++) b0[j] = *reinterpret_cast<const f16x8 *>(cur + f16_off(brow + j * 32, g));
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             if (s < 3) {
 #pragma unroll
-                for (int i = 0; i < C::FM; i++)
+                for (int i = 0; i < FMV; i++)
                     a1[i] = *reinterpret_cast<const f16x8 *>(cur + f16_off(arow + i * 32, (s + 1) * 2 + g));
 #pragma unroll
                 for (int j = 0; j < C::FN; j++)
@@ -232,10 +239,10 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
 #pragma unroll
             for (int j = 0; j < C::FN; j++)
 #pragma unroll
-                for (int i = 0; i < C::FM; i++) acc[i][j] = mfma32_f16(a0[i], b0[j], acc[i][j]);
+                for (int i = 0; i < FMV; i++) acc[i][j] = mfma32_f16(a0[i], b0[j], acc[i][j]);
             if (s < 3) {
 #pragma unroll
-                for (int i = 0; i < C::FM; i++) a0[i] = a1[i];
+                for (int i = 0; i < FMV; i++) a0[i] = a1[i];
 #pragma unroll
                 for (int j = 0; j < C::FN; j++) b0[j] = b1[j];
             }
@@ -243,6 +250,22 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         }
         gload(rs, kt0 + min(kt + 1 + PF, nk - 1));
         lds_barrier();      // the prefetches of steps kt+2 .. kt+1+PF stay in flight
+    }
+    };
+    // valid fragment rows of this wave (wave-uniform)
+    const int fm_ok = (int)min<int64_t>(C::FM, max<int64_t>(0, (M - (m0 + wm * C::WM) + 31) / 32));
+    static_assert(C::FM == 2 || C::FM == 4, "fragment rows per wave");
+    if (fm_ok >= C::FM)
+        main_loop(std::integral_constant<int, C::FM>{});
+    else if (fm_ok == 0)
+        main_loop(std::integral_constant<int, 0>{});
+    else if (fm_ok == 1)
+        main_loop(std::integral_constant<int, 1>{});
+    else if constexpr (C::FM == 4) {
+        if (fm_ok == 2)
+            main_loop(std::integral_constant<int, 2>{});
+        else
+            main_loop(std::integral_constant<int, 3>{});
     }
 
     // ---- K split over workgroups: the partial tile goes to the workspace with
