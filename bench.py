@@ -65,6 +65,8 @@ def parse():
                          "(the run that rocprofv3 --pmc passes profile)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DB", "FETCH_DB", "WRITE_DB"),
                     help="write the profiles/ summaries from rocprofv3 result databases")
+    ap.add_argument("--traced-line", metavar="LOG",
+                    help="with --summarize: the traced command's output, whose bench line the summary quotes")
     ap.add_argument("--summarize-extras", metavar="TRACE_DB",
                     help="write the profiles/ kernel-time summary of a full run (all extras)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DB",
@@ -88,7 +90,7 @@ def kernel_source_hash():
 def main():
     args = parse()
     if args.summarize:
-        summarize(*args.summarize)
+        summarize(*args.summarize, traced_line=args.traced_line)
         return
     if args.summarize_extras:
         summarize_extras(args.summarize_extras)
@@ -1010,7 +1012,7 @@ def _db_rows(db, sql):
         con.close()
 
 
-def summarize(trace_db, fetch_db, write_db):
+def summarize(trace_db, fetch_db, write_db, traced_line=None):
     """Writes the kernel-time summary of a bench run and the HBM traffic of
     the prefill SpliceGEMM (FETCH_SIZE and WRITE_SIZE in KiB per dispatch,
     each scaled by the reading of the same counter for the calibration copy
@@ -1021,21 +1023,26 @@ def summarize(trace_db, fetch_db, write_db):
     by = {}
     for name, wg, dur in rows:
         by.setdefault((name, wg), []).append(dur)
-    passes = 4           # the profiled command: one warm-up step, three timed
+    # the profiled command: PROFILE_WARMUP warm-up steps (the clocks settle over
+    # the first few), then PROFILE_STEPS timed ones
+    passes = PROFILE_WARMUP + PROFILE_STEPS
     out = ["# Kernel times: bench step, Qwen3-8B layer prefill (M = 8192, k = 64)", "",
            "Command (repo root, MI355X):", "",
            "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o run -- "
-           "python3 bench.py --steps 3 --warmup 1 --no-cpu --no-extra --no-forward", "",
-           "Four passes of the step, one warm-up and three timed, over the seven projections in four "
-           "GEMM launches (q|k|v and gate|up each one splice_gemm_multi launch). One row per kernel and "
-           "launch grid; for kernels launched a multiple of four times the first quarter (the warm-up "
-           "pass) is left out.", "",
+           f"python3 bench.py --steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} --no-cpu --no-extra --no-forward "
+           "> gpurun_out/prof.log",
+           "    python3 bench.py --summarize gpurun_out/prof/run_results.db gpurun_out/pmc_fetch/run_results.db "
+           "gpurun_out/pmc_write/run_results.db --traced-line gpurun_out/prof.log", "",
+           f"{passes} passes of the step, {PROFILE_WARMUP} warm-up and {PROFILE_STEPS} timed, over the seven "
+           "projections in four GEMM launches (q|k|v and gate|up each one splice_gemm_multi launch). One row "
+           f"per kernel and launch grid; for kernels launched a multiple of {passes} times, the calls of the "
+           "warm-up passes are left out.", "",
            "| kernel | workgroups | calls | avg us | total ms | min us | max us |",
            "|---|---:|---:|---:|---:|---:|---:|"]
     stats = []
     for (name, wg), d in by.items():
         if len(d) % passes == 0 and len(d) >= passes:
-            d = d[len(d) // passes:]
+            d = d[len(d) // passes * PROFILE_WARMUP:]
         stats.append((sum(d), name, wg, d))
     for tot, name, wg, d in sorted(stats, reverse=True):
         out.append(f"| `{name[:90]}` | {wg} | {len(d)} | {np.mean(d) / 1e3:.2f} | {tot / 1e6:.3f} | "
@@ -1065,6 +1072,12 @@ def summarize(trace_db, fetch_db, write_db):
         out.append(f"- achieved: {ach:.1f} TFLOP/s = {ach / MFMA_F16_PEAK_TFLOPS:.4f} of "
                    f"{MFMA_F16_PEAK_TFLOPS:.0f} (the bench line's roofline.achieved times the same "
                    f"launches with HIP events)")
+        if traced_line:
+            line = [l for l in open(traced_line).read().splitlines() if l.startswith("{")][-1]
+            r = json.loads(line)["roofline"]
+            out.append(f"- the traced command's own bench line: roofline.achieved {r['achieved']} TFLOP/s "
+                       f"(frac {r['frac']}); this summary differs from it by "
+                       f"{100 * (ach / r['achieved'] - 1):+.1f}%")
     path = os.path.join(ROOT, "profiles", "bench_step_kernels_qwen3_8b_prefill.md")
     open(path, "w").write("\n".join(out) + "\n")
     print("wrote", path)
@@ -1123,6 +1136,7 @@ def summarize(trace_db, fetch_db, write_db):
 
 
 COUNTER_FILE = os.path.join(ROOT, "profiles", "prefill_splice_gemm_counters_qwen3_8b.md")
+PROFILE_STEPS, PROFILE_WARMUP = 3, 5
 COUNTER_PASSES = (
     "SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
     "SQ_INSTS_VALU SQ_INSTS_LDS SQ_WAVES GRBM_GUI_ACTIVE",
