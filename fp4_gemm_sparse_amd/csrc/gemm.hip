@@ -1370,7 +1370,7 @@ size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int n
 //    over 8 waves;
 //  - M in 33..64: streaming, 48 columns per workgroup for wide N.
 enum class Kern { P256, P128, XL8_4, XL16_4, XL16_6, XL16_8, D2_1_3, D3_1_1, D2_1_1, D3_2_3_W4, D3_2_3_W8,
-                  D2_2_1, D2_4_3, D2_4_1 };
+                  D2_2_1, D2_4_3, D2_4_1, D2_2_3 };
 
 struct GemmPlan {
     Path path;
@@ -1410,8 +1410,13 @@ static GemmPlan plan_gemm(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg
     } else if (M <= 32) {
         g.rows = 32;
         g.cols = 16;
-        if (colblocks >= 512 && nchunk <= 8 * 4) {
-            g.kern = nchunk <= 4 * 4 ? Kern::D3_2_3_W4 : Kern::D3_2_3_W8;
+        if (colblocks >= 512 && nchunk <= 4 * 4) {
+            g.kern = Kern::D3_2_3_W4;
+            g.cols = 48;
+        } else if (colblocks >= 512 && nchunk <= 8 * 4) {
+            // streaming beat the single round here: gate at M = 32, K = 4096,
+            // 15.2 against 16.4 us
+            g.kern = Kern::D2_2_3;
             g.cols = 48;
         } else {
             g.kern = Kern::D2_2_1;
@@ -1443,6 +1448,7 @@ static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, vo
     case Kern::D3_2_3_W4: return run_decode3<2, 3, 4, 4>(a, sp, s);
     case Kern::D3_2_3_W8: return run_decode3<2, 3, 8, 4>(a, sp, s);
     case Kern::D2_2_1: return run_decode2<2, 1, 8, 1>(a, sp, s);
+    case Kern::D2_2_3: return run_decode2<2, 3, 8, 1>(a, sp, s);
     case Kern::D2_4_3: return run_decode2<4, 3, 8, 1>(a, sp, s);
     case Kern::D2_4_1: return run_decode2<4, 1, 8, 2>(a, sp, s);
     }
