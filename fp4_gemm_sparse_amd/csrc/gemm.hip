@@ -1369,7 +1369,7 @@ size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int n
 //    per workgroup (one workgroup per CU at N = 12288); otherwise streaming
 //    over 8 waves;
 //  - M in 33..64: streaming, 48 columns per workgroup for wide N.
-enum class Kern { P256, P128, XL8_4, XL16_4, XL16_6, XL16_8, D2_1_3, D3_1_1, D2_1_1, D3_2_3_W4, D3_2_3_W8,
+enum class Kern { P256, P128, XL8_4, XL16_4, XL16_6, XL16_8, D2_1_3, D3_1_1, D2_1_1, D3_2_3_W4,
                   D2_2_1, D2_4_3, D2_4_1, D2_2_3 };
 
 struct GemmPlan {
@@ -1446,7 +1446,6 @@ static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, vo
     case Kern::D3_1_1: return run_decode3<1, 1, 8, 4>(a, sp, s);
     case Kern::D2_1_1: return run_decode2<1, 1, 8, 1>(a, sp, s);
     case Kern::D3_2_3_W4: return run_decode3<2, 3, 4, 4>(a, sp, s);
-    case Kern::D3_2_3_W8: return run_decode3<2, 3, 8, 4>(a, sp, s);
     case Kern::D2_2_1: return run_decode2<2, 1, 8, 1>(a, sp, s);
     case Kern::D2_2_3: return run_decode2<2, 3, 8, 1>(a, sp, s);
     case Kern::D2_4_3: return run_decode2<4, 3, 8, 1>(a, sp, s);
