@@ -432,10 +432,12 @@ def test_prefill_full_size_every_row(name):
     Y = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
     assert np.array_equal(host(gx[0]), o["xq"]) and np.array_equal(host(gx[1]), o["xs"])
     assert np.array_equal(host(gw[0]), o["wq"]) and np.array_equal(host(gw[1]), o["ws"])
-    # 33.5 M outputs of 4096-term dot products: allow the scaled floor for at
-    # most 8 elements whose products cancel, and report how many needed it
+    # 33.5 M outputs of 4096-term dot products: the scaled floor for at most
+    # one element, where the FP4 and BF16 parts cancel to a result far below
+    # their fp32 resolution (the products are deterministic: q and o each have
+    # exactly one such element); report how many needed it
     n = assert_gemm_close(host(Y), o["Y"], f"prefill {name}, all rows",
-                          terms=lambda i, j: product_magnitudes(o, i, j), max_scaled=8)
+                          terms=lambda i, j: product_magnitudes(o, i, j), max_scaled=1)
     print(f"prefill {name}, all {M * p['N']} outputs: {n} beyond the literal 1e-6 floor")
 
 
