@@ -26,6 +26,7 @@ namespace splice {
 constexpr int BK = 128;              // channels per decode-path K chunk
 constexpr int CODE_ROW = BK / 2;     // 64 code bytes per row per chunk
 constexpr int SCALE_ROW = BK / 16;   // 8 scale bytes per row per chunk
+constexpr int DECODE_SPLIT_MAX = 8;  // K splits of a decode-path column group at most
 
 // ===========================================================================
 // Prefill path
@@ -731,8 +732,12 @@ struct DecodeCfg {
     static constexpr int RED_TILES = (T * NW <= 128) ? T : (128 / NW);   // tiles per LDS round
 };
 
-template <int MB, int CB, int NW, int BB, bool TAIL>
-__device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
+// SPLIT: the K chunks may be split over sk.nsplit workgroups, each summing a
+// contiguous range; the workgroup sums go to the workspace and the last of a
+// column group's workgroups to arrive adds them in split order and finishes
+// the tiles (the prefill path's fixup).
+template <int MB, int CB, int NW, int BB, bool TAIL, bool SPLIT = false>
+__device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk, const SplitK &sk = SplitK{})
 {
     using C = DecodeCfg<MB, CB, NW, BB>;
     __shared__ f32x4 red[NW][C::RED_TILES][WAVE];
@@ -742,6 +747,13 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
     const int64_t rowb = K / 2, rows = K / 16;
     const int64_t n0 = blk * (16 * CB);
     const int nchunk = (int)(K / BK);
+    const bool split = SPLIT && sk.nsplit > 1;
+    int c_lo = 0, c_hi = nchunk;
+    if (split) {
+        const int per = (nchunk + sk.nsplit - 1) / sk.nsplit;
+        c_lo = sk.split * per;
+        c_hi = min(nchunk, c_lo + per);
+    }
 
     const uint8_t *wrow[CB];
     const uint8_t *wsrow[CB];
@@ -773,7 +785,7 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
     auto load = [&](int c, u32x4 (*wc)[CB], unsigned (*ws)[CB], u32x4 (*xc)[MB], unsigned (*xs)[MB]) {
 #pragma unroll
         for (int b = 0; b < BB; b++) {
-            const int ci = min(c + b * NW, nchunk - 1);      // clamped; masked at use
+            const int ci = min(c + b * NW, c_hi - 1);        // clamped; masked at use
 #pragma unroll
             for (int j = 0; j < CB; j++) {
                 wc[b][j] = *reinterpret_cast<const u32x4 *>(wrow[j] + (int64_t)ci * CODE_ROW);
@@ -789,7 +801,7 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
     auto compute = [&](int c, u32x4 (*wc)[CB], unsigned (*ws)[CB], u32x4 (*xc)[MB], unsigned (*xs)[MB]) {
 #pragma unroll
         for (int b = 0; b < BB; b++) {
-            const bool ok = c + b * NW < nchunk;
+            const bool ok = c + b * NW < c_hi;
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 f16x8 af[MB];
@@ -808,8 +820,8 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
         }
     };
 
-    int c = wave;
-    if (c < nchunk) load(c, wc0, ws0, xc0, xs0);
+    int c = c_lo + wave;
+    if (c < c_hi) load(c, wc0, ws0, xc0, xs0);
     // W_S fragments (k = 32 or 64) of the tile this wave finishes, issued by
     // every wave alike right behind its first batch: the waits for later
     // batches, younger loads, include them, and by then they have arrived.
@@ -819,7 +831,14 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
     // round: two would hold 8 more registers than the widest form can spare.
     constexpr int TPW = (C::T + NW - 1) / NW;
     const int k = a.k;
-    const bool side_pre = TAIL && TPW == 1 && C::RED_TILES == C::T && (k == 32 || k == 64);
+    // With the K range split, every workgroup of a column group loads them,
+    // though only the last to arrive uses them (the splits run side by side
+    // on one XCD, so the later loads hit L2) -- where each wave finishes a
+    // tile of its own: with fewer tiles than waves, the duplicate loads of
+    // all splits cost more than the last workgroup's wait for W_S (k at
+    // M = 8: 7.1 against 6.7 us).
+    const bool side_pre = TAIL && TPW == 1 && C::RED_TILES == C::T && (k == 32 || k == 64) &&
+                          (!split || C::T == NW);
     bf16x8 tb[2];
     if (side_pre) {
         const int t = min(wave, C::T - 1);
@@ -831,19 +850,61 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
             tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
         }
     }
-    while (c < nchunk) {
+    while (c < c_hi) {
         const int c1 = c + BB * NW;
-        if (c1 < nchunk) load(c1, wc1, ws1, xc1, xs1);
+        if (c1 < c_hi) load(c1, wc1, ws1, xc1, xs1);
         compute(c, wc0, ws0, xc0, xs0);
-        if (c1 >= nchunk) break;
+        if (c1 >= c_hi) break;
         const int c2 = c1 + BB * NW;
-        if (c2 < nchunk) load(c2, wc0, ws0, xc0, xs0);
+        if (c2 < c_hi) load(c2, wc0, ws0, xc0, xs0);
         compute(c1, wc1, ws1, xc1, xs1);
         c = c2;
     }
 
     // ---- deterministic cross-wave sum through LDS, in rounds of RED_TILES tiles
     const float alpha = (*a.alpha_x) * (*a.alpha_w);
+    auto store_tile = [&](int t, const f32x4 &v) {
+        const int64_t n = n0 + (t % CB) * 16 + rr;
+        if (n < N)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int64_t m = (t / CB) * 16 + g * 4 + q;
+                if (m < M) a.Y[m * a.ldy + n] = v[q];
+            }
+    };
+    // tile t's sum v: scale, add the side product, store
+    auto finish = [&](int t, f32x4 v) {
+        const int i = t / CB, j = t % CB;
+        v *= alpha;
+        const int64_t n = n0 + j * 16 + rr;
+        const int64_t mrow = i * 16 + rr;
+        if (side_pre) {                // one round, one tile per wave: t == wave
+            const bf16x8 z = {};
+            const bool okm = mrow < M, okn = n < N;
+            const uint16_t *xa = a.X_S + (okm ? mrow : 0) * k + g * 8;
+            const bf16x8 ta0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa));
+            v = mfma_bf16(okm ? ta0 : z, okn ? tb[0] : z, v);
+            if (k == 64) {
+                const bf16x8 ta1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + 32));
+                v = mfma_bf16(okm ? ta1 : z, okn ? tb[1] : z, v);
+            }
+        } else if (TAIL) {
+            const bool al = (k % 8) == 0;
+            for (int kk = 0; kk < k; kk += 32) {
+                const int cc = kk + g * 8;
+                const int valid = max(0, min(8, k - cc));
+                bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
+                bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
+                v = mfma_bf16(af, bf, v);
+            }
+        }
+        store_tile(t, v);
+    };
+    // split: workgroup sums of tile t from split sp, lane-contiguous 16 bytes
+    auto slot = [&](int sp, int t, int h) {
+        return reinterpret_cast<uint64_t *>(sk.part) +
+               ((((int64_t)sk.wtile * sk.nsplit + sp) * C::T + t) * WAVE + lane) * 2 + h;
+    };
 #pragma unroll
     for (int t0 = 0; t0 < C::T; t0 += C::RED_TILES) {
         if (t0 > 0) __syncthreads();
@@ -852,39 +913,76 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk)
             if (t0 + t < C::T) red[wave][t][lane] = acc[(t0 + t) / CB][(t0 + t) % CB];
         __syncthreads();
         for (int t = wave; t < C::RED_TILES && t0 + t < C::T; t += NW) {
-            const int i = (t0 + t) / CB, j = (t0 + t) % CB;
             f32x4 v = red[0][t][lane];
 #pragma unroll
             for (int w = 1; w < NW; w++) v += red[w][t][lane];
-            v *= alpha;
-            const int64_t n = n0 + j * 16 + rr;
-            const int64_t mrow = i * 16 + rr;
-            if (side_pre) {                // one round, one tile per wave: t == wave
-                const bf16x8 z = {};
-                const bool okm = mrow < M, okn = n < N;
-                const uint16_t *xa = a.X_S + (okm ? mrow : 0) * k + g * 8;
-                const bf16x8 ta0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa));
-                v = mfma_bf16(okm ? ta0 : z, okn ? tb[0] : z, v);
-                if (k == 64) {
-                    const bf16x8 ta1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xa + 32));
-                    v = mfma_bf16(okm ? ta1 : z, okn ? tb[1] : z, v);
-                }
-            } else if (TAIL) {
-                const bool al = (k % 8) == 0;
-                for (int kk = 0; kk < k; kk += 32) {
-                    const int cc = kk + g * 8;
-                    const int valid = max(0, min(8, k - cc));
-                    bf16x8 af = load_bf16x8(a.X_S + mrow * k + cc, (mrow < M) ? valid : 0, al);
-                    bf16x8 bf = load_bf16x8(a.W_S + n * k + cc, (n < N) ? valid : 0, al);
-                    v = mfma_bf16(af, bf, v);
-                }
+            if (split) {
+                const f32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+                __hip_atomic_store(slot(sk.split, t0 + t, 0), __builtin_bit_cast(uint64_t, lo), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(slot(sk.split, t0 + t, 1), __builtin_bit_cast(uint64_t, hi), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                finish(t0 + t, v);
             }
-            if (n < N)
+        }
+    }
+    if (SPLIT && split) {
+        __shared__ int last_flag;
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(sk.cnt + sk.wtile, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = prev == (unsigned)(sk.nsplit - 1);
+            if (last) __hip_atomic_store(sk.cnt + sk.wtile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = last;
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        // the side fragments (k = 32 or 64: X_S here, W_S since the main
+        // loop where each wave finishes one tile), then every split's sums of
+        // a tile, are loaded before any is used (loads complete in issue
+        // order, so the side loads' latency passes while the sums arrive);
+        // the sum runs in split order
+        const bool pre = TAIL && (k == 32 || k == 64);
+        for (int t = wave; t < C::T; t += NW) {
+            bf16x8 sa[2] = {}, sb[2] = {};
+            const int64_t n = n0 + (t % CB) * 16 + rr, mrow = (t / CB) * 16 + rr;
+            if (pre) {
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int64_t m = i * 16 + g * 4 + q;
-                    if (m < M) a.Y[m * a.ldy + n] = v[q];
+                for (int h = 0; h < 2; h++)
+                    if (h * 32 < k) {
+                        if (mrow < M)
+                            sa[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(a.X_S + mrow * k + h * 32 + g * 8));
+                        if (n < N)
+                            sb[h] = side_pre ? tb[h]
+                                             : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(a.W_S + n * k + h * 32 + g * 8));
+                    }
+            }
+            uint64_t p[DECODE_SPLIT_MAX][2];
+#pragma unroll
+            for (int sp = 0; sp < DECODE_SPLIT_MAX; sp++)
+                if (sp < sk.nsplit)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+                        p[sp][h] = __hip_atomic_load(slot(sp, t, h), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            f32x4 v;
+#pragma unroll
+            for (int sp = 0; sp < DECODE_SPLIT_MAX; sp++)
+                if (sp < sk.nsplit) {
+                    const f32x2 lo = __builtin_bit_cast(f32x2, p[sp][0]), hi = __builtin_bit_cast(f32x2, p[sp][1]);
+                    const f32x4 u = {lo.x, lo.y, hi.x, hi.y};
+                    v = sp == 0 ? u : v + u;
                 }
+            if (pre) {
+                v *= alpha;
+                v = mfma_bf16(sa[0], sb[0], v);
+                if (k == 64) v = mfma_bf16(sa[1], sb[1], v);
+                store_tile(t, v);
+            } else {
+                finish(t, v);
+            }
         }
     }
 }
@@ -901,6 +999,60 @@ __global__ __launch_bounds__(64 * NW) void decode2_seg_kernel(SegTable t)
     int local;
     const GemmArgs a = seg_args(t, blockIdx.x, local);
     decode2_body<MB, CB, NW, BB, TAIL>(a, local);
+}
+
+// K split over workgroups: the splits of a column group are consecutive work
+// items, so they usually run on one XCD
+template <int MB, int CB, int NW, int BB, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode2s_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
+{
+    const int item = xcd_order(blockIdx.x, gridDim.x);
+    SplitK sk;
+    sk.nsplit = nsplit;
+    sk.wtile = item / nsplit;
+    sk.split = item - (int)sk.wtile * nsplit;
+    sk.cnt = cnt;
+    sk.part = part;
+    decode2_body<MB, CB, NW, BB, TAIL, true>(a, sk.wtile, sk);
+}
+
+template <int MB, int CB, int NW, int BB, bool TAIL>
+__global__ __launch_bounds__(64 * NW) void decode2s_seg_kernel(SegTable t, int nsplit, unsigned *cnt, float *part)
+{
+    const int item = xcd_order(blockIdx.x, gridDim.x);
+    SplitK sk;
+    sk.nsplit = nsplit;
+    sk.wtile = item / nsplit;
+    sk.split = item - (int)sk.wtile * nsplit;
+    sk.cnt = cnt;
+    sk.part = part;
+    int local;
+    const GemmArgs a = seg_args(t, (int)sk.wtile, local);
+    decode2_body<MB, CB, NW, BB, TAIL, true>(a, local, sk);
+}
+
+template <int MB, int CB, int NW, int BB>
+static hipError_t run_decode2s(const GemmArgs &a, const SegSpec *sp, int nsplit, void *ws, hipStream_t s)
+{
+    unsigned *cnt = static_cast<unsigned *>(ws);
+    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + SPLIT_COUNTER_BYTES);
+    if (sp) {
+        const SegTable t = make_seg_table(a, *sp, 16 * CB);
+        const dim3 grid((unsigned)(t.start[t.nseg] * nsplit));
+        if (a.k > 0)
+            hipLaunchKernelGGL((decode2s_seg_kernel<MB, CB, NW, BB, true>), grid, dim3(64 * NW), 0, s, t, nsplit,
+                               cnt, part);
+        else
+            hipLaunchKernelGGL((decode2s_seg_kernel<MB, CB, NW, BB, false>), grid, dim3(64 * NW), 0, s, t, nsplit,
+                               cnt, part);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)(((a.N + 16 * CB - 1) / (16 * CB)) * nsplit));
+    if (a.k > 0)
+        hipLaunchKernelGGL((decode2s_kernel<MB, CB, NW, BB, true>), grid, dim3(64 * NW), 0, s, a, nsplit, cnt, part);
+    else
+        hipLaunchKernelGGL((decode2s_kernel<MB, CB, NW, BB, false>), grid, dim3(64 * NW), 0, s, a, nsplit, cnt, part);
+    return hipGetLastError();
 }
 
 template <int MB, int CB, int NW, int BB>
@@ -1349,21 +1501,6 @@ static int64_t tiles_n128(int64_t N, const GemmSeg *seg, int nseg)
     return t;
 }
 
-size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K)
-{
-    // the decode path keeps no partial results in device memory
-    if (p != Path::Prefill || M <= 0 || N <= 0 || K <= 0) return 0;
-    return plan_prefill(M, N, K, tiles_n128(N, nullptr, 0)).ws;
-}
-
-size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int nseg)
-{
-    int64_t N = 0;
-    for (int i = 0; i < nseg; i++) N += seg[i].N;
-    if (p != Path::Prefill || M <= 0 || N <= 0 || K <= 0) return 0;
-    return plan_prefill(M, N, K, tiles_n128(N, seg, nseg)).ws;
-}
-
 // ===========================================================================
 // Configuration choice (plan_gemm) and launch (dispatch_gemm).
 // Decode configurations come from measured sweeps on MI355X (Qwen3-8B
@@ -1380,14 +1517,50 @@ size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int n
 //    over 8 waves;
 //  - M in 33..64: streaming, 48 columns per workgroup for wide N.
 enum class Kern { P256, P128, XL8_4, XL16_4, XL16_6, XL16_8, D2_1_3, D3_1_1, D2_1_1, D3_2_3_W4,
-                  D2_2_1, D2_4_3, D2_4_1, D2_2_3 };
+                  D2_2_1, D2_4_3, D2_4_1, D2_2_3, D2S_1_1, D2S_2_1, D2S_2_4, D2S_4_2 };
 
 struct GemmPlan {
     Path path;
     Kern kern;
     int rows, cols;         // output tile of one workgroup
-    PrefillPlan pp;         // prefill: tile size, K split, workspace
+    PrefillPlan pp;         // tile size (prefill), K split and workspace (both paths)
 };
+
+// Decode path, K split over workgroups (decode2s): as many splits as bring
+// the column groups to 256 workgroups, at most DECODE_SPLIT_MAX and at most
+// one per eight chunks (every wave of a split holds a chunk).  Returns 1 when
+// that leaves nothing to split.
+static int decode_splits(int64_t colgroups, int nchunk)
+{
+    const int64_t cap = std::min<int64_t>(DECODE_SPLIT_MAX, nchunk / 8);
+    const int64_t s = std::min<int64_t>(cap, 256 / std::max<int64_t>(colgroups, 1));
+    return s >= 2 ? (int)s : 1;
+}
+
+// column groups of 16*cb columns: over the segments of seg (each rounded up
+// alone, as the segment launch counts them), or of N
+static int64_t column_groups(int64_t N, const GemmSeg *seg, int nseg, int cb)
+{
+    const int64_t u = 16 * cb;
+    if (!seg) return (N + u - 1) / u;
+    int64_t t = 0;
+    for (int i = 0; i < nseg; i++) t += (seg[i].N + u - 1) / u;
+    return t;
+}
+
+static void set_decode_split(GemmPlan &g, Kern kern, int mb, int cb, int64_t N, const GemmSeg *seg, int nseg,
+                             int nchunk)
+{
+    const int64_t cg = column_groups(N, seg, nseg, cb);
+    const int ns = decode_splits(cg, nchunk);
+    if (ns < 2) return;
+    g.kern = kern;
+    g.rows = 16 * mb;
+    g.cols = 16 * cb;
+    g.pp.nsplit = ns;
+    g.pp.tiles = cg;
+    g.pp.ws = SPLIT_COUNTER_BYTES + (size_t)cg * ns * mb * cb * WAVE * 16;
+}
 
 static GemmPlan plan_gemm(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg *seg, int nseg)
 {
@@ -1416,6 +1589,7 @@ static GemmPlan plan_gemm(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg
             g.cols = 48;
         } else {
             g.kern = nchunk <= 32 ? Kern::D3_1_1 : Kern::D2_1_1;
+            if (colblocks <= 64) set_decode_split(g, Kern::D2S_1_1, 1, 1, N, seg, nseg, nchunk);
         }
     } else if (M <= 32) {
         g.rows = 32;
@@ -1430,11 +1604,14 @@ static GemmPlan plan_gemm(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg
             g.cols = 48;
         } else {
             g.kern = Kern::D2_2_1;
+            if (colblocks <= 64) set_decode_split(g, Kern::D2S_2_1, 2, 1, N, seg, nseg, nchunk);
+            else if (nchunk >= 64) set_decode_split(g, Kern::D2S_2_4, 2, 4, N, seg, nseg, nchunk);
         }
     } else {
         g.rows = 64;
         g.cols = colblocks >= 512 ? 48 : 16;
         g.kern = colblocks >= 512 ? Kern::D2_4_3 : Kern::D2_4_1;
+        if (colblocks <= 256) set_decode_split(g, Kern::D2S_4_2, 4, 2, N, seg, nseg, nchunk);
     }
     return g;
 }
@@ -1460,8 +1637,27 @@ static hipError_t dispatch_gemm(Path p, const GemmArgs &a, const SegSpec *sp, vo
     case Kern::D2_2_3: return run_decode2<2, 3, 8, 1>(a, sp, s);
     case Kern::D2_4_3: return run_decode2<4, 3, 8, 1>(a, sp, s);
     case Kern::D2_4_1: return run_decode2<4, 1, 8, 2>(a, sp, s);
+    case Kern::D2S_1_1: return run_decode2s<1, 1, 8, 1>(a, sp, g.pp.nsplit, ws, s);
+    case Kern::D2S_2_1: return run_decode2s<2, 1, 8, 1>(a, sp, g.pp.nsplit, ws, s);
+    case Kern::D2S_2_4: return run_decode2s<2, 4, 8, 1>(a, sp, g.pp.nsplit, ws, s);
+    case Kern::D2S_4_2: return run_decode2s<4, 2, 8, 1>(a, sp, g.pp.nsplit, ws, s);
     }
     return hipErrorInvalidValue;
+}
+
+// workspace of a call: the K split's counters and partial sums, or none
+size_t gemm_ws_bytes(Path p, int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || (p == Path::Decode && M > SPLICE_DECODE_MAX_M)) return 0;
+    return plan_gemm(p, M, N, K, nullptr, 0).pp.ws;
+}
+
+size_t gemm_seg_ws_bytes(Path p, int64_t M, int64_t K, const GemmSeg *seg, int nseg)
+{
+    int64_t N = 0;
+    for (int i = 0; i < nseg; i++) N += seg[i].N;
+    if (M <= 0 || N <= 0 || K <= 0 || (p == Path::Decode && M > SPLICE_DECODE_MAX_M)) return 0;
+    return plan_gemm(p, M, N, K, seg, nseg).pp.ws;
 }
 
 void gemm_plan_info(Path p, int64_t M, int64_t N, int64_t K, const GemmSeg *seg, int nseg, int32_t out[5])

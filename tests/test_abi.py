@@ -63,9 +63,9 @@ def test_gemm_argument_errors(L, kw, code):
 
 
 def test_gemm_workspace_size(L):
-    # the decode path keeps no partial results in device memory; the prefill
-    # path splits K (and needs a workspace) only where its tiles alone leave
-    # CUs idle, and the size covers a call forced onto the prefill path
+    # either path splits K (and needs a workspace) only where its tiles or
+    # column groups alone leave CUs idle, and the size covers a call forced
+    # onto either path
     for M, N, K, k in ((8192, 4096, 4096, 64), (4096, 12288, 4096, 64), (0, 1024, 4096, 64)):
         assert L.splice_workspace_size(M, N, K, k) == 0
     for M, N, K in ((1, 1024, 4096), (64, 4096, 4096), (65, 4096, 4096), (128, 1024, 4096),
@@ -79,6 +79,9 @@ def test_gemm_missing_workspace(L):
     assert gemm(L, M=128, N=1024, K=4096, k=64) == splice.ERR_WORKSPACE
     assert gemm(L, M=128, N=1024, K=4096, k=64, ws=FAKE, wsb=need - 1) == splice.ERR_WORKSPACE
     assert gemm(L, M=128, N=1024, K=4096, k=64, ws=FAKE + 8, wsb=need) == splice.ERR_WORKSPACE
+    # a decode-path call whose K range is split (M = 64, N = 1024)
+    assert splice.gemm_plan(64, 1024, 4096, splice.PATH_DECODE)[4] > 1
+    assert gemm(L, M=64, N=1024, K=4096, k=64, path=splice.PATH_DECODE) == splice.ERR_WORKSPACE
 
 
 def test_multi_workspace_size(L):

@@ -42,6 +42,42 @@ def test_mid_range_plans():
     assert S.gemm_plan(2048, 4096, 4096)[1:] == (0, 128, 128, 1)
 
 
+def test_decode_split_plans():
+    """Decode path: the K range is split where the column groups alone leave
+    CUs idle -- narrow N at 5..64 rows, deep K at 17..32 rows, N <= 4096 at
+    33..64 rows -- as many ways as bring the grid to 256 workgroups, at most
+    8 and at most one per eight chunks."""
+    q, k, gate, down = (4096, 4096), (1024, 4096), (12288, 4096), (4096, 12288)
+    expect = {  # M: {shape: (rows, cols, splits)}
+        4: {q: (16, 16, 1), k: (16, 16, 1), gate: (16, 16, 1), down: (16, 16, 1)},
+        8: {q: (16, 16, 1), k: (16, 16, 4), gate: (16, 48, 1), down: (16, 16, 1)},
+        16: {q: (16, 16, 1), k: (16, 16, 4), gate: (16, 48, 1), down: (16, 16, 1)},
+        32: {q: (32, 16, 1), k: (32, 16, 4), gate: (32, 48, 1), down: (32, 64, 4)},
+        64: {q: (64, 32, 2), k: (64, 32, 4), gate: (64, 48, 1), down: (64, 32, 2)},
+    }
+    for M, shapes in expect.items():
+        for (N, K), want in shapes.items():
+            path, kern, rows, cols, ns = S.gemm_plan(M, N, K, S.PATH_DECODE)
+            assert (path, rows, cols, ns) == (1,) + want, (M, N, K)
+            if ns > 1:
+                cg = -(-N // cols)
+                assert S.workspace_size(M, N, K) >= 1024 + cg * ns * rows * cols * 4
+
+
+def test_decode_split_counts_stay_in_bounds():
+    for M in (5, 8, 16, 17, 24, 32, 33, 48, 64):
+        for N in (16, 64, 500, 1000, 1024, 2100, 4096, 4100, 12288):
+            for K in (128, 1024, 2048, 4096, 5248, 8192, 12288, 17408, 65536):
+                ns = S.gemm_plan(M, N, K, S.PATH_DECODE)[4]
+                cols = S.gemm_plan(M, N, K, S.PATH_DECODE)[3]
+                nchunk = K // 128
+                assert 1 <= ns <= 8 and ns <= max(1, nchunk // 8)
+                cg = -(-N // cols)
+                assert ns == 1 or cg * ns <= 256
+                per = -(-nchunk // ns)
+                assert (ns - 1) * per < nchunk, (M, N, K, ns)
+
+
 def test_split_ranges_are_never_empty():
     for K in (512, 640, 1152, 4096, 12288, 17408):
         for M, N in ((65, 64), (128, 1024), (200, 300)):

@@ -48,11 +48,13 @@ def untouched(big, M, N):
 
 
 # (M, N, K, k, path): 256 x 256 tiles with ragged edges, 128 x 128 unsplit,
-# 128 x 128 with the K range split, decode
+# 128 x 128 with the K range split, decode unsplit, decode with the K range
+# split (1, 2 and 4 row blocks)
 CASES = [(4000, 4000, 256, 64, S.PATH_PREFILL), (2000, 1100, 512, 64, S.PATH_PREFILL),
          (100, 300, 1664, 64, S.PATH_PREFILL), (130, 250, 4096, 32, S.PATH_PREFILL),
          (37, 1000, 1024, 64, S.PATH_DECODE), (3, 8200, 384, 64, S.PATH_DECODE),
-         (64, 520, 12288, 16, S.PATH_DECODE)]
+         (64, 520, 12288, 16, S.PATH_DECODE), (8, 1000, 8192, 32, S.PATH_DECODE),
+         (24, 4000, 12288, 64, S.PATH_DECODE), (40, 1000, 4096, 64, S.PATH_DECODE)]
 
 
 @pytest.mark.parametrize("M,N,K,k,path", CASES)
@@ -66,9 +68,11 @@ def test_gemm_writes_only_its_product(M, N, K, k, path):
     assert untouched(big, M, N), (M, N, K, k, path, S.gemm_plan(M, N, K, path))
 
 
-@pytest.mark.parametrize("M,path", [(300, S.PATH_PREFILL), (96, S.PATH_PREFILL), (8, S.PATH_DECODE)])
-def test_multi_writes_only_its_products(M, path):
-    K, k, widths = 1024, 64, [520, 136, 136]
+@pytest.mark.parametrize("M,K,path", [(300, 1024, S.PATH_PREFILL), (96, 1024, S.PATH_PREFILL),
+                                      (8, 1024, S.PATH_DECODE), (8, 4096, S.PATH_DECODE),
+                                      (40, 4096, S.PATH_DECODE)])
+def test_multi_writes_only_its_products(M, K, path):
+    k, widths = 64, [520, 136, 136]
     gx, _, ax, _ = packs(M, 8, K, k, 7 + M)
     weights = []
     for i, n in enumerate(widths):

@@ -1,6 +1,7 @@
-"""GPU parity of the prefill path where its K sum is split over workgroups
-(M from 65 to a few hundred rows: the 128 x 128 tile grid alone would leave
-CUs idle), through the C ABI.
+"""GPU parity where the K sum is split over workgroups, through the C ABI: the
+prefill path (M from 65 to a few hundred rows: the 128 x 128 tile grid alone
+would leave CUs idle) and the decode path (narrow N or deep K at 5..64 rows:
+the column groups alone would leave CUs idle).
 
 Each split's partial tile goes to the workspace and the workgroup completing a
 tile's arrival count sums the partials in split order, so the result must not
@@ -146,6 +147,101 @@ def test_split_prefill_in_hip_graph():
         S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2], out=Y)
     for r in range(3):
         X = synth.to_bf16(g.standard_normal((M, K)))
+        S.quantize_nvfp4(dev(X), idx, ax, out=gx)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref), f"replay {r}"
+
+
+# decode path, (M, N, K, k): every split form (1, 2 and 4 row blocks; 1, 2 and 4
+# column blocks per group), ragged rows and columns, split counts that do not
+# divide the chunks (K = 5248: 41 chunks in 9, 9, 9, 9, 5; K = 17408: 136 in
+# 46, 46, 44), side operands k = 0, 32 and 64 (loaded ahead of the partial
+# sums) and 5, 100, 256 (the general side loop)
+DECODE_CASES = [(8, 1000, 8192, 32), (13, 1024, 4096, 64), (20, 500, 4608, 32), (29, 777, 5248, 5),
+                (24, 4000, 12288, 64), (40, 1000, 4096, 64), (64, 4096, 12288, 0), (33, 2100, 17408, 100),
+                (50, 64, 2048, 256)]
+
+
+def oracle_case(M, N, K, k, seed):
+    g = np.random.default_rng(seed)
+    X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
+    W = synth.to_bf16(g.normal(0, 0.02, (N, K)))
+    idx = np.sort(g.choice(K, size=k, replace=False)).astype(np.int32)
+    return X, W, idx
+
+
+@pytest.mark.parametrize("M,N,K,k", DECODE_CASES)
+def test_split_decode_ragged(M, N, K, k):
+    X, W, idx = oracle_case(M, N, K, k, M * 11 + N + K + k)
+    ax, aw = np.float32(O.compute_alpha(X, idx)), np.float32(O.compute_alpha(W, idx))
+    xq, xs, xS = O.quantize_nvfp4(X, idx, ax)
+    wq, ws, wS = O.quantize_nvfp4(W, idx, aw)
+    Yo = O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS)
+    plan = S.gemm_plan(M, N, K, S.PATH_DECODE)
+    assert plan[0] == 1 and plan[4] > 1, plan
+    Xd, Wd, idxd = dev(X), dev(W), dev(idx)
+    axd, awd = S.compute_alpha(Xd, idxd), S.compute_alpha(Wd, idxd)
+    gx, gw = S.quantize_nvfp4(Xd, idxd, axd), S.quantize_nvfp4(Wd, idxd, awd)
+    args = (gx[0], gx[1], axd, gx[2] if k else None, gw[0], gw[1], awd, gw[2] if k else None)
+    Y = S.splice_gemm(*args, path=S.PATH_DECODE)
+    Y2 = S.splice_gemm(*args, path=S.PATH_DECODE)
+    torch.cuda.synchronize()
+    assert_gemm_close(host(Y), Yo, f"M={M} N={N} K={K} k={k} plan={plan}")
+    assert torch.equal(Y, Y2)
+    if k == 0:
+        Yn = S.nvfp4_gemm(gx[0], gx[1], axd, gw[0], gw[1], awd, path=S.PATH_DECODE)
+        assert torch.equal(Yn, Y)
+
+
+def test_split_decode_shares_workspace_with_prefill():
+    """Decode-path and prefill-path split calls take turns on one workspace:
+    every call gives its first call's bits and the counters end at zero."""
+    shapes = [(64, 1024, 4096, S.PATH_DECODE), (128, 1024, 4096, S.PATH_PREFILL),
+              (24, 4000, 12288, S.PATH_DECODE), (8, 1000, 8192, S.PATH_DECODE),
+              (65, 4096, 4096, S.PATH_PREFILL), (40, 4096, 4096, S.PATH_DECODE)]
+    ops = []
+    for i, (M, N, K, path) in enumerate(shapes):
+        assert S.gemm_plan(M, N, K, path)[4] > 1
+        X, W, idx = oracle_case(M, N, K, 64, 300 + i)
+        Xd, Wd, idxd = dev(X), dev(W), dev(idx)
+        ax, aw = S.compute_alpha(Xd, idxd), S.compute_alpha(Wd, idxd)
+        ops.append((S.quantize_nvfp4(Xd, idxd, ax), S.quantize_nvfp4(Wd, idxd, aw), ax, aw, path))
+    ws = torch.zeros(max(S.workspace_size(M, N, K) for M, N, K, _ in shapes), dtype=torch.uint8, device="cuda")
+    first = []
+    for r in range(3):
+        for i, (gx, gw, ax, aw, path) in enumerate(ops):
+            Y = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2], path=path, ws=ws)
+            if r == 0:
+                first.append(Y)
+            else:
+                torch.cuda.synchronize()
+                assert torch.equal(Y, first[i]), f"round {r} shape {shapes[i]}"
+    torch.cuda.synchronize()
+    assert int(ws[:1024].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_split_decode_in_hip_graph():
+    """A decode-path split call (k at M = 32: four K ranges) captured once and
+    replayed with new activations: every replay gives the eager call's bits."""
+    M, N, K, k = 32, 1024, 4096, 64
+    assert S.gemm_plan(M, N, K)[4] > 1
+    X0, W, idx_h = oracle_case(M, N, K, k, 23)
+    g = np.random.default_rng(24)
+    idx = dev(idx_h)
+    Xd, Wd = dev(X0), dev(W)
+    ax, aw = S.compute_alpha(Xd, idx), S.compute_alpha(Wd, idx)
+    gx, gw = S.quantize_nvfp4(Xd, idx, ax), S.quantize_nvfp4(Wd, idx, aw)
+    Y = torch.empty(M, N, device="cuda")
+    S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2], out=Y)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2], out=Y)
+    for r in range(3):
+        X = synth.to_bf16(g.standard_normal((M, K)) * 2.0 ** r)
         S.quantize_nvfp4(dev(X), idx, ax, out=gx)
         graph.replay()
         torch.cuda.synchronize()

@@ -1,7 +1,8 @@
 """splice_gemm_noalloc on the GPU, through the C ABI: the allocation-free
 entry point (its workspace is the library's own per-device array) gives
 splice_gemm's bits, for two calls in a row on the K-split prefill path, the
-second smaller, and a decode-path call after them."""
+second smaller, and decode-path calls after them, with and without a K
+split."""
 import numpy as np
 import pytest
 import torch
@@ -33,12 +34,12 @@ def packs(M, N, K, k, seed):
 
 def test_noalloc_matches_splice_gemm_two_calls():
     # (M, N, K, k): a K-split prefill call, a smaller one (fewer tiles, a
-    # different split count), then a decode-path call that needs no workspace
-    cases = [(200, 1000, 4096, 64), (96, 300, 2176, 64), (8, 512, 1024, 64)]
+    # different split count), a decode-path call with its K range split, and
+    # one that needs no workspace
+    cases = [(200, 1000, 4096, 64), (96, 300, 2176, 64), (40, 1000, 4096, 64), (8, 512, 1024, 64)]
     for i, (M, N, K, k) in enumerate(cases):
         gx, gw, ax, aw, (X, W, idx) = packs(M, N, K, k, 31 + i)
-        if i < 2:
-            assert S.gemm_plan(M, N, K)[4] > 1
+        assert (S.gemm_plan(M, N, K)[4] > 1) == (i < 3)
         Y_ref = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
         Y = torch.full((M, N), float("nan"), device="cuda")
         torch.cuda.synchronize()
