@@ -1548,12 +1548,18 @@ static int64_t column_groups(int64_t N, const GemmSeg *seg, int nseg, int cb)
     return t;
 }
 
+// the largest decode split workspace (256 workgroups of 8 tiles) fits the
+// allocation-free entry's array
+static_assert(SPLIT_COUNTER_BYTES + (size_t)256 * 8 * WAVE * 16 <= SPLICE_NOALLOC_SCRATCH_BYTES, "no-alloc scratch");
+
 static void set_decode_split(GemmPlan &g, Kern kern, int mb, int cb, int64_t N, const GemmSeg *seg, int nseg,
                              int nchunk)
 {
     const int64_t cg = column_groups(N, seg, nseg, cb);
     const int ns = decode_splits(cg, nchunk);
     if (ns < 2) return;
+    // one arrival counter per column group, in the fixed counter region
+    if (cg * 4 > (int64_t)SPLIT_COUNTER_BYTES || mb * cb > 8) return;
     g.kern = kern;
     g.rows = 16 * mb;
     g.cols = 16 * cb;

@@ -168,16 +168,18 @@ int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda,
  *       SPLICE_PATH_PREFILL.
  * ws: DEVICE workspace of at least splice_workspace_size(M, N, K, k) bytes,
  *     16-byte aligned (NULL is allowed when that size is 0; a smaller or
- *     missing workspace returns SPLICE_ERR_WORKSPACE).  The prefill path
- *     splits the K range over workgroups when its output tiles alone would
- *     leave CUs idle (small M: up to a few hundred rows); the workspace then
- *     holds one arrival counter per output tile and the fp32 partial tiles,
- *     which the workgroup completing a tile sums in split order, so Y does not
- *     depend on arrival order.  The counters must be zero when the workspace
- *     is first used -- zero-fill it once after allocating it -- and every call
- *     leaves them zero again, so one workspace serves any sequence of calls
- *     ordered on a stream (calls that may run concurrently need workspaces of
- *     their own).  At most about 24 MiB; 0 for large M and on the decode path. */
+ *     missing workspace returns SPLICE_ERR_WORKSPACE).  Either path splits
+ *     the K range over workgroups when its output tiles alone would leave CUs
+ *     idle: the prefill path at small M (up to a few hundred rows), the decode
+ *     path for narrow or deep projections (few column groups, or long K).
+ *     The workspace then holds one arrival counter per output tile (column
+ *     group) and the fp32 partial sums, which the workgroup completing a tile
+ *     adds in split order, so Y does not depend on arrival order.  The
+ *     counters must be zero when the workspace is first used -- zero-fill it
+ *     once after allocating it -- and every call leaves them zero again, so
+ *     one workspace serves any sequence of calls ordered on a stream (calls
+ *     that may run concurrently need workspaces of their own).  At most
+ *     16 MiB + 1 KiB; 0 for large M. */
 int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
                 const uint8_t *Wq, const uint8_t *Ws, const float *alpha_w, const uint16_t *W_S,
                 int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy,
