@@ -92,11 +92,11 @@ def rows(draw, max_blocks=4, max_rows=3):
 
 
 @st.composite
-def gemm_case(draw, max_m=70, max_n=70, max_k128=3):
+def gemm_case(draw, max_m=70, max_n=70, min_k128=1, max_k128=3, min_m=1):
     """(X bits [M, K], alpha_x, W bits [N, K], alpha_w, protected columns),
     K a multiple of 128 as the GEMM entry points require."""
-    nb = 8 * draw(st.integers(1, max_k128))
-    M, N = draw(st.integers(1, max_m)), draw(st.integers(1, max_n))
+    nb = 8 * draw(st.integers(min_k128, max_k128))
+    M, N = draw(st.integers(min_m, max_m)), draw(st.integers(1, max_n))
     X, ax = draw(operand(M, nb))
     W, aw = draw(operand(N, nb))
     return X, ax, W, aw, draw(protected(nb))

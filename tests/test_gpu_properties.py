@@ -62,9 +62,7 @@ def test_quantize_bit_exact(case):
     assert scalar(a_g) == np.float32(O.compute_alpha(A, idx))
 
 
-@SETTINGS
-@given(gemm_case())
-def test_gemm_within_fp32_summation_bound(case):
+def check_gemm_bound(case):
     X, ax, W, aw, prot = case
     M, K = X.shape
     N = W.shape[0]
@@ -94,3 +92,23 @@ def test_gemm_within_fp32_summation_bound(case):
         bad = np.argwhere(err > bound)
         assert not bad.size, (f"path {path} M={M} N={N} K={K} k={k}: {len(bad)} outside; first "
                               f"{tuple(bad[0])}: err {err[tuple(bad[0])]!r} bound {bound[tuple(bad[0])]!r}")
+
+
+@SETTINGS
+@given(gemm_case())
+def test_gemm_within_fp32_summation_bound(case):
+    check_gemm_bound(case)
+
+
+@settings(max_examples=12, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(gemm_case(min_m=5, max_m=20, max_n=80, min_k128=64, max_k128=72))
+def test_gemm_bound_with_k_split(case):
+    """K = 8192..9216 at 5 to 20 rows and up to 80 columns: both paths split
+    the K range over workgroups (the decode path eight ways, the prefill path
+    16 or 18)."""
+    X, _, W, _, _ = case
+    M, K = X.shape
+    assert S.gemm_plan(M, W.shape[0], K, S.PATH_DECODE)[4] > 1
+    assert S.gemm_plan(M, W.shape[0], K, S.PATH_PREFILL)[4] > 1
+    check_gemm_bound(case)
