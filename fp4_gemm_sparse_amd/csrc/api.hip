@@ -4,6 +4,9 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -101,15 +104,40 @@ inline Path choose_path(int64_t M, int path)
     return M <= SPLICE_DECODE_MAX_M ? Path::Decode : Path::Prefill;
 }
 
-int run_gemm(const GemmArgs &a, void *ws, size_t ws_bytes, int path, hipStream_t s)
+// SPLICE_LOG set to anything but "" or "0" when the library is first used:
+// every GEMM call that passes its argument checks writes one line to stderr
+// with its shape, the launch its plan chose and the status it returns.
+bool log_on()
+{
+    static const bool on = [] {
+        const char *v = std::getenv("SPLICE_LOG");
+        return v != nullptr && *v != 0 && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+int log_gemm(const char *fn, Path p, int64_t M, int64_t N, int64_t K, int32_t k, const GemmSeg *seg, int nseg,
+             int rc)
+{
+    if (!log_on()) return rc;
+    int32_t pl[5] = {0, 0, 0, 0, 0};
+    gemm_plan_info(p, M, N, K, seg, nseg, pl);
+    std::fprintf(stderr, "[splice] %s M=%lld N=%lld K=%lld k=%d segments=%d path=%s kernel=%d tile=%dx%d "
+                 "splits=%d status=%d\n", fn, (long long)M, (long long)N, (long long)K, (int)k, nseg,
+                 pl[0] == 1 ? "decode" : "prefill", (int)pl[1], (int)pl[2], (int)pl[3], (int)pl[4], rc);
+    return rc;
+}
+
+int run_gemm(const char *fn, const GemmArgs &a, void *ws, size_t ws_bytes, int path, hipStream_t s)
 {
     int rc = check_gemm(a, path);
     if (rc) return rc;
     if (a.M == 0 || a.N == 0) return SPLICE_OK;
     const Path p = choose_path(a.M, path);
     const size_t need = gemm_ws_bytes(p, a.M, a.N, a.K);
-    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16))) return SPLICE_ERR_WORKSPACE;
-    return hip_status(launch_gemm(p, a, ws, ws_bytes, s));
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16)))
+        return log_gemm(fn, p, a.M, a.N, a.K, a.k, nullptr, 0, SPLICE_ERR_WORKSPACE);
+    return log_gemm(fn, p, a.M, a.N, a.K, a.k, nullptr, 0, hip_status(launch_gemm(p, a, ws, ws_bytes, s)));
 }
 
 }  // namespace
@@ -283,7 +311,7 @@ int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, cons
                 size_t ws_bytes, int path, splice_stream_t stream)
 {
     GemmArgs a{Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy};
-    return run_gemm(a, ws, ws_bytes, path, hs(stream));
+    return run_gemm("splice_gemm", a, ws, ws_bytes, path, hs(stream));
 }
 
 int splice_gemm_noalloc(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
@@ -297,13 +325,15 @@ int splice_gemm_noalloc(const uint8_t *Xq, const uint8_t *Xs, const float *alpha
     if (a.M == 0 || a.N == 0) return SPLICE_OK;
     const Path p = choose_path(a.M, path);
     const size_t need = gemm_ws_bytes(p, a.M, a.N, a.K);
-    if (need > SPLICE_NOALLOC_SCRATCH_BYTES) return SPLICE_ERR_WORKSPACE;
+    if (need > SPLICE_NOALLOC_SCRATCH_BYTES)
+        return log_gemm("splice_gemm_noalloc", p, M, N, K, k, nullptr, 0, SPLICE_ERR_WORKSPACE);
     void *ws = nullptr;
     if (need > 0) {
         const hipError_t e = noalloc_scratch(hs(stream), &ws);
-        if (e != hipSuccess) return SPLICE_ERR_HIP;
+        if (e != hipSuccess) return log_gemm("splice_gemm_noalloc", p, M, N, K, k, nullptr, 0, SPLICE_ERR_HIP);
     }
-    return hip_status(launch_gemm(p, a, ws, need, hs(stream)));
+    return log_gemm("splice_gemm_noalloc", p, M, N, K, k, nullptr, 0,
+                    hip_status(launch_gemm(p, a, ws, need, hs(stream))));
 }
 
 int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint8_t *Wq,
@@ -311,7 +341,7 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const
                int64_t ldy, void *ws, size_t ws_bytes, int path, splice_stream_t stream)
 {
     GemmArgs a{Xq, Xs, alpha_x, nullptr, Wq, Ws, alpha_w, nullptr, M, N, K, 0, Y, ldy};
-    return run_gemm(a, ws, ws_bytes, path, hs(stream));
+    return run_gemm("nvfp4_gemm", a, ws, ws_bytes, path, hs(stream));
 }
 
 int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const uint16_t *X_S,
@@ -334,9 +364,11 @@ int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x
     if (M == 0 || total == 0) return SPLICE_OK;
     const Path p = choose_path(M, path);
     const size_t need = gemm_seg_ws_bytes(p, M, K, seg, nseg);
-    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16))) return SPLICE_ERR_WORKSPACE;
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16)))
+        return log_gemm("splice_gemm_multi", p, M, total, K, k, seg, nseg, SPLICE_ERR_WORKSPACE);
     GemmArgs base{Xq, Xs, alpha_x, X_S, nullptr, nullptr, nullptr, nullptr, M, total, K, k, nullptr, 0};
-    return hip_status(launch_gemm_seg(p, base, seg, nseg, ws, hs(stream)));
+    return log_gemm("splice_gemm_multi", p, M, total, K, k, seg, nseg,
+                    hip_status(launch_gemm_seg(p, base, seg, nseg, ws, hs(stream))));
 }
 
 int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,

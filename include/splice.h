@@ -46,6 +46,12 @@
  *     workspace buffers must be ordered by the caller.
  *   - Results do not depend on the path taken or the launch configuration
  *     except for fp32 rounding order in the GEMM accumulators.
+ *   - Logging: with SPLICE_LOG set to anything but "" or "0" in the
+ *     environment when the library is first used, every GEMM call
+ *     (splice_gemm, splice_gemm_noalloc, nvfp4_gemm, splice_gemm_multi) that
+ *     passes its argument checks writes one line to stderr: its shape, the
+ *     path, kernel, tile and K split its plan chose (as splice_gemm_plan
+ *     reports them) and the status it returns.
  */
 #ifndef SPLICE_H
 #define SPLICE_H

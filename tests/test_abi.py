@@ -322,3 +322,42 @@ def test_probe_argument_errors(L):
     assert r(FAKE + 8, 1 << 20, 8, FAKE, None) == splice.ERR_INVALID_ARG  # misaligned source
     assert r(None, 1 << 20, 8, FAKE, None) == splice.ERR_INVALID_ARG
     assert r(FAKE, 1 << 20, 8, None, None) == splice.ERR_INVALID_ARG
+
+
+LOG_PROBE = """
+import ctypes
+from fp4_gemm_sparse_amd import splice
+L = splice.lib()
+F = 0x100000
+def gemm(M, N, K, k, path):
+    return L.splice_gemm(F, F, F, F, F, F, F, F, M, N, K, k, F, N, None, 0, path, None)
+print(gemm(128, 1024, 4096, 64, splice.PATH_AUTO), gemm(64, 1024, 4096, 64, splice.PATH_DECODE),
+      gemm(8, 64, 100, 8, splice.PATH_AUTO))
+"""
+
+
+@pytest.mark.parametrize("flag", ["1", "0", None])
+def test_splice_log_lines(flag):
+    """SPLICE_LOG: one stderr line per GEMM call that passes its argument
+    checks, with the plan it chose and its status; nothing when unset or 0."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("SPLICE_LOG", None)
+    if flag is not None:
+        env["SPLICE_LOG"] = flag
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", LOG_PROBE], capture_output=True, text=True, env=env, cwd=root,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == [str(splice.ERR_WORKSPACE), str(splice.ERR_WORKSPACE), str(splice.ERR_INVALID_ARG)]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[splice]")]
+    if flag != "1":
+        assert lines == []
+        return
+    assert len(lines) == 2, r.stderr
+    assert "splice_gemm M=128 N=1024 K=4096 k=64 segments=0 path=prefill" in lines[0]
+    assert "tile=128x128 splits=8 status=-3" in lines[0]
+    assert "M=64 N=1024 K=4096 k=64 segments=0 path=decode" in lines[1]
+    assert "tile=64x32 splits=4 status=-3" in lines[1]
