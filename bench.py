@@ -306,6 +306,25 @@ def timed(torch, stream, fn, iters):
     return d[iters // 2]
 
 
+def timed_pair(torch, stream, fa, fb, iters):
+    """timed() for two functions whose calls alternate (a, b, a, b, ...), each
+    call bracketed by HIP events on the launch stream, so that a drift of the
+    clocks affects both alike: (median a call, median b call) in ms."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2 * iters)]
+    for i in range(iters):
+        for j, fn in enumerate((fa, fb)):
+            e = ev[2 * i + j]
+            e[0].record(stream)
+            fn(i)
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    out = []
+    for j in range(2):
+        d = sorted(ev[2 * i + j][0].elapsed_time(ev[2 * i + j][1]) for i in range(iters))
+        out.append(d[iters // 2])
+    return out
+
+
 def graph_timed(torch, fn, iters, reps=7):
     """ms per call of fn(i) replayed from a captured HIP graph of `iters` calls
     (removes host launch overhead; each kernel still pays its own dispatch):
@@ -764,7 +783,8 @@ def m_sweep_measurements(torch, S, P, dev, stream):
     plan (tile, K split).  Rows past the 8192 of the prefill workload repeat
     its activations.  Up to 2048 rows the weights are walked in copies past
     the last-level cache (HIP-graph replay); above, each call is
-    compute-bound and timed back to back."""
+    compute-bound and timed on its own, SpliceGEMM and NVFP4 calls
+    alternating."""
     res = {}
     for n in ("q", "gate"):
         p = P[n]
@@ -793,8 +813,7 @@ def m_sweep_measurements(torch, S, P, dev, stream):
                 for _ in range(2):
                     sp(0)
                     nv(0)
-                t = timed(torch, stream, sp, 10)
-                tn = timed(torch, stream, nv, 10)
+                t, tn = timed_pair(torch, stream, sp, nv, 10)
             fl = 2.0 * M * N * K
             plan = S.gemm_plan(M, N, K, S.PATH_PREFILL)
             res[f"{n}@M{M}"] = {"us": round(t * 1e3, 2), "nvfp4_us": round(tn * 1e3, 2),
@@ -807,7 +826,7 @@ def m_sweep_measurements(torch, S, P, dev, stream):
         del cp
         torch.cuda.empty_cache()
     res["timing"] = ("prefill path; M <= 2048: HIP-graph replay walking weight copies (over 512 MiB), "
-                     "median of 7 replays alternating with nvfp4_gemm; larger M: median of 10 calls")
+                     "median of 7 replays alternating with nvfp4_gemm; larger M: median of 10 calls, each alternating with an nvfp4_gemm call")
     return res
 
 
