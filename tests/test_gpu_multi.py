@@ -58,8 +58,22 @@ def same_plan(M, K, widths, path):
 def test_ragged_segments(M, k):
     """Five segments of ragged widths (one empty) against separate calls and
     the oracle; K = 1024."""
-    K, widths = 1024, [100, 17, 0, 300, 64]
-    g = np.random.default_rng(M * 10 + k)
+    check_ragged_segments(M, k, 1024)
+
+
+@pytest.mark.parametrize("M", [8, 20, 40, 64, 100])
+@pytest.mark.parametrize("k", [0, 64])
+def test_ragged_segments_split_k(M, k):
+    """The same five segments at K = 4096, where the launch splits its K range
+    over workgroups on either path (column groups or tiles counted per
+    segment)."""
+    assert S.multi_plan(M, 4096, [100, 17, 0, 300, 64])[4] > 1
+    check_ragged_segments(M, k, 4096)
+
+
+def check_ragged_segments(M, k, K):
+    widths = [100, 17, 0, 300, 64]
+    g = np.random.default_rng(M * 10 + k + (0 if K == 1024 else K))
     X = synth.to_bf16(g.standard_normal((M, K)) * np.where(g.random(K) < 0.03, 30.0, 1.0))
     Ws = [synth.to_bf16(g.normal(0, 0.02, (n, K))) for n in widths]
     xq, ax, wp = packs(X, Ws, k, M + k)
