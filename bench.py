@@ -684,6 +684,10 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
     # ---------------- token counts between decode and the timed prefill
     out["m_sweep"] = m_sweep_measurements(torch, S, P, dev, stream)
 
+    # ---------------- one rank's share under 8-way tensor parallelism
+    out["tp8_rank"] = tp_rank_measurements(torch, S, P, dev, stream)
+    log("tp8 rank", out["tp8_rank"])
+
     # ---------------- grouped MoE stand-in
     out["moe_grouped"] = moe_measurement(torch, S, synth, dev)
     log("moe", out["moe_grouped"])
@@ -735,6 +739,78 @@ def extra_measurements(args, torch, S, synth, P, names, gemm_ms, flops, stream):
 
 
 M_SWEEP = (65, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+TP = 8
+TP_SHARDS = (("q", "col"), ("k", "col"), ("gate", "col"), ("o", "row"), ("down", "row"))
+
+
+def tp_rank_measurements(torch, S, P, dev, stream):
+    """Rank 0's share of Qwen3-8B projections under 8-way tensor parallelism.
+    Column-parallel q, k and gate hold N/8 rows of W and the whole X;
+    row-parallel o and down hold K/8 channels of X and W, with the protected
+    channels that fall among them.  The protected set and both tensor scales
+    are the whole layer's: the sharded method gets them with one all-gather
+    and one all-reduce-max.  A row-parallel rank's fp32 Y is a partial sum
+    that an all-reduce would add.  Prefill runs the workload's 8192 rows,
+    alternating with nvfp4_gemm calls; decode runs 1 and 64 rows under
+    HIP-graph replay, walking weight copies."""
+    res = {}
+    for n, kind in TP_SHARDS:
+        p = P[n]
+        K, N = p["K"], p["N"]
+        idx = p["idx"]
+        if kind == "col":
+            Kr, Nr = K, N // TP
+            X, W, idx_r = p["X"], p["W"][:Nr], idx
+        else:
+            Kr, Nr = K // TP, N
+            X, W = p["X"][:, :Kr], p["W"][:, :Kr]
+            idx_r = idx[idx < Kr].contiguous()
+        kr = int(idx_r.numel())
+        xq = S.quantize_nvfp4(X, idx_r, p["ax"])
+        wq = S.quantize_nvfp4(W, idx_r, p["aw"])
+        xS = xq[2] if kr else None
+        M = X.shape[0]
+        Y = torch.empty(M, Nr, dtype=torch.float32, device=dev)
+        ws = S.workspace(max(1, S.workspace_size(M, Nr, Kr, kr)), dev)
+
+        def sp(i, M=M):
+            S.splice_gemm(xq[0][:M], xq[1][:M], p["ax"], xS[:M] if kr else None, wq[0], wq[1], p["aw"],
+                          wq[2] if kr else None, out=Y[:M], ws=ws)
+
+        def nv(i, M=M):
+            S.nvfp4_gemm(xq[0][:M], xq[1][:M], p["ax"], wq[0], wq[1], p["aw"], out=Y[:M], ws=ws)
+        for _ in range(3):
+            sp(0)
+            nv(0)
+        t, tn = timed_pair(torch, stream, sp, nv, 20)
+        r = {"K": Kr, "N": Nr, "k": kr, "parallel": "column" if kind == "col" else "row",
+             "prefill_us": round(t * 1e3, 2), "prefill_nvfp4_us": round(tn * 1e3, 2),
+             "prefill_tflops": round(2.0 * M * Nr * Kr / (t * 1e-3) / 1e12, 1),
+             "plan": list(S.gemm_plan(M, Nr, Kr))}
+        wbytes = pack_bytes(wq) if kr else pack_bytes(wq[:2])
+        ncopy = copies_for(wbytes)
+        cp = [wq] + [tuple(x.clone() for x in wq) for _ in range(ncopy - 1)]
+        for Md in (1, 64):
+            def dsp(i, Md=Md):
+                w = cp[i % ncopy]
+                S.splice_gemm(xq[0][:Md], xq[1][:Md], p["ax"], xS[:Md] if kr else None, w[0], w[1], p["aw"],
+                              w[2] if kr else None, out=Y[:Md], ws=ws)
+
+            def dnv(i, Md=Md):
+                w = cp[i % ncopy]
+                S.nvfp4_gemm(xq[0][:Md], xq[1][:Md], p["ax"], w[0], w[1], p["aw"], out=Y[:Md], ws=ws)
+            td, tdn = graph_timed_pair(torch, dsp, dnv, ncopy)
+            r[f"decode_M{Md}"] = {"us": round(td * 1e3, 2), "nvfp4_us": round(tdn * 1e3, 2),
+                                  "GBps": round(wbytes / (td * 1e-3) / 1e9, 1),
+                                  "plan": list(S.gemm_plan(Md, Nr, Kr))}
+        res[n] = r
+        del cp
+        torch.cuda.empty_cache()
+    res["what"] = ("rank 0 of 8-way tensor parallelism: column-parallel q, k, gate (N/8), row-parallel o, down "
+                   "(K/8, the protected channels of the shard); the layer's protected set and tensor scales")
+    return res
 
 
 def moe_measurement(torch, S, synth, dev):

@@ -588,10 +588,11 @@ __global__ __launch_bounds__(256, 2) void grouped_prefill_kernel(GroupedArgs ga)
 }
 
 // ---------------------------------------------------------------------------
-// Prefill plan: the 256 x 256 tile when its grid fills the GPU, else the
-// 128 x 128 tile.  At up to 128 tiles the K range is also split, as many ways
-// as keep the workgroups within 256 (one per CU) and each split at least eight
-// 64-channel steps: at M = 65..1024 on the Qwen3-8B shapes that count was the
+// Prefill plan: the 256 x 256 tile when its grid fills the GPU or the
+// 128 x 128 grid needs more than one round, else the 128 x 128 tile.  At up
+// to 128 tiles the K range is also split, as many ways as keep the
+// workgroups within 256 (one per CU) and each split at least eight 64-channel
+// steps: at M = 65..1024 on the Qwen3-8B shapes that count was the
 // fastest measured or within 1 us of it (q at M = 128: 52 us unsplit, 27 us in
 // eight splits; q at M = 512, 128 tiles: 51.5 -> 37.4 us in two; down at
 // M = 256: 145 -> 52 us in four).  More workgroups than CUs measured slower
@@ -621,12 +622,20 @@ static PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, int64_t tiles_n
 {
     PrefillPlan p{false, 1, 0, 0};
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= 240) {
+    const int64_t t128 = ((M + 127) / 128) * tiles_n128;
+    // the 256 x 256 tile when its grid fills the GPU, or when the 128 x 128
+    // tiles need more than one round at two per CU: a round of 256 x 256
+    // tiles (one per CU) takes about 4/3 of a full 128 x 128 round, so one
+    // big round beats one and a bit small ones (gate at M = 1024: 128 against
+    // 162 us; a gate shard of 1536 columns at M = 8192: 121 against 165 us),
+    // while at most one small round is as fast or faster (q at M = 2048: 107
+    // against 109 us; q at M = 1536: 101 against 86 us)
+    if (t256 >= 240 || t128 > 512) {
         p.big = true;
         p.tiles = t256;
         return p;
     }
-    p.tiles = ((M + 127) / 128) * tiles_n128;
+    p.tiles = t128;
     const int64_t nk = K / LdsCfg::BKL;
     if (p.tiles <= SPLIT_MAX_TILES && p.tiles > 0) {
         int64_t sp = std::min<int64_t>(SPLIT_WORKGROUPS / p.tiles, nk / SPLIT_MIN_STEPS);

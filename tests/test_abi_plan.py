@@ -78,6 +78,17 @@ def test_decode_split_counts_stay_in_bounds():
                 assert (ns - 1) * per < nchunk, (M, N, K, ns)
 
 
+def test_big_tile_when_small_tiles_need_two_rounds():
+    """Below 240 tiles of 256 x 256 the big tile still runs when the 128 x 128
+    grid needs more than one round (more than 512 tiles): gate at M = 768 and
+    1024, a 1536-column gate shard at M = 8192, q at M = 3072; at 512 small
+    tiles or fewer the small tile stays (q at M = 2048, gate at M = 512)."""
+    for M, N in ((768, 12288), (1024, 12288), (8192, 1536), (3072, 4096)):
+        assert S.gemm_plan(M, N, 4096)[2:] == (256, 256, 1), (M, N)
+    for M, N in ((2048, 4096), (512, 12288), (8192, 512), (1024, 4096)):
+        assert S.gemm_plan(M, N, 4096)[2] == 128, (M, N)
+
+
 def test_split_ranges_are_never_empty():
     for K in (512, 640, 1152, 4096, 12288, 17408):
         for M, N in ((65, 64), (128, 1024), (200, 300)):

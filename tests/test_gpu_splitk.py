@@ -64,6 +64,28 @@ def test_split_prefill_full_size_sampled(name, M):
     assert torch.isfinite(Yn).all()
 
 
+@pytest.mark.parametrize("M", [700, 1024])
+def test_prefill_mid_range_big_tile_sampled(M):
+    """gate at 700 and 1024 rows: fewer than 240 tiles of 256 x 256, but more
+    than one round of 128 x 128, so the big tile runs (ragged in the last
+    tile row at 700): 160 sampled columns against the oracle's own
+    calibration, packs and product."""
+    p = synth.projection(synth.CFG_PREFILL, "gate", M)
+    K, N = p["K"], p["N"]
+    assert S.gemm_plan(M, N, K)[2:] == (256, 256, 1)
+    cols = np.sort(np.random.default_rng(M + N).choice(N, size=160, replace=False))
+    idx_o, ax_o, _ = O.select_channels(p["X_warm"], 64)
+    aw_o = O.compute_alpha(p["W"], idx_o)
+    xo = O.quantize_nvfp4(p["X"], idx_o, ax_o)
+    wo = O.quantize_nvfp4(p["W"][cols], idx_o, aw_o)
+    Yo = O.splice_gemm(xo[0], xo[1], ax_o, xo[2], wo[0], wo[1], aw_o, wo[2])
+    idx, ax, aw, gx, gw = gpu_packs(p["X_warm"], p["X"], p["W"], 64)
+    Y = S.splice_gemm(gx[0], gx[1], ax, gx[2], gw[0], gw[1], aw, gw[2])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gx[0]), xo[0]) and np.array_equal(host(gw[0])[cols], wo[0])
+    assert_gemm_close(host(Y)[:, cols], Yo, f"gate M={M}")
+
+
 # (M, N, K, k): ragged tiles in M and N, split counts that do not divide the
 # K steps (K = 1664: 26 steps in splits of 9, 9, 8; K = 2176: 34 steps in
 # 9, 9, 9, 7), many splits (K = 17408: 34; K = 12288: 24), every side-operand
