@@ -181,10 +181,12 @@ def test_split_prefill_in_hip_graph():
 # column blocks per group), ragged rows and columns, split counts that do not
 # divide the chunks (K = 5248: 41 chunks in 9, 9, 9, 9, 5; K = 17408: 136 in
 # 46, 46, 44), side operands k = 0, 32 and 64 (loaded ahead of the partial
-# sums) and 5, 100, 256 (the general side loop)
+# sums; W_S behind the first weight batch where each wave finishes a tile of
+# its own, the 64 x 32 and 32 x 64 forms) and 5, 100, 256 (the general side
+# loop)
 DECODE_CASES = [(8, 1000, 8192, 32), (13, 1024, 4096, 64), (20, 500, 4608, 32), (29, 777, 5248, 5),
                 (24, 4000, 12288, 64), (40, 1000, 4096, 64), (64, 4096, 12288, 0), (33, 2100, 17408, 100),
-                (50, 64, 2048, 256)]
+                (50, 64, 2048, 256), (48, 3000, 4096, 32), (30, 2000, 12288, 32)]
 
 
 def oracle_case(M, N, K, k, seed):
