@@ -100,3 +100,27 @@ def gemm_case(draw, max_m=70, max_n=70, min_k128=1, max_k128=3, min_m=1):
     X, ax = draw(operand(M, nb))
     W, aw = draw(operand(N, nb))
     return X, ax, W, aw, draw(protected(nb))
+
+
+@st.composite
+def channel_moments(draw, max_k_chan=5008):
+    """(count, mean fp64 [K], m2 fp64 [K], absmax fp32 [K], k): running
+    moments with many exact ties (values drawn from a small pool), zeros,
+    subnormal and huge values, and k from 0 to all channels; K a multiple of
+    16, as the entry points require."""
+    K = draw(st.sampled_from([16, 32, 64, 304, 1024, 4096, max_k_chan]))
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    g = np.random.default_rng(seed)
+    pool = np.array([0.0, 5e-324, 1e-300, 1.0, 1.0 + 2 ** -52, 2.0, 3.5, 1e10, 1e300])
+    kind = draw(st.sampled_from(["pool", "pool", "wide", "integers"]))
+    if kind == "pool":
+        m2 = g.choice(pool, K)
+    elif kind == "wide":
+        m2 = np.abs(g.standard_normal(K)) * 10.0 ** g.integers(-300, 300, K)
+    else:
+        m2 = g.integers(0, 4, K).astype(np.float64)
+    count = draw(st.integers(0, 10 ** 6))
+    mean = g.standard_normal(K) * 10.0 ** g.integers(-5, 5, K)
+    absmax = np.abs(g.standard_normal(K)).astype(np.float32) * np.float32(2.0 ** int(g.integers(-20, 20)))
+    k = draw(st.integers(0, min(K, 300)))
+    return count, mean, m2, absmax, k

@@ -25,7 +25,7 @@ from hypothesis import HealthCheck, given, settings
 import oracle as O
 from fp4_gemm_sparse_amd import splice as S
 from gpu_util import dev, host, scalar
-from props import gemm_case, rows
+from props import channel_moments, gemm_case, rows
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +112,21 @@ def test_gemm_bound_with_k_split(case):
     assert S.gemm_plan(M, W.shape[0], K, S.PATH_DECODE)[4] > 1
     assert S.gemm_plan(M, W.shape[0], K, S.PATH_PREFILL)[4] > 1
     check_gemm_bound(case)
+
+
+@SETTINGS
+@given(channel_moments())
+def test_select_topk_bit_exact(case):
+    """Top-k by variance and by second moment on moments with many exact
+    ties, subnormal and huge values: indices and alpha_x bit-exact against
+    the oracle."""
+    count, mean, m2, absmax, k = case
+    st = O.Stats(len(m2))
+    st.count, st.mean, st.m2, st.absmax = count, mean, m2, absmax
+    stats = S.ChannelStats(count, dev(mean), dev(m2), dev(absmax))
+    for crit, ocrit in ((S.SELECT_VARIANCE, O.VARIANCE), (S.SELECT_SECOND_MOMENT, O.SECOND_MOMENT)):
+        idx_o, ax_o = O.select_from_stats(st, k, ocrit)
+        idx, ax = S.select_topk(stats, k, crit)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx), idx_o), (crit, k)
+        assert scalar(ax) == np.float32(ax_o), (crit, k)

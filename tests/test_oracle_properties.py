@@ -8,7 +8,7 @@ import numpy as np
 from hypothesis import HealthCheck, given, settings
 
 import brute
-from props import rows
+from props import channel_moments, rows
 
 SETTINGS = settings(max_examples=250, deadline=None, derandomize=True, database=None,
                     suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
@@ -48,3 +48,19 @@ def test_quantize_sign_symmetry(oracle_lib, case):
     # unprotected lanes flip their sign bit, protected lanes stay +0
     assert np.array_equal(n2[:, ~pm], n1[:, ~pm] ^ 8)
     assert not n1[:, pm].any() and not n2[:, pm].any()
+
+
+def brute_topk(values, k):
+    """The k largest values, ties to the lower index, as ascending indices."""
+    order = sorted(range(len(values)), key=lambda j: (-values[j], j))
+    return np.sort(np.asarray(order[:k], dtype=np.int64))
+
+
+@settings(max_examples=150, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(channel_moments())
+def test_select_topk_matches_sort(oracle_lib, case):
+    """The oracle's top-k against a plain sort, on values with many exact
+    ties: the set is the k largest and ties go to the lower index."""
+    _, _, m2, _, k = case
+    assert np.array_equal(oracle_lib.select_topk(m2, k), brute_topk(m2, k))
