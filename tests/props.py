@@ -124,3 +124,33 @@ def channel_moments(draw, max_k_chan=5008):
     absmax = np.abs(g.standard_normal(K)).astype(np.float32) * np.float32(2.0 ** int(g.integers(-20, 20)))
     k = draw(st.integers(0, min(K, 300)))
     return count, mean, m2, absmax, k
+
+
+@st.composite
+def rollout_batch(draw):
+    """(logp float32 [B, L], lengths int32 [B], log_tau, (k1_num, k1_den),
+    k2): per-token log-probabilities built from runs of tail tokens (at or
+    just below log tau, or far below) and ordinary tokens (at or just above
+    log tau, or near 0), so that both gate counts sit near their limits;
+    lengths from 0 to L."""
+    B = draw(st.integers(1, 300))
+    L = draw(st.sampled_from([1, 2, 7, 64, 513, 2048]))
+    log_tau = float(np.log(np.float32(draw(st.sampled_from([1e-4, 1e-2, 0.5])))))
+    k1 = draw(st.sampled_from([(0, 1), (1, 100), (3, 7), (1, 1), (2, 1000)]))
+    k2 = draw(st.integers(0, 40))
+    seed = draw(st.integers(0, 2 ** 32 - 1))
+    g = np.random.default_rng(seed)
+    t = np.float32(log_tau)
+    tail = np.array([t, np.nextafter(t, np.float32(-np.inf)), np.float32(-30.0)], np.float32)
+    ordinary = np.array([np.nextafter(t, np.float32(np.inf)), np.float32(0.0), np.float32(-1e-3)], np.float32)
+    logp = np.empty((B, L), np.float32)
+    p_tail = g.uniform(0.0, 0.5)
+    for b in range(B):
+        j = 0
+        while j < L:
+            run = int(g.integers(1, 12))
+            src = tail if g.random() < p_tail else ordinary
+            logp[b, j:j + run] = g.choice(src, min(run, L - j))
+            j += run
+    lengths = g.integers(0, L + 1, B).astype(np.int32)
+    return logp, lengths, log_tau, k1, k2

@@ -25,7 +25,7 @@ from hypothesis import HealthCheck, given, settings
 import oracle as O
 from fp4_gemm_sparse_amd import splice as S
 from gpu_util import dev, host, scalar
-from props import channel_moments, gemm_case, rows
+from props import channel_moments, gemm_case, rollout_batch, rows
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +130,21 @@ def test_select_topk_bit_exact(case):
         torch.cuda.synchronize()
         assert np.array_equal(host(idx), idx_o), (crit, k)
         assert scalar(ax) == np.float32(ax_o), (crit, k)
+
+
+@SETTINGS
+@given(rollout_batch())
+def test_tim_filter_bit_exact(case):
+    """The TIM-aware filter on batches built from runs of tail and ordinary
+    tokens, at and next to log tau, with every gate setting drawn: keep, both
+    gate counts and the masked advantages bit-exact against the oracle."""
+    logp, lengths, log_tau, k1, k2 = case
+    B = logp.shape[0]
+    adv = np.random.default_rng(B).standard_normal((B, 3)).astype(np.float32)
+    ko, g1o, g2o, ao = O.tim_filter(logp, lengths, np.float32(log_tau), k1[0], k1[1], k2, adv=adv)
+    advd = dev(adv)
+    keep, g1, g2 = S.tim_filter(dev(logp), dev(lengths), np.float32(log_tau), k1, k2, adv=advd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(keep), ko)
+    assert np.array_equal(host(g1), g1o) and np.array_equal(host(g2), g2o)
+    assert np.array_equal(host(advd).view(np.uint32), ao.view(np.uint32))
