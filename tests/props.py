@@ -154,3 +154,32 @@ def rollout_batch(draw):
             j += run
     lengths = g.integers(0, L + 1, B).astype(np.int32)
     return logp, lengths, log_tau, k1, k2
+
+
+@st.composite
+def token_batches(draw):
+    """(K, [(bf16 bits [T, K], row step)...]): two to four batches of token
+    rows for running channel moments, each folded through a row stride that
+    keeps every row or every second or third one; values normal, tiny, huge,
+    constant per channel or zero, so that the Welford updates meet
+    cancellation and exact zeros."""
+    K = draw(st.sampled_from([16, 48, 256, 1040]))
+    nb = draw(st.integers(2, 4))
+    out = []
+    for _ in range(nb):
+        T = draw(st.integers(1, 200))
+        step = draw(st.sampled_from([1, 1, 2, 3]))
+        kind = draw(st.sampled_from(["normal", "scaled", "constant", "zero", "offset"]))
+        g = np.random.default_rng(draw(st.integers(0, 2 ** 32 - 1)))
+        if kind == "normal":
+            x = g.standard_normal((T, K))
+        elif kind == "scaled":
+            x = g.standard_normal((T, K)) * 2.0 ** g.integers(-100, 100, K)
+        elif kind == "constant":
+            x = np.tile(g.standard_normal(K) * 1e3, (T, 1))
+        elif kind == "zero":
+            x = np.zeros((T, K))
+        else:
+            x = 1e4 + g.standard_normal((T, K))
+        out.append((synth.to_bf16(x), step))
+    return K, out

@@ -25,7 +25,7 @@ from hypothesis import HealthCheck, given, settings
 import oracle as O
 from fp4_gemm_sparse_amd import splice as S
 from gpu_util import dev, host, scalar
-from props import channel_moments, gemm_case, rollout_batch, rows
+from props import channel_moments, gemm_case, rollout_batch, rows, token_batches
 
 pytestmark = pytest.mark.gpu
 
@@ -148,3 +148,23 @@ def test_tim_filter_bit_exact(case):
     assert np.array_equal(host(keep), ko)
     assert np.array_equal(host(g1), g1o) and np.array_equal(host(g2), g2o)
     assert np.array_equal(host(advd).view(np.uint32), ao.view(np.uint32))
+
+
+@SETTINGS
+@given(token_batches())
+def test_running_channel_stats_bit_exact(case):
+    """Running moments folded batch after batch, each through a drawn row
+    stride: count, mean, M2 and absmax bit-exact against the oracle's fold
+    of the same rows after every batch."""
+    K, batches = case
+    st_o = O.Stats(K)
+    st_g = S.ChannelStats.empty(K)
+    for X, step in batches:
+        T = (X.shape[0] + step - 1) // step
+        st_o.update(np.ascontiguousarray(X[::step]))
+        st_g = S.channel_stats(dev(X), st_g, ldx=step * K, T=T)
+        torch.cuda.synchronize()
+        assert st_g.count == st_o.count
+        assert np.array_equal(host(st_g.mean).view(np.uint64), st_o.mean.view(np.uint64))
+        assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
+        assert np.array_equal(host(st_g.absmax), st_o.absmax)
