@@ -183,3 +183,23 @@ def token_batches(draw):
             x = 1e4 + g.standard_normal((T, K))
         out.append((synth.to_bf16(x), step))
     return K, out
+
+
+@st.composite
+def grouped_case(draw):
+    """(N, K, k, [(X bits [M_e, K], alpha_x, W bits [N, K], alpha_w,
+    protected columns)...]): 1 to 40 groups sharing N, K and the protected
+    count k, each with its own rows (0 to 300), blocks, tensor scales and
+    protected set."""
+    nb = 8 * draw(st.integers(1, 3))
+    K = 16 * nb
+    N = draw(st.integers(1, 300))
+    k = draw(st.sampled_from([0, 0, 3, 16, 32, 64]))
+    groups = []
+    for _ in range(draw(st.integers(1, 40))):
+        M = draw(st.sampled_from([0, 1, 5, 64, 127, 128, 129, 300]))
+        X, ax = draw(operand(M, nb))
+        W, aw = draw(operand(N, nb))
+        prot = sorted(draw(st.permutations(range(K)))[:k]) if k else []
+        groups.append((X, ax, W, aw, prot))
+    return N, K, k, groups

@@ -25,7 +25,7 @@ from hypothesis import HealthCheck, given, settings
 import oracle as O
 from fp4_gemm_sparse_amd import splice as S
 from gpu_util import dev, host, scalar
-from props import channel_moments, gemm_case, rollout_batch, rows, token_batches
+from props import channel_moments, gemm_case, grouped_case, rollout_batch, rows, token_batches
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,21 @@ def test_quantize_bit_exact(case):
     if len(prot):
         assert np.array_equal(host(side_g), side_o)
     assert scalar(a_g) == np.float32(O.compute_alpha(A, idx))
+
+
+def oracle_with_bound(X, ax, W, aw, idx):
+    """The oracle's product of these operands and the fp32 summation bound
+    of every output (section above)."""
+    K = X.shape[1]
+    k = len(idx)
+    xq, xs, xS = O.quantize_nvfp4(X, idx, ax)
+    wq, ws, wS = O.quantize_nvfp4(W, idx, aw)
+    Yo = O.splice_gemm(xq, xs, ax, xS, wq, ws, aw, wS).astype(np.float64)
+    T = np.abs(O.dequantize(xq, xs, ax)) @ np.abs(O.dequantize(wq, ws, aw)).T
+    if k:
+        T += np.abs(bf16_values(xS)) @ np.abs(bf16_values(wS)).T
+    n = K + k + 8
+    return Yo, n * U / (1 - n * U) * T
 
 
 def check_gemm_bound(case):
@@ -168,3 +183,40 @@ def test_running_channel_stats_bit_exact(case):
         assert np.array_equal(host(st_g.mean).view(np.uint64), st_o.mean.view(np.uint64))
         assert np.array_equal(host(st_g.m2).view(np.uint64), st_o.m2.view(np.uint64))
         assert np.array_equal(host(st_g.absmax), st_o.absmax)
+
+
+@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(grouped_case())
+def test_grouped_within_fp32_summation_bound(case):
+    """The grouped launch over 1 to 40 groups of drawn sizes (empty groups
+    included) on adversarial blocks, each with its own tensor scales and
+    protected set: every group's output within the fp32 summation bound of
+    the oracle's product."""
+    N, K, k, groups = case
+    dgroups, refs = [], []
+    for X, ax, W, aw, prot in groups:
+        M = X.shape[0]
+        idx = np.asarray(prot, np.int32)
+        ax32, aw32 = np.float32(ax), np.float32(aw)
+        axd, awd = dev(np.array([ax32], np.float32)), dev(np.array([aw32], np.float32))
+        if M:
+            gx = S.quantize_nvfp4(dev(X), dev(idx), axd)
+            refs.append(oracle_with_bound(X, ax32, W, aw32, idx))
+        else:
+            gx = (torch.zeros(0, K // 2, dtype=torch.uint8, device="cuda"),
+                  torch.zeros(0, K // 16, dtype=torch.uint8, device="cuda"),
+                  torch.zeros(0, max(k, 1), dtype=torch.int16, device="cuda"))
+            refs.append(None)
+        gw = S.quantize_nvfp4(dev(W), dev(idx), awd)
+        dgroups.append(dict(Xq=gx[0], Xs=gx[1], alpha_x=axd, X_S=gx[2], Wq=gw[0], Ws=gw[1], alpha_w=awd,
+                            W_S=gw[2], Y=torch.full((M, N), float("nan"), device="cuda")))
+    S.splice_gemm_grouped(dgroups, N, K, k)
+    torch.cuda.synchronize()
+    for e, (g, ref) in enumerate(zip(dgroups, refs)):
+        if ref is None:
+            continue
+        Yo, bound = ref
+        err = np.abs(host(g["Y"]).astype(np.float64) - Yo)
+        bad = np.argwhere(~(err <= bound))
+        assert not bad.size, f"group {e} of {len(groups)}: M={g['Y'].shape[0]} N={N} K={K} k={k}: {len(bad)} outside"
