@@ -4,11 +4,14 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
+
+#include <dlfcn.h>
 
 #include <hip/hip_runtime.h>
 
@@ -128,6 +131,62 @@ int log_gemm(const char *fn, Path p, int64_t M, int64_t N, int64_t K, int32_t k,
     return rc;
 }
 
+// SPLICE_ROCTX set to anything but "" or "0" when the library is first used:
+// every compute entry point runs inside a roctx range named for the call and
+// its shape, for profilers that trace markers (rocprofv3 --marker-trace).
+// The roctx library is opened at that first use, so the library itself does
+// not depend on it; when it cannot be opened the ranges are left out.
+struct RoctxApi {
+    int (*push)(const char *) = nullptr;
+    int (*pop)() = nullptr;
+};
+
+const RoctxApi &roctx()
+{
+    static const RoctxApi api = [] {
+        RoctxApi r;
+        const char *v = std::getenv("SPLICE_ROCTX");
+        if (v == nullptr || *v == 0 || std::strcmp(v, "0") == 0) return r;
+        for (const char *name : {"librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so", "libroctx64.so.4",
+                                 "libroctx64.so"}) {
+            void *h = dlopen(name, RTLD_NOW | RTLD_LOCAL);
+            if (!h) continue;
+            r.push = reinterpret_cast<int (*)(const char *)>(dlsym(h, "roctxRangePushA"));
+            r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+            if (r.push && r.pop) return r;
+            r = RoctxApi{};
+        }
+        return r;
+    }();
+    return api;
+}
+
+// a roctx range for the lifetime of the object (nothing when SPLICE_ROCTX is off)
+class Range {
+public:
+    explicit Range(const char *fmt, ...) __attribute__((format(printf, 2, 3)))
+    {
+        const RoctxApi &r = roctx();
+        if (!r.push) return;
+        char name[160];
+        va_list ap;
+        va_start(ap, fmt);
+        std::vsnprintf(name, sizeof(name), fmt, ap);
+        va_end(ap);
+        r.push(name);
+        on_ = true;
+    }
+    ~Range()
+    {
+        if (on_) roctx().pop();
+    }
+    Range(const Range &) = delete;
+    Range &operator=(const Range &) = delete;
+
+private:
+    bool on_ = false;
+};
+
 int run_gemm(const char *fn, const GemmArgs &a, void *ws, size_t ws_bytes, int path, hipStream_t s)
 {
     int rc = check_gemm(a, path);
@@ -162,6 +221,7 @@ int splice_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx,
                            int64_t *count, double *mean, double *m2, float *absmax, int32_t *idx,
                            float *alpha_x, void *ws, size_t ws_bytes, splice_stream_t stream)
 {
+    const Range range("splice_select_channels T=%lld K=%lld k=%d", (long long)T, (long long)K, (int)k);
     (void)ws;
     (void)ws_bytes;
     if (T < 0 || !count || *count < 0) return SPLICE_ERR_INVALID_ARG;
@@ -187,6 +247,7 @@ int splice_select_channels(const uint16_t *X, int64_t T, int64_t K, int64_t ldx,
 int splice_channel_stats(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, int64_t *count,
                          double *mean, double *m2, float *absmax, splice_stream_t stream)
 {
+    const Range range("splice_channel_stats T=%lld K=%lld", (long long)T, (long long)K);
     if (T < 0 || !count || *count < 0) return SPLICE_ERR_INVALID_ARG;
     int rc = check_k(K, 0);
     if (rc) return rc;
@@ -208,6 +269,7 @@ int splice_select_topk(const double *mean, const double *m2, const float *absmax
                        int64_t K, int32_t k, int criterion, int32_t *idx, float *alpha_x,
                        splice_stream_t stream)
 {
+    const Range range("splice_select_topk K=%lld k=%d", (long long)K, (int)k);
     if (count < 0) return SPLICE_ERR_INVALID_ARG;
     int rc = check_k(K, k);
     if (rc) return rc;
@@ -229,6 +291,7 @@ int splice_compute_alpha(const uint16_t *A, int64_t R, int64_t K, int64_t lda, c
                          int32_t k, float *alpha, void *ws, size_t ws_bytes,
                          splice_stream_t stream)
 {
+    const Range range("splice_compute_alpha R=%lld K=%lld", (long long)R, (long long)K);
     if (R < 0) return SPLICE_ERR_INVALID_ARG;
     int rc = check_k(K, k);
     if (rc) return rc;
@@ -245,6 +308,7 @@ int splice_quantize_nvfp4(const uint16_t *A, int64_t R, int64_t K, int64_t lda, 
                           int32_t k, const float *alpha, uint8_t *codes, uint8_t *scales,
                           uint16_t *side, splice_stream_t stream)
 {
+    const Range range("splice_quantize_nvfp4 R=%lld K=%lld k=%d", (long long)R, (long long)K, (int)k);
     if (R < 0) return SPLICE_ERR_INVALID_ARG;
     int rc = check_k(K, k);
     if (rc) return rc;
@@ -310,6 +374,7 @@ int splice_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, cons
                 int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy, void *ws,
                 size_t ws_bytes, int path, splice_stream_t stream)
 {
+    const Range range("splice_gemm M=%lld N=%lld K=%lld k=%d", (long long)M, (long long)N, (long long)K, (int)k);
     GemmArgs a{Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy};
     return run_gemm("splice_gemm", a, ws, ws_bytes, path, hs(stream));
 }
@@ -319,6 +384,7 @@ int splice_gemm_noalloc(const uint8_t *Xq, const uint8_t *Xs, const float *alpha
                         int64_t M, int64_t N, int64_t K, int32_t k, float *Y, int64_t ldy, int path,
                         splice_stream_t stream)
 {
+    const Range range("splice_gemm_noalloc M=%lld N=%lld K=%lld k=%d", (long long)M, (long long)N, (long long)K, (int)k);
     GemmArgs a{Xq, Xs, alpha_x, X_S, Wq, Ws, alpha_w, W_S, M, N, K, k, Y, ldy};
     int rc = check_gemm(a, path);
     if (rc) return rc;
@@ -340,6 +406,7 @@ int nvfp4_gemm(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x, const
                const uint8_t *Ws, const float *alpha_w, int64_t M, int64_t N, int64_t K, float *Y,
                int64_t ldy, void *ws, size_t ws_bytes, int path, splice_stream_t stream)
 {
+    const Range range("nvfp4_gemm M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
     GemmArgs a{Xq, Xs, alpha_x, nullptr, Wq, Ws, alpha_w, nullptr, M, N, K, 0, Y, ldy};
     return run_gemm("nvfp4_gemm", a, ws, ws_bytes, path, hs(stream));
 }
@@ -348,6 +415,7 @@ int splice_gemm_multi(const uint8_t *Xq, const uint8_t *Xs, const float *alpha_x
                       int64_t M, int64_t K, int32_t k, const splice_weight_seg *segs, int32_t nseg,
                       void *ws, size_t ws_bytes, int path, splice_stream_t stream)
 {
+    const Range range("splice_gemm_multi M=%lld K=%lld k=%d segments=%d", (long long)M, (long long)K, (int)k, (int)nseg);
     static_assert(SPLICE_SEG_MAX == SEG_MAX, "segment limit");
     if (nseg < 1 || nseg > SPLICE_SEG_MAX || !segs) return SPLICE_ERR_INVALID_ARG;
     GemmSeg seg[SEG_MAX];
@@ -376,6 +444,7 @@ int splice_gemm_decode_fused(const uint16_t *X, int64_t ldx, const int32_t *idx,
                              const float *alpha_w, const uint16_t *W_S, int64_t M, int64_t N,
                              int64_t K, int32_t k, float *Y, int64_t ldy, splice_stream_t stream)
 {
+    const Range range("splice_gemm_decode_fused M=%lld N=%lld K=%lld k=%d", (long long)M, (long long)N, (long long)K, (int)k);
     if (M < 0 || N < 0) return SPLICE_ERR_INVALID_ARG;
     int rc = check_k(K, k);
     if (rc) return rc;
@@ -400,6 +469,7 @@ int splice_gemm_decode_fused_multi(const uint16_t *X, int64_t ldx, const int32_t
                                    const float *alpha_x, int64_t M, int64_t K, int32_t k,
                                    const splice_weight_seg *segs, int32_t nseg, splice_stream_t stream)
 {
+    const Range range("splice_gemm_decode_fused_multi M=%lld K=%lld k=%d segments=%d", (long long)M, (long long)K, (int)k, (int)nseg);
     if (nseg < 1 || nseg > SPLICE_SEG_MAX || !segs) return SPLICE_ERR_INVALID_ARG;
     GemmSeg seg[SEG_MAX];
     int64_t total = 0;
@@ -439,6 +509,7 @@ int splice_tim_filter(const float *logp, int64_t B, int64_t ldl, const int32_t *
                       int32_t *g2, float *adv, int64_t adv_cols, int64_t lda,
                       splice_stream_t stream)
 {
+    const Range range("splice_tim_filter B=%lld", (long long)B);
     constexpr int64_t I31 = 2147483647;
     if (B < 0 || ldl < 0 || k1_num < 0 || k1_den <= 0 || k2 < 0 || adv_cols < 0)
         return SPLICE_ERR_INVALID_ARG;
@@ -478,6 +549,7 @@ size_t splice_grouped_workspace_size(const splice_group *, int32_t, int64_t, int
 int splice_gemm_grouped(const splice_group *groups, int32_t G, int64_t N, int64_t K, int32_t k,
                         void *, size_t, splice_stream_t stream)
 {
+    const Range range("splice_gemm_grouped groups=%d N=%lld K=%lld k=%d", (int)G, (long long)N, (long long)K, (int)k);
     if (G < 0 || (G > 0 && !groups)) return SPLICE_ERR_INVALID_ARG;
     std::vector<GemmArgs> args;
     args.reserve(G);

@@ -52,6 +52,13 @@
  *     passes its argument checks writes one line to stderr: its shape, the
  *     path, kernel, tile and K split its plan chose (as splice_gemm_plan
  *     reports them) and the status it returns.
+ *   - Profiler ranges: with SPLICE_ROCTX set to anything but "" or "0" when
+ *     the library is first used, every compute entry point runs inside a
+ *     roctx range named for the function and its shape (for example
+ *     "splice_gemm M=128 N=4096 K=4096 k=64"), which marker traces such as
+ *     rocprofv3 --marker-trace line up with the kernels the call launched.
+ *     The roctx library is opened at that first use, so linking against this
+ *     library needs no roctx; when it cannot be opened, calls run unmarked.
  */
 #ifndef SPLICE_H
 #define SPLICE_H

@@ -361,3 +361,31 @@ def test_splice_log_lines(flag):
     assert "tile=128x128 splits=8 status=-3" in lines[0]
     assert "M=64 N=1024 K=4096 k=64 segments=0 path=decode" in lines[1]
     assert "tile=64x32 splits=4 status=-3" in lines[1]
+
+
+ROCTX_PROBE = LOG_PROBE + """
+with open("/proc/self/maps") as f:
+    print(int(any("rocprofiler-sdk-roctx" in line for line in f)))
+"""
+
+
+@pytest.mark.parametrize("flag", ["1", "0", None])
+def test_splice_roctx_ranges(flag):
+    """SPLICE_ROCTX: the library opens ROCm's roctx library at its first
+    call only when the flag is set (torch maps a roctx library of its own, so
+    the check names ROCm's), and the ranges leave every status as it was."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("SPLICE_ROCTX", None)
+    env.pop("SPLICE_LOG", None)
+    if flag is not None:
+        env["SPLICE_ROCTX"] = flag
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", ROCTX_PROBE], capture_output=True, text=True, env=env, cwd=root,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    out = r.stdout.split()
+    assert out[:3] == [str(splice.ERR_WORKSPACE), str(splice.ERR_WORKSPACE), str(splice.ERR_INVALID_ARG)]
+    assert out[3] == ("1" if flag == "1" else "0"), r.stdout
