@@ -97,6 +97,27 @@ __device__ __forceinline__ void wait_vmem()
     asm volatile("" ::: "memory");
 }
 
+// Device-coherent 16-byte accesses for partial sums exchanged between
+// workgroups: raw buffer loads and stores with the sc1 cache policy, the
+// policy the compiler gives agent-scope relaxed atomics (they bypass the
+// per-XCD caches that are not coherent with each other), but twice as wide
+// as a 64-bit atomic and free to be scheduled like ordinary loads.  The
+// resource covers `bytes` bytes from `base`; offsets past it read 0 and
+// write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ u32x4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_SC1));
+}
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, CPOL_SC1);
+}
+
 // 8 bf16 values (16 bytes) of a side buffer row, zero past `valid` elements.
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p, int valid, bool aligned16)
 {

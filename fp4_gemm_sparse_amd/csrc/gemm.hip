@@ -94,6 +94,16 @@ struct SplitK {
 // Decode share per thread and step (both forms): 2 units of (row, 32-channel
 // half) = 32 code bytes + 4 scale bytes -> 64 FP16 values.
 // ===========================================================================
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled at compile time
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 struct LdsCfg {
     static constexpr int BKL = 64;
     static constexpr int ROWB = BKL * 2;                 // 128 bytes of FP16 per row
@@ -127,9 +137,10 @@ struct LdsGeo {
 // PF: register stages of operand codes in flight.  The codes of step t are
 // loaded PF steps ahead (at the end of step t - 1 - PF) and decoded during
 // step t - 1, so a load has PF - 1 full steps of matrix work to arrive; with
-// PF = 1 it is issued just before the barrier that precedes its use, which is
-// enough where eight waves keep the matrix cores busy (the 256 x 256 tile)
-// but exposes the load latency every step for the 128 x 128 tile's few waves.
+// PF = 1 it is issued just before the barrier that precedes its use and the
+// first decode of the next step waits for it.  The scale bytes are held as
+// 16-bit values (widened to 32 bits, the compiler masked them at the loop's
+// back edge, which waited for the stages just issued).
 // SPLIT: the kernel may split K over workgroups (sk.nsplit > 1); only then is
 // the partial-tile epilogue compiled in.
 template <int BM, int BN, int WGM, int WGN, bool TAIL, int PF = 1, bool SPLIT = false>
@@ -172,7 +183,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     }
     // register stage r holds the codes of the steps t with t % PF == r
     u32x4 pc[PF][UNITS];
-    unsigned ps[PF][UNITS];
+    uint16_t ps[PF][UNITS];
     auto gload = [&](int r, int kt) {
 #pragma unroll
         for (int i = 0; i < UNITS; i++) {
@@ -213,12 +224,11 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     // is its own branch-free copy of the loop.
     auto main_loop = [&](auto fmv) {
     constexpr int FMV = decltype(fmv)::value;
-    for (int kb = 0; kb < nk; kb += PF)
-#pragma unroll
-    for (int u = 0; u < PF; u++) {
-        const int kt = kb + u;
-        if (kt >= nk) break;
-        const int rs = (u + 1) % PF;         // stage holding step kt + 1
+    // K step kt; its decode fills register stage (u + 1) % PF's step into
+    // the idle buffer, and the stage is refilled PF steps ahead
+    auto step = [&](int kt, auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int rs = (u + 1) % PF;     // stage holding step kt + 1
         const uint8_t *cur = lds + (kt & 1) * C::TILE;
         uint8_t *nxt = lds + ((kt + 1) & 1) * C::TILE;
         f16x8 a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
@@ -251,7 +261,18 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         }
         gload(rs, kt0 + min(kt + 1 + PF, nk - 1));
         lds_barrier();      // the prefetches of steps kt+2 .. kt+1+PF stay in flight
-    }
+    };
+    // Whole groups of PF steps in the loop, the rest after it: a loop body
+    // with no exit between its steps lets the compiler see that each step
+    // waits only for the stage loaded PF steps earlier (with exits inside the
+    // body it waited for every load in flight at the top of each group, the
+    // ones just issued included).
+    int kt = 0;
+    for (; kt + PF <= nk; kt += PF)
+        static_for<PF>([&](auto uc) { step(kt + decltype(uc)::value, uc); });
+    static_for<PF - 1>([&](auto uc) {
+        if (kt + decltype(uc)::value < nk) step(kt + decltype(uc)::value, uc);
+    });
     };
     // valid fragment rows of this wave (wave-uniform)
     const int fm_ok = (int)min<int64_t>(C::FM, max<int64_t>(0, (M - (m0 + wm * C::WM) + 31) / 32));
@@ -314,19 +335,23 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     if (SPLIT && sk.nsplit > 1) {
         __shared__ int last_flag;
         constexpr int NWV = NT / WAVE;
-        uint64_t *pt = reinterpret_cast<uint64_t *>(sk.part) + sk.wtile * (int64_t)sk.nsplit * (C::BM * C::BN / 2);
-        auto slot = [&](int sp, int i, int j, int q) {
-            return pt + ((((int64_t)sp * NWV + wave) * C::FM + i) * C::FN + j) * 8 * WAVE + q * WAVE + lane;
+        // a wave's partial tile: FM x FN fragments of four 16-byte pieces per
+        // lane, each piece stored lane-contiguous (one 1 KB row per wave)
+        constexpr int PV = C::FM * C::FN * 4;
+        constexpr uint32_t SPLIT_BYTES = (uint32_t)C::BM * C::BN * 4;
+        const __amdgpu_buffer_rsrc_t rs =
+            coherent_rsrc(sk.part + sk.wtile * (int64_t)sk.nsplit * (C::BM * C::BN), sk.nsplit * SPLIT_BYTES);
+        auto off = [&](int sp, int pv) -> uint32_t {
+            return (uint32_t)sp * SPLIT_BYTES + (uint32_t)(((wave * PV + pv) * WAVE + lane) * 16);
         };
 #pragma unroll
         for (int i = 0; i < C::FM; i++)
 #pragma unroll
             for (int j = 0; j < C::FN; j++)
 #pragma unroll
-                for (int q = 0; q < 8; q++) {
-                    const f32x2 v = {acc[i][j][2 * q], acc[i][j][2 * q + 1]};
-                    __hip_atomic_store(slot(sk.split, i, j, q), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                for (int q = 0; q < 4; q++) {
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    coherent_store16(rs, off(sk.split, (i * C::FN + j) * 4 + q), __builtin_bit_cast(u32x4, v));
                 }
         wait_vmem();
         __syncthreads();
@@ -344,41 +369,36 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         // issue order: the partials' waits cover them)
         u32x4 pre[PU];
         if (staged) stage_load(0, 0, pre);
-        // SPR splits per round: every load of a round is issued before any
-        // is used (the compiler keeps device-coherent loads in program order,
-        // so loads interleaved with the sums would each wait for the last),
-        // and each round costs one round trip to memory.  Two splits per
-        // round where a wave's partial tile is 32 words (the 128 x 128 tile):
-        // q at M = 128 in eight splits spent 14.5 of its 26.3 us in this
-        // loop with one split per round.  The sum runs in split order.
-        constexpr int SPR = C::FM * C::FN <= 4 ? 2 : 1;
-        for (int sp0 = 0; sp0 < sk.nsplit; sp0 += SPR) {
-            uint64_t v[SPR][C::FM][C::FN][8];
+        // The partial tiles are read two splits deep: split sp + 1's loads are
+        // in flight while split sp is added, so the finishing workgroup keeps
+        // two partial tiles of loads outstanding instead of draining them
+        // every round.  The sum runs in split order.
+        u32x4 pbuf[2][PV];
+        auto pload = [&](int sp, u32x4 (&b)[PV]) {
 #pragma unroll
-            for (int h = 0; h < SPR; h++)
-                if (sp0 + h < sk.nsplit)
+            for (int pv = 0; pv < PV; pv++) b[pv] = coherent_load16(rs, off(sp, pv));
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto padd = [&](const u32x4 (&b)[PV], bool first) {
 #pragma unroll
-                    for (int i = 0; i < C::FM; i++)
+            for (int i = 0; i < C::FM; i++)
 #pragma unroll
-                        for (int j = 0; j < C::FN; j++)
+                for (int j = 0; j < C::FN; j++)
 #pragma unroll
-                            for (int q = 0; q < 8; q++)
-                                v[h][i][j][q] = __hip_atomic_load(slot(sp0 + h, i, j, q), __ATOMIC_RELAXED,
-                                                                  __HIP_MEMORY_SCOPE_AGENT);
+                    for (int q = 0; q < 4; q++) {
+                        const f32x4 t = __builtin_bit_cast(f32x4, b[(i * C::FN + j) * 4 + q]);
 #pragma unroll
-            for (int h = 0; h < SPR; h++)
-                if (sp0 + h < sk.nsplit)
-#pragma unroll
-                    for (int i = 0; i < C::FM; i++)
-#pragma unroll
-                        for (int j = 0; j < C::FN; j++)
-#pragma unroll
-                            for (int q = 0; q < 8; q++) {
-                                const f32x2 t = __builtin_bit_cast(f32x2, v[h][i][j][q]);
-                                const bool first = sp0 + h == 0;
-                                acc[i][j][2 * q] = first ? t.x : acc[i][j][2 * q] + t.x;
-                                acc[i][j][2 * q + 1] = first ? t.y : acc[i][j][2 * q + 1] + t.y;
-                            }
+                        for (int e = 0; e < 4; e++)
+                            acc[i][j][4 * q + e] = first ? t[e] : acc[i][j][4 * q + e] + t[e];
+                    }
+        };
+        pload(0, pbuf[0]);
+        for (int sp = 0; sp < sk.nsplit; sp += 2) {
+            if (sp + 1 < sk.nsplit) pload(sp + 1, pbuf[1]);
+            padd(pbuf[0], sp == 0);
+            if (sp + 1 >= sk.nsplit) break;
+            if (sp + 2 < sk.nsplit) pload(sp + 2, pbuf[0]);
+            padd(pbuf[1], false);
         }
         if (staged) {
             stage_store(0, pre);
@@ -492,6 +512,10 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         }
 }
 
+// code stages in flight for the 256 x 256 tile: two (2.1-3.0% faster than
+// one on q, gate and down at M = 8192; three measured the same as two)
+constexpr int PF256 = 2;
+
 template <bool TAIL>
 __global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
 {
@@ -499,19 +523,28 @@ __global__ __launch_bounds__(512) void prefill_lds_kernel(GemmArgs a)
     const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    lds_tile<256, 256, 2, 4, TAIL>(a, tm, tn, lds);
+    lds_tile<256, 256, 2, 4, TAIL, PF256>(a, tm, tn, lds);
 }
 
 // code stages in flight for the 128 x 128 tile (one wave per SIMD per
 // workgroup): three measured 5-9% faster than one at M = 65..1024
 constexpr int PF128 = 3;
+// the same tile with the K range split over workgroups runs at most 256
+// workgroups, one per CU, so a lane may hold up to 512 registers.  Ranges of
+// more than 16 K steps keep six steps of codes in flight, shorter ones three
+// (measured on MI355X, us, three / six stages: q at M = 128 in eight ranges
+// of 8 steps 23.5 / 24.3, k 20.4 / 21.4; down at M = 128 in eight of 24
+// steps 37.1 / 36.6, at M = 256 in four of 48 50.2 / 48.5; gate at M = 65 in
+// two of 32 35.9 / 35.0).
+constexpr int PF128S_SHORT = 3, PF128S_LONG = 6, PF128S_SHORT_MAX_STEPS = 16;
 
-// 128 x 128 tiles, four waves of 64 x 64 (two workgroups per CU, so at most
-// 256 registers per lane: the launch bound says so): for grids
-// too small for the 256 x 256 tile; where even these tiles leave CUs idle,
-// the K range is split nsplit ways (cnt and part in the workspace)
-template <bool TAIL>
-__global__ __launch_bounds__(256, 2) void prefill_lds128_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
+// 128 x 128 tiles, four waves of 64 x 64: for grids too small for the
+// 256 x 256 tile.  Unsplit, two workgroups per CU (so at most 256 registers
+// per lane: the launch bound says so).  Where even these tiles leave CUs
+// idle, the K range is split nsplit ways (cnt and part in the workspace),
+// one workgroup per CU.
+template <bool TAIL, int PF, int OCC>
+__global__ __launch_bounds__(256, OCC) void prefill_lds128_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tiles_m = (int)((a.M + 127) / 128), tiles_n = (int)((a.N + 127) / 128);
@@ -523,12 +556,12 @@ __global__ __launch_bounds__(256, 2) void prefill_lds128_kernel(GemmArgs a, int 
     sk.wtile = (int64_t)tm * tiles_n + tn;
     sk.cnt = cnt;
     sk.part = part;
-    lds_tile<128, 128, 2, 2, TAIL, PF128, true>(a, tm, tn, lds, sk);
+    lds_tile<128, 128, 2, 2, TAIL, PF, true>(a, tm, tn, lds, sk);
 }
 
 // the same tiles over column segments: tile columns numbered across them
-template <int BT, int WGN, bool TAIL>
-__global__ __launch_bounds__(64 * 2 * WGN, BT == 128 ? 2 : 1) void prefill_seg_kernel(SegTable t, int nsplit, unsigned *cnt,
+template <int BT, int WGN, bool TAIL, int PF, int OCC>
+__global__ __launch_bounds__(64 * 2 * WGN, OCC) void prefill_seg_kernel(SegTable t, int nsplit, unsigned *cnt,
                                                                    float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -542,7 +575,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, BT == 128 ? 2 : 1) void prefill_seg_k
     sk.wtile = (int64_t)tm * tiles_n + tn;
     sk.cnt = cnt;
     sk.part = part;
-    lds_tile<BT, BT, 2, WGN, TAIL, (BT == 128 ? PF128 : 1), (BT == 128)>(a, tm, local, lds, sk);
+    lds_tile<BT, BT, 2, WGN, TAIL, PF, (BT == 128)>(a, tm, local, lds, sk);
 }
 
 // ---------------------------------------------------------------------------
@@ -659,14 +692,14 @@ static hipError_t launch_prefill_lds(const GemmArgs &a, const SegSpec *sp, hipSt
         reinterpret_cast<const void *>(&prefill_lds_kernel<TAIL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     static const hipError_t attr_seg = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&prefill_seg_kernel<256, 4, TAIL>),
+        reinterpret_cast<const void *>(&prefill_seg_kernel<256, 4, TAIL, PF256, 1>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     if (attr_seg != hipSuccess) return attr_seg;
     const int64_t tiles_m = (a.M + C::BM - 1) / C::BM;
     if (sp) {
         const SegTable t = make_seg_table(a, *sp, C::BN);
-        hipLaunchKernelGGL((prefill_seg_kernel<256, 4, TAIL>), dim3((unsigned)(tiles_m * t.start[t.nseg])),
+        hipLaunchKernelGGL((prefill_seg_kernel<256, 4, TAIL, PF256, 1>), dim3((unsigned)(tiles_m * t.start[t.nseg])),
                            dim3(C::NT), lds, s, t, 1, (unsigned *)nullptr, (float *)nullptr);
     } else {
         const int64_t tiles = tiles_m * ((a.N + C::BN - 1) / C::BN);
@@ -685,11 +718,29 @@ static hipError_t launch_prefill_lds128(const GemmArgs &a, const SegSpec *sp, co
     float *part = p.nsplit > 1 ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + SPLIT_COUNTER_BYTES)
                                : nullptr;
     const dim3 grid((unsigned)(p.tiles * p.nsplit));
+    const int64_t nk = a.K / LdsCfg::BKL;
+    const bool long_range = p.nsplit > 1 && (nk + p.nsplit - 1) / p.nsplit > PF128S_SHORT_MAX_STEPS;
     if (sp) {
         const SegTable t = make_seg_table(a, *sp, C::BN);
-        hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL>), grid, dim3(C::NT), lds, s, t, p.nsplit, cnt, part);
+        if (p.nsplit == 1)
+            hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL, PF128, 2>), grid, dim3(C::NT), lds, s, t, p.nsplit,
+                               cnt, part);
+        else if (long_range)
+            hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL, PF128S_LONG, 1>), grid, dim3(C::NT), lds, s, t,
+                               p.nsplit, cnt, part);
+        else
+            hipLaunchKernelGGL((prefill_seg_kernel<128, 2, TAIL, PF128S_SHORT, 1>), grid, dim3(C::NT), lds, s, t,
+                               p.nsplit, cnt, part);
     } else {
-        hipLaunchKernelGGL(prefill_lds128_kernel<TAIL>, grid, dim3(C::NT), lds, s, a, p.nsplit, cnt, part);
+        if (p.nsplit == 1)
+            hipLaunchKernelGGL((prefill_lds128_kernel<TAIL, PF128, 2>), grid, dim3(C::NT), lds, s, a, p.nsplit, cnt,
+                               part);
+        else if (long_range)
+            hipLaunchKernelGGL((prefill_lds128_kernel<TAIL, PF128S_LONG, 1>), grid, dim3(C::NT), lds, s, a, p.nsplit,
+                               cnt, part);
+        else
+            hipLaunchKernelGGL((prefill_lds128_kernel<TAIL, PF128S_SHORT, 1>), grid, dim3(C::NT), lds, s, a, p.nsplit,
+                               cnt, part);
     }
     return hipGetLastError();
 }
@@ -763,7 +814,8 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk, con
 {
     using C = DecodeCfg<MB, CB, NW, BB>;
     __shared__ f32x4 red[NW][C::RED_TILES][WAVE];
-    const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+    const int tid = threadIdx.x, lane = tid % WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int g = lane >> 4, rr = lane & 15;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t rowb = K / 2, rows = K / 16;
@@ -802,9 +854,12 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk, con
 #pragma unroll
         for (int j = 0; j < CB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // scale pairs held as 16-bit values: widened to 32 bits, the compiler
+    // masked them where the loop's register copies meet, which waited for
+    // the batch just issued
     u32x4 wc0[BB][CB], xc0[BB][MB], wc1[BB][CB], xc1[BB][MB];
-    unsigned ws0[BB][CB], xs0[BB][MB], ws1[BB][CB], xs1[BB][MB];
-    auto load = [&](int c, u32x4 (*wc)[CB], unsigned (*ws)[CB], u32x4 (*xc)[MB], unsigned (*xs)[MB]) {
+    uint16_t ws0[BB][CB], xs0[BB][MB], ws1[BB][CB], xs1[BB][MB];
+    auto load = [&](int c, u32x4 (*wc)[CB], uint16_t (*ws)[CB], u32x4 (*xc)[MB], uint16_t (*xs)[MB]) {
 #pragma unroll
         for (int b = 0; b < BB; b++) {
             const int ci = min(c + b * NW, c_hi - 1);        // clamped; masked at use
@@ -820,7 +875,7 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk, con
             }
         }
     };
-    auto compute = [&](int c, u32x4 (*wc)[CB], unsigned (*ws)[CB], u32x4 (*xc)[MB], unsigned (*xs)[MB]) {
+    auto compute = [&](int c, u32x4 (*wc)[CB], uint16_t (*ws)[CB], u32x4 (*xc)[MB], uint16_t (*xs)[MB]) {
 #pragma unroll
         for (int b = 0; b < BB; b++) {
             const bool ok = c + b * NW < c_hi;
@@ -843,7 +898,8 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk, con
     };
 
     int c = c_lo + wave;
-    if (c < c_hi) load(c, wc0, ws0, xc0, xs0);
+    const bool any = c < c_hi;            // wave-uniform
+    if (any) load(c, wc0, ws0, xc0, xs0);
     // W_S fragments (k = 32 or 64) of the tile this wave finishes, issued by
     // every wave alike right behind its first batch: the waits for later
     // batches, younger loads, include them, and by then they have arrived.
@@ -872,15 +928,40 @@ __device__ __forceinline__ void decode2_body(const GemmArgs &a, int64_t blk, con
             tb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wb + hh * 32));
         }
     }
-    while (c < c_hi) {
-        const int c1 = c + BB * NW;
-        if (c1 < c_hi) load(c1, wc1, ws1, xc1, xs1);
+    // Two register batches, both in flight from the start: while one batch
+    // is decoded and multiplied, the loads of the batch two ahead go into
+    // its registers.  The loop runs while four or more batches remain, so
+    // each of its loads is real and it has a single exit; the last two or
+    // three batches follow it.  (With exits between the batches, or loads
+    // that might not be issued, the compiler could not count the younger
+    // loads at the top of the loop and waited for all of them, the batch
+    // just issued included.)  The scheduling barriers keep the compiler from
+    // sinking a batch's loads below the arithmetic before them.
+    constexpr int STEP = BB * NW;
+    const int nbatch = any ? (c_hi - c + STEP - 1) / STEP : 0;
+    if (nbatch == 1) {
         compute(c, wc0, ws0, xc0, xs0);
-        if (c1 >= c_hi) break;
-        const int c2 = c1 + BB * NW;
-        if (c2 < c_hi) load(c2, wc0, ws0, xc0, xs0);
-        compute(c1, wc1, ws1, xc1, xs1);
-        c = c2;
+    } else if (nbatch > 1) {
+        load(c + STEP, wc1, ws1, xc1, xs1);
+        __builtin_amdgcn_sched_barrier(0);
+        int j = 0;
+        for (; j + 4 <= nbatch; j += 2) {
+            compute(c, wc0, ws0, xc0, xs0);
+            load(c + 2 * STEP, wc0, ws0, xc0, xs0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(c + STEP, wc1, ws1, xc1, xs1);
+            load(c + 3 * STEP, wc1, ws1, xc1, xs1);
+            __builtin_amdgcn_sched_barrier(0);
+            c += 2 * STEP;
+        }
+        const int rest = nbatch - j;                           // 2 or 3
+        compute(c, wc0, ws0, xc0, xs0);
+        if (rest == 3) {
+            load(c + 2 * STEP, wc0, ws0, xc0, xs0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        compute(c + STEP, wc1, ws1, xc1, xs1);
+        if (rest == 3) compute(c + 2 * STEP, wc0, ws0, xc0, xs0);
     }
 
     // ---- deterministic cross-wave sum through LDS, in rounds of RED_TILES tiles
