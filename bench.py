@@ -840,13 +840,20 @@ def moe_measurement(torch, S, synth, dev):
                        for _ in range(nset - 1)]
     tg = graph_timed(torch, lambda i: S.splice_gemm_grouped(sets[i % nset], N, K, K_PROT), 3 * nset)
     fl = 2.0 * int(counts.sum()) * N * K
-    # 128 x 128 tiles of the launch, and the flops they issue over the useful ones
-    tiles = int(sum(-(-int(c) // 128) for c in counts)) * (N // 128)
+    # tiles of the launch (64 x 192 for experts of at most 64 tokens, else
+    # 128 x 128), and the flops they issue over the useful ones
+    tiles, padded = 0, 0
+    for c in (int(c) for c in counts):
+        if c == 0:
+            continue
+        t = -(-N // 192) if c <= 64 else -(-c // 128) * -(-N // 128)
+        tiles += t
+        padded += t * (64 * 192 if c <= 64 else 128 * 128)
     out["moe_grouped"] = {"experts": len(counts), "tokens": int(counts.sum()), "max_tokens": int(counts.max()),
                           "ms": round(tg, 4), "TFLOPs": round(fl / (tg * 1e-3) / 1e12, 2),
                           "frac_peak": round(fl / (tg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                           "weight_GBps": round(wbytes / (tg * 1e-3) / 1e9, 1),
-                          "tiles_128": tiles, "padded_flop_ratio": round(tiles * 128 * 128 / (int(counts.sum()) * N), 3),
+                          "tiles": tiles, "padded_flop_ratio": round(padded / (int(counts.sum()) * N), 3),
                           "weight_copies": nset}
     del sets
     return out["moe_grouped"]

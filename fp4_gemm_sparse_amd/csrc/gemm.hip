@@ -276,7 +276,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
     };
     // valid fragment rows of this wave (wave-uniform)
     const int fm_ok = (int)min<int64_t>(C::FM, max<int64_t>(0, (M - (m0 + wm * C::WM) + 31) / 32));
-    static_assert(C::FM == 2 || C::FM == 4, "fragment rows per wave");
+    static_assert(C::FM == 1 || C::FM == 2 || C::FM == 4, "fragment rows per wave");
     if (fm_ok >= C::FM)
         main_loop(std::integral_constant<int, C::FM>{});
     else if (fm_ok == 0)
@@ -606,6 +606,12 @@ struct GroupedArgs {
     int k, tiles_n, G;
 };
 
+// Groups of at most GROUP_SMALL_M rows take 64 x 192 tiles (four waves of
+// 32 x 96, the same 256 LDS rows per step as 128 x 128): a small group's
+// 128 x 128 tiles decoded 128 activation rows for at most 64 real ones, and
+// sixteen of them per 2048 columns against eleven.
+constexpr int GROUP_SMALL_M = 64, GROUP_SMALL_BN = 192;
+
 template <int BM, int BN, bool TAIL>
 __global__ __launch_bounds__(256, 2) void grouped_prefill_kernel(GroupedArgs ga)
 {
@@ -617,7 +623,10 @@ __global__ __launch_bounds__(256, 2) void grouped_prefill_kernel(GroupedArgs ga)
     const GroupDesc &d = ga.g[e];
     const GemmArgs a{d.Xq, d.Xs, d.alpha_x, d.X_S, d.Wq, d.Ws, d.alpha_w, d.W_S,
                      d.M, ga.N, ga.K, ga.k, d.Y, ga.N};
-    lds_tile<BM, BN, 2, 2, TAIL, PF128>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
+    if (d.M <= GROUP_SMALL_M)
+        lds_tile<GROUP_SMALL_M, GROUP_SMALL_BN, 2, 2, TAIL, PF128>(a, 0, local, lds);
+    else
+        lds_tile<BM, BN, 2, 2, TAIL, PF128>(a, local / ga.tiles_n, local % ga.tiles_n, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -776,7 +785,9 @@ hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s)
             ga.g[i] = GroupDesc{a.Xq, a.Xs, a.alpha_x, a.X_S, a.Wq, a.Ws, a.alpha_w, a.W_S, a.Y,
                                 a.M > 0 ? a.M : 0};
             ga.tile_start[i] = tiles;
-            tiles += (int)((ga.g[i].M + BM - 1) / BM) * ga.tiles_n;
+            if (ga.g[i].M <= 0) continue;
+            tiles += ga.g[i].M <= GROUP_SMALL_M ? (int)((N + GROUP_SMALL_BN - 1) / GROUP_SMALL_BN)
+                                                : (int)((ga.g[i].M + BM - 1) / BM) * ga.tiles_n;
         }
         ga.tile_start[cnt] = tiles;
         ga.G = cnt;
