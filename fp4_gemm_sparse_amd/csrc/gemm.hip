@@ -331,6 +331,12 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         lds_barrier();
     };
     bool first_staged = false;
+    // K split, up to 64 side channels: the finishing workgroup loads each
+    // wave's side fragments straight into registers ahead of the partial
+    // tiles, so neither an LDS staging pass nor its barrier sits in the
+    // launch's serial tail; the products are summed in the staged order
+    bool side_direct = false;
+    bf16x8 sxa[SPLIT ? C::FM : 1][4], swb[SPLIT ? C::FN : 1][4];
 
     if (SPLIT && sk.nsplit > 1) {
         __shared__ int last_flag;
@@ -368,7 +374,34 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         // their latency passes while the partials arrive (loads complete in
         // issue order: the partials' waits cover them)
         u32x4 pre[PU];
-        if (staged) stage_load(0, 0, pre);
+        side_direct = staged && k <= 64;
+        if (side_direct) {
+            // rows past M or N read the last row (clamped) and are zeroed
+            const bf16x8 z = {};
+#pragma unroll
+            for (int i = 0; i < C::FM; i++) {
+                const int64_t m = m0 + wm * C::WM + i * 32 + rr;
+                const uint16_t *xp = a.X_S + min<int64_t>(m, M - 1) * k + g * 8;
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++) {
+                    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xp + min(kk * 16, k - 16)));
+                    sxa[SPLIT ? i : 0][kk] = m < M ? v : z;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < C::FN; j++) {
+                const int64_t n = n0 + wn * C::WN + j * 32 + rr;
+                const uint16_t *wp = a.W_S + min<int64_t>(n, N - 1) * k + g * 8;
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++) {
+                    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wp + min(kk * 16, k - 16)));
+                    swb[SPLIT ? j : 0][kk] = n < N ? v : z;
+                }
+            }
+            first_staged = true;          // nothing left to stage for the first pass
+        } else if (staged) {
+            stage_load(0, 0, pre);
+        }
         // The partial tiles are read two splits deep: split sp + 1's loads are
         // in flight while split sp is added, so the finishing workgroup keeps
         // two partial tiles of loads outstanding instead of draining them
@@ -400,7 +433,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
             if (sp + 2 < sk.nsplit) pload(sp + 2, pbuf[0]);
             padd(pbuf[1], false);
         }
-        if (staged) {
+        if (staged && !side_direct) {
             stage_store(0, pre);
             if (kn0 > C::BKL) {
                 u32x4 v[PU];
@@ -472,7 +505,14 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
         for (int j = 0; j < C::FN; j++)
 #pragma unroll
             for (int q = 0; q < 16; q++) side[j][q] = 0.f;
-        if (staged) {
+        if (SPLIT && side_direct) {
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++)
+                if (kk < k / 16)
+#pragma unroll
+                    for (int j = 0; j < C::FN; j++)
+                        side[j] = mfma32_bf16(sxa[SPLIT ? i : 0][kk], swb[SPLIT ? j : 0][kk], side[j]);
+        } else if (staged) {
             side_staged(i, kn0, side);
         } else if (TAIL && k > 0) {     // k not a multiple of 16: direct loads, masked
             const bool al = (k % 8) == 0;
@@ -542,7 +582,7 @@ constexpr int PF128S_SHORT = 3, PF128S_LONG = 6, PF128S_SHORT_MAX_STEPS = 16;
 // 256 x 256 tile.  Unsplit, two workgroups per CU (so at most 256 registers
 // per lane: the launch bound says so).  Where even these tiles leave CUs
 // idle, the K range is split nsplit ways (cnt and part in the workspace),
-// one workgroup per CU.
+// one workgroup per CU; only these instances compile the split epilogue.
 template <bool TAIL, int PF, int OCC>
 __global__ __launch_bounds__(256, OCC) void prefill_lds128_kernel(GemmArgs a, int nsplit, unsigned *cnt, float *part)
 {
@@ -556,7 +596,7 @@ __global__ __launch_bounds__(256, OCC) void prefill_lds128_kernel(GemmArgs a, in
     sk.wtile = (int64_t)tm * tiles_n + tn;
     sk.cnt = cnt;
     sk.part = part;
-    lds_tile<128, 128, 2, 2, TAIL, PF, true>(a, tm, tn, lds, sk);
+    lds_tile<128, 128, 2, 2, TAIL, PF, OCC == 1>(a, tm, tn, lds, sk);
 }
 
 // the same tiles over column segments: tile columns numbered across them
@@ -575,7 +615,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, OCC) void prefill_seg_kernel(SegTable
     sk.wtile = (int64_t)tm * tiles_n + tn;
     sk.cnt = cnt;
     sk.part = part;
-    lds_tile<BT, BT, 2, WGN, TAIL, PF, (BT == 128)>(a, tm, local, lds, sk);
+    lds_tile<BT, BT, 2, WGN, TAIL, PF, (BT == 128 && OCC == 1)>(a, tm, local, lds, sk);
 }
 
 // ---------------------------------------------------------------------------
