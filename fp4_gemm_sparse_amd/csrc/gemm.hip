@@ -403,9 +403,11 @@ __device__ __forceinline__ void lds_tile(const GemmArgs &a, int tm, int tn, uint
             stage_load(0, 0, pre);
         }
         // The partial tiles are read two splits deep: split sp + 1's loads are
-        // in flight while split sp is added, so the finishing workgroup keeps
-        // two partial tiles of loads outstanding instead of draining them
-        // every round.  The sum runs in split order.
+        // issued before split sp is added.  (Because the later loads are
+        // conditional, the compiler's wait before each add after the first
+        // also covers the loads just issued; a single-exit form without that
+        // wait, measured together with the side product computed ahead of the
+        // sums, was slower.)  The sum runs in split order.
         u32x4 pbuf[2][PV];
         auto pload = [&](int sp, u32x4 (&b)[PV]) {
 #pragma unroll
