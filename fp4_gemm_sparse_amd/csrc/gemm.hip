@@ -821,9 +821,14 @@ hipError_t launch_gemm_grouped(const GemmArgs *groups, int G, hipStream_t s)
     ga.tiles_n = (int)((N + BN - 1) / BN);
     for (int g0 = 0; g0 < G; g0 += GROUP_MAX) {
         const int cnt = G - g0 < GROUP_MAX ? G - g0 : GROUP_MAX;
+        // the largest groups' tiles first: workgroups are dispatched in
+        // order, so the cheaper tiles of the small groups fill the last round
+        int order[GROUP_MAX];
+        for (int i = 0; i < cnt; i++) order[i] = g0 + i;
+        std::stable_sort(order, order + cnt, [&](int x, int y) { return groups[x].M > groups[y].M; });
         int tiles = 0;
         for (int i = 0; i < cnt; i++) {
-            const GemmArgs &a = groups[g0 + i];
+            const GemmArgs &a = groups[order[i]];
             ga.g[i] = GroupDesc{a.Xq, a.Xs, a.alpha_x, a.X_S, a.Wq, a.Ws, a.alpha_w, a.W_S, a.Y,
                                 a.M > 0 ? a.M : 0};
             ga.tile_start[i] = tiles;
